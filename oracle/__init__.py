@@ -1,0 +1,15 @@
+"""Oracle package: plain fp64 CPU implementation of the Longformer combined
+attention forward.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by
+the benchmark's CPU-baseline leg, never by the product library.  It shares
+no code with the HIP path.
+"""
+from .longformer_attention import (  # noqa: F401
+    dense_bruteforce,
+    forward,
+    forward_rows,
+    in_window,
+    pair_count,
+    pattern,
+)

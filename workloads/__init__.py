@@ -1,0 +1,231 @@
+"""Seeded synthetic inputs for the Longformer combined attention forward.
+
+This module only draws inputs.  It holds none of the attention arithmetic:
+no windows, no scores, no softmax, no counting.  Both sides of every parity
+check (the fp64 oracle under ``oracle/`` and the HIP library) receive the
+tensors produced here, and nothing else is shared between them.
+
+Recipe (the same for every workload):
+
+* ``numpy.random.Generator(PCG64(seed))``;
+* draw q, k, v, q_g, k_g, v_g in that order, each
+  ``standard_normal([B, n, H, D], float32)``;
+* cast to the workload dtype with round-to-nearest-even (torch ``.to``);
+  the oracle consumes the cast values widened to fp64, so both sides see
+  bit-identical inputs;
+* then draw the mask structure (sequence lengths, global positions) from the
+  same generator, after the tensors.
+
+Mask values follow the Longformer attention-mask convention (allenai
+longformer README, "Usage", run-the-model step): 0 = no attention,
+1 = local (sliding window), 2 = global.
+
+The named workloads are stand-ins for the attention inputs of the pages'
+models: a longformer-base layer at 4096 tokens (ultralytics glossary,
+"How Longformer attention works"; 256 tokens per side), question answering
+with question tokens global and padded documents (allenai README, "Usage"),
+the causal dilated character-level LM layer trained up to 23040 tokens
+(segmentfault summary, "Training"), and the LED encoder at 16K tokens
+(allenai README, LED news item).  No dataset is read.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+D_HEAD = 64
+
+
+@dataclasses.dataclass
+class Problem:
+    """One attention call's inputs (CPU tensors) and parameters."""
+
+    name: str
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    q_g: torch.Tensor
+    k_g: torch.Tensor
+    v_g: torch.Tensor
+    mask: torch.Tensor  # int8 [B, n] with values in {0, 1, 2}
+    window: int  # one-sided
+    dilation: Optional[List[int]]  # per head, None = all 1
+    causal: bool
+    scale: Optional[float]  # None = 1/sqrt(D)
+    aliased_global: bool = False  # q_g/k_g/v_g are the same tensors as q/k/v
+
+    @property
+    def shape(self):
+        return tuple(self.q.shape)
+
+    def max_global(self) -> int:
+        return int((self.mask == 2).sum(dim=1).max().item()) if self.mask.numel() else 0
+
+    def describe(self) -> dict:
+        B, n, H, D = self.shape
+        return {
+            "workload": self.name,
+            "B": B,
+            "n": n,
+            "H": H,
+            "D": D,
+            "w": self.window,
+            "dilation": self.dilation,
+            "causal": self.causal,
+            "dtype": str(self.q.dtype).replace("torch.", ""),
+            "globals_per_row": [int(x) for x in (self.mask == 2).sum(dim=1).tolist()],
+        }
+
+
+def _draw(rng: np.random.Generator, shape, dtype: torch.dtype) -> torch.Tensor:
+    a = rng.standard_normal(shape, dtype=np.float32)
+    return torch.from_numpy(a).to(dtype)
+
+
+def random_problem(
+    seed: int,
+    B: int,
+    n: int,
+    H: int,
+    window: int,
+    dtype: torch.dtype = torch.bfloat16,
+    dilation: Optional[List[int]] = None,
+    causal: bool = False,
+    n_global: int = 0,
+    pad_tail: int = 0,
+    zero_frac: float = 0.0,
+    global_positions: Optional[List[int]] = None,
+    aliased_global: bool = False,
+    scale: Optional[float] = None,
+    D: int = D_HEAD,
+    name: str = "random",
+) -> Problem:
+    """Draw a problem.
+
+    ``n_global`` distinct positions per batch row get mask 2 (or the fixed
+    ``global_positions``); the last ``pad_tail`` positions of each row get
+    mask 0; ``zero_frac`` scatters additional mask-0 positions.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (B, n, H, D)
+    q = _draw(rng, shape, dtype)
+    k = _draw(rng, shape, dtype)
+    v = _draw(rng, shape, dtype)
+    if aliased_global:
+        q_g, k_g, v_g = q, k, v
+    else:
+        q_g = _draw(rng, shape, dtype)
+        k_g = _draw(rng, shape, dtype)
+        v_g = _draw(rng, shape, dtype)
+    mask = np.ones((B, n), dtype=np.int8)
+    for b in range(B):
+        if zero_frac > 0:
+            z = rng.random(n) < zero_frac
+            mask[b, z] = 0
+        if pad_tail > 0:
+            mask[b, n - pad_tail:] = 0
+        if global_positions is not None:
+            mask[b, list(global_positions)] = 2
+        elif n_global > 0:
+            cand = np.flatnonzero(mask[b] != 0)
+            if len(cand) > 0:
+                pick = rng.choice(cand, size=min(n_global, len(cand)), replace=False)
+                mask[b, pick] = 2
+    return Problem(
+        name=name,
+        q=q, k=k, v=v, q_g=q_g, k_g=k_g, v_g=v_g,
+        mask=torch.from_numpy(mask),
+        window=window,
+        dilation=list(dilation) if dilation is not None else None,
+        causal=causal,
+        scale=scale,
+        aliased_global=aliased_global,
+    )
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads.  Seed = workload index (1..5).
+# ---------------------------------------------------------------------------
+
+WORKLOADS = ("single_head_fp32_n512", "longformer_base_n4096",
+             "qa_padded_b2_n4096", "charlm_causal_dilated_n23040",
+             "led_large_n16384")
+
+
+def single_head_fp32_n512() -> Problem:
+    """B1 n512 H1 D64, one-sided window 64, fp32, mask all 1, no globals."""
+    rng = np.random.Generator(np.random.PCG64(1))
+    shape = (1, 512, 1, D_HEAD)
+    q = _draw(rng, shape, torch.float32)
+    k = _draw(rng, shape, torch.float32)
+    v = _draw(rng, shape, torch.float32)
+    mask = torch.ones((1, 512), dtype=torch.int8)
+    return Problem("single_head_fp32_n512", q, k, v, q, k, v, mask, 64, None,
+                   False, 1.0 / 8.0, aliased_global=True)
+
+
+def longformer_base_n4096() -> Problem:
+    """B1 n4096 H12 D64, w=256 per side, bf16, token 0 global, rest local."""
+    rng = np.random.Generator(np.random.PCG64(2))
+    shape = (1, 4096, 12, D_HEAD)
+    t = [_draw(rng, shape, torch.bfloat16) for _ in range(6)]
+    mask = torch.ones((1, 4096), dtype=torch.int8)
+    mask[0, 0] = 2
+    return Problem("longformer_base_n4096", *t, mask, 256, None, False, None)
+
+
+def qa_padded_b2_n4096() -> Problem:
+    """B2 n4096 H12 D64, w=256, bf16; first 64 tokens global; lengths
+    U[2500, 4096] with a mask-0 tail (n is already a multiple of 2w=512)."""
+    rng = np.random.Generator(np.random.PCG64(3))
+    shape = (2, 4096, 12, D_HEAD)
+    t = [_draw(rng, shape, torch.bfloat16) for _ in range(6)]
+    lengths = rng.integers(2500, 4096, size=2, endpoint=True)
+    mask = torch.zeros((2, 4096), dtype=torch.int8)
+    for b in range(2):
+        L = int(lengths[b])
+        mask[b, :L] = 1
+        mask[b, :64] = 2
+    return Problem("qa_padded_b2_n4096", *t, mask, 256, None, False, None)
+
+
+def charlm_causal_dilated_n23040() -> Problem:
+    """B1 n23040 H8 D64, causal w=512, dilation 1 on heads 0-5 and 2 on
+    heads 6-7, bf16, no globals."""
+    rng = np.random.Generator(np.random.PCG64(4))
+    shape = (1, 23040, 8, D_HEAD)
+    t = [_draw(rng, shape, torch.bfloat16) for _ in range(6)]
+    mask = torch.ones((1, 23040), dtype=torch.int8)
+    return Problem("charlm_causal_dilated_n23040", *t, mask, 512,
+                   [1, 1, 1, 1, 1, 1, 2, 2], True, None)
+
+
+def led_large_n16384() -> Problem:
+    """B1 n16384 H16 D64, w=512, bf16; global at 0 plus 16 distinct random
+    positions in 1..n-1."""
+    rng = np.random.Generator(np.random.PCG64(5))
+    shape = (1, 16384, 16, D_HEAD)
+    t = [_draw(rng, shape, torch.bfloat16) for _ in range(6)]
+    g = rng.choice(np.arange(1, 16384), size=16, replace=False)
+    mask = torch.ones((1, 16384), dtype=torch.int8)
+    mask[0, 0] = 2
+    mask[0, torch.from_numpy(g.astype(np.int64))] = 2
+    return Problem("led_large_n16384", *t, mask, 512, None, False, None)
+
+
+def by_name(name: str) -> Problem:
+    return {
+        "single_head_fp32_n512": single_head_fp32_n512,
+        "longformer_base_n4096": longformer_base_n4096,
+        "qa_padded_b2_n4096": qa_padded_b2_n4096,
+        "charlm_causal_dilated_n23040": charlm_causal_dilated_n23040,
+        "led_large_n16384": led_large_n16384,
+    }[name]()
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact widening of a bf16/fp32 CPU tensor to a float64 array."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
