@@ -1,0 +1,290 @@
+"""Benchmark: Longformer sliding-window + global attention forward on one MI355X.
+
+One step = one lf_attn_forward over one batch of seeded synthetic inputs
+already resident in HBM (the whole hot path: mask scan, band tiles, global
+columns, split global rows and their merge; one kernel launch).
+
+Default workload: the longformer-base layer shape, B=1, n=4096, H=12, D=64,
+one-sided window 256, bf16, token 0 global.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu-baseline] [--no-check] [--eager]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNEL_SOURCES = ["sparse_long_document_amd/csrc/lf_attn_kernels.hip",
+                  "sparse_long_document_amd/csrc/lf_attn_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def band_flops(prob) -> float:
+    """Useful band FLOPs of one forward: 4*n*(2w+1)*D*H*B (QK^T and PV over
+    the 2w+1 window diagonals); for a causal window the w+1 diagonals that
+    exist."""
+    B, n, H, D = prob.shape
+    keys = prob.window + 1 if prob.causal else 2 * prob.window + 1
+    return 4.0 * n * keys * D * H * B
+
+
+def algorithmic_bytes(prob) -> float:
+    """Bytes the method must move once: q, k, v read and out written per
+    (token, head); k_g, v_g per (token, head) of batch rows with a global
+    token; q_g of global rows; the mask."""
+    B, n, H, D = prob.shape
+    elt = prob.q.element_size()
+    g = (prob.mask == 2).sum(dim=1)
+    total = 4.0 * B * n * H * D * elt + B * n
+    for b in range(B):
+        if int(g[b]) > 0:
+            total += 2.0 * n * H * D * elt + int(g[b]) * H * D * elt
+    return total
+
+
+class Runner:
+    """Prepared arguments for repeated lf_attn_forward calls on torch's
+    current stream (ctypes call only, no per-call validation)."""
+
+    def __init__(self, prob, device):
+        import torch
+
+        import sparse_long_document_amd as lf
+
+        self.lf = lf
+        self.prob = prob
+        self.t = [x.to(device).contiguous() for x in (prob.q, prob.k, prob.v, prob.q_g, prob.k_g, prob.v_g)]
+        self.mask = prob.mask.to(device).contiguous()
+        self.out = torch.empty_like(self.t[0])
+        B, n, H, D = prob.shape
+        self.row_nnz = torch.empty((B, H, n), dtype=torch.int32, device=device)
+        self.max_global = 0 if prob.causal else prob.max_global()
+        self.params, self._keep = lf.make_params(B, n, H, D, prob.window, prob.dilation, prob.causal,
+                                                 prob.scale, self.max_global, prob.q.dtype)
+        lib = lf.library()
+        need = lib.lf_attn_workspace_bytes(ctypes.byref(self.params))
+        self.stream = torch.cuda.current_stream(device).cuda_stream
+        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        st = lib.lf_attn_workspace_init(ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(),
+                                        ctypes.c_void_p(self.stream))
+        assert st == 0, st
+        vp = ctypes.c_void_p
+        self.args = (ctypes.byref(self.params), *[vp(x.data_ptr()) for x in self.t], vp(self.mask.data_ptr()),
+                     vp(self.out.data_ptr()), vp(self.row_nnz.data_ptr()), vp(self.ws.data_ptr()),
+                     ctypes.c_size_t(self.ws.numel()), vp(self.stream))
+        self.fn = lib.lf_attn_forward
+
+    def launch(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"lf_attn_forward failed with status {st}")
+
+
+def check_parity(prob, out, row_nnz, max_rows=48):
+    """Sampled rows of the timed output against the fp64 oracle."""
+    import numpy as np
+
+    import oracle
+
+    B, n, H, D = prob.shape
+    arrs = [x.float().numpy() for x in (prob.q, prob.k, prob.v, prob.q_g, prob.k_g, prob.v_g)]
+    mask = prob.mask.numpy()
+    o = out.float().cpu().numpy()
+    c = row_nnz.cpu().numpy()
+    rng = np.random.default_rng(1)
+    worst, nnz_ok = 0.0, True
+    for b in range(B):
+        for h in sorted({0, H // 2, H - 1}):
+            rows = sorted(set([0, 1, n - 1, n // 2] + [int(x) for x in rng.integers(0, n, size=max_rows)]
+                              + [int(x) for x in np.flatnonzero(mask[b] == 2)[:8]]))
+            ref, rc = oracle.forward_rows(*arrs, mask, prob.window, b, h, rows, dilation=prob.dilation,
+                                          causal=prob.causal, scale=prob.scale)
+            worst = max(worst, float(np.abs(o[b, rows, h] - ref).max()))
+            nnz_ok &= bool(np.array_equal(c[b, h, rows], rc))
+    tol = 2e-2 if prob.q.dtype.is_floating_point and prob.q.element_size() == 2 else 1e-4
+    return {"max_abs_err_sampled": worst, "tolerance": tol, "row_nnz_exact": nnz_ok,
+            "ok": bool(worst <= tol and nnz_ok)}
+
+
+def cpu_baseline(prob, budget_s=12.0):
+    """The fp64 oracle as it stands, on a bounded sample of the same workload
+    (whole heads, all rows), single BLAS thread; scaled to tokens/s of the
+    full job."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    B, n, H, D = prob.shape
+    arrs = [x.float().numpy() for x in (prob.q, prob.k, prob.v, prob.q_g, prob.k_g, prob.v_g)]
+    mask = prob.mask.numpy()
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    done, t0 = 0, time.perf_counter()
+    try:
+        if ctx:
+            ctx.__enter__()
+        for b in range(B):
+            for h in range(H):
+                oracle.forward_rows(*arrs, mask, prob.window, b, h, range(n), dilation=prob.dilation,
+                                    causal=prob.causal, scale=prob.scale)
+                done += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            if time.perf_counter() - t0 > budget_s:
+                break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    el = time.perf_counter() - t0
+    per_head = el / done
+    full = per_head * B * H
+    return {"value": B * n / full, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {B * H} (batch row, head) pairs, all {n} rows each, "
+                      f"{el:.1f} s, scaled to the full {B}x{H}-head job"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="longformer_base_n4096")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time direct launches instead of a graph replay")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU layout of this "
+              "path is a design note, not a measured configuration", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+
+    prob = workloads.by_name(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    run = Runner(prob, dev)
+    for _ in range(max(1, args.warmup)):
+        run.launch()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    mode = "eager"
+    graph = None
+    if not args.eager:
+        try:
+            ref = run.out.clone()
+            per = min(K, 50)
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                run.stream = s.cuda_stream
+                run.args = run.args[:-1] + (ctypes.c_void_p(s.cuda_stream),)
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=s):
+                    for _ in range(per):
+                        run.launch()
+            torch.cuda.current_stream().wait_stream(s)
+            graph.replay()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(ref, run.out):
+                raise RuntimeError("graph replay output differs from the eager launch")
+            mode = f"graph({per} launches per replay)"
+        except Exception as e:  # fall back to eager timing
+            print(f"graph capture unavailable ({e}); timing eager launches", file=sys.stderr)
+            graph = None
+            run.args = run.args[:-1] + (ctypes.c_void_p(torch.cuda.current_stream().cuda_stream),)
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    if graph is not None:
+        per = min(K, 50)
+        reps = max(1, K // per)
+        K = reps * per
+        start.record()
+        for _ in range(reps):
+            graph.replay()
+        end.record()
+    else:
+        start.record()
+        for _ in range(K):
+            run.launch()
+        end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(end) / K
+
+    B, n, H, D = prob.shape
+    flops = band_flops(prob)
+    achieved = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if prob.q.dtype == torch.bfloat16 else PEAK_F32_TFLOPS
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        ent = tr.get(args.workload)
+        if ent and ent.get("kernel_hash") == kernel_hash():
+            traffic = ent["bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
+    result = {
+        "metric": "sliding-window attn fwd tokens/s, n=4096 H=12 w=256/side bf16; MFMA util %",
+        "value": B * n / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if prob.q.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded N(0,1) q/k/v/q_g/k_g/v_g, mask per workload recipe)",
+        "config": {"workload": args.workload, "B": B, "n": n, "H": H, "D": D, "w": prob.window,
+                   "causal": prob.causal, "dilation": prob.dilation,
+                   "globals_per_row": [int(x) for x in (prob.mask == 2).sum(dim=1).tolist()],
+                   "timing": mode, "wall_s": round(t_wall, 3)},
+        "mfma_util_band": achieved / peak,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "kernel": "lf_attn_fwd<bf16>" if prob.q.dtype == torch.bfloat16 else "lf_attn_fwd<f32>",
+                     "flops_per_launch": flops, "algorithmic_bytes": algorithmic_bytes(prob),
+                     "kernel_hash": kernel_hash()},
+    }
+    if not args.no_check:
+        result["parity"] = check_parity(prob, run.out, run.row_nnz)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(prob)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

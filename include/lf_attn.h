@@ -1,0 +1,123 @@
+/*
+ * lf_attn.h — C ABI of the MI355X (gfx950) Longformer attention forward.
+ *
+ * One operation: the forward pass of Longformer's combined attention layer,
+ * i.e. a sliding window over a fixed number of diagonals of QK^T (optionally
+ * dilated per head, optionally causal) merged with symmetric global
+ * attention on a few selected tokens that uses its own Q_g/K_g/V_g
+ * projections.  Sources for the definition:
+ *   - sliding window, dilation, global attention, separate global
+ *     projections, banded QK^T: segmentfault.com Longformer summary,
+ *     sections "Sliding window", "Dilated sliding window", "Global
+ *     attention", "Linear projections for global attention",
+ *     "Implementation";
+ *   - 256 tokens per side, inclusive |i-j| <= window/2, global row and
+ *     column set in a boolean mask (a set union): ultralytics glossary
+ *     "Longformer", section "How Longformer attention works" and its worked
+ *     mask-count example;
+ *   - mask values 0 = no attention, 1 = local, 2 = global, sequence padded
+ *     to a multiple of the window: allenai/longformer README, "Usage".
+ *
+ * Definition computed, for every batch row b and head h (d = dilation[h],
+ * s = scale, D = 64), with W(i) = { i + k*d : -w <= k <= (causal ? 0 : w),
+ * 0 <= i + k*d < n }, Valid = { j : mask[b,j] != 0 }, G = { j : mask[b,j] == 2 }:
+ *   mask[b,i] == 1 (local row):  S(i) = (W(i) u G) n Valid,
+ *       out[b,i,h] = sum_{j in S(i)} softmax_j(s <q[b,i,h], k[b,j,h]>) v[b,j,h]
+ *   mask[b,i] == 2 (global row): S(i) = Valid,
+ *       out[b,i,h] = sum_{j in S(i)} softmax_j(s <q_g[b,i,h], k_g[b,j,h]>) v_g[b,j,h]
+ *   mask[b,i] == 0 (padding):    out[b,i,h] = 0, S(i) = {}
+ *   row_nnz[b,h,i] = |S(i)|.
+ * A global key inside a row's window is counted once.  Keys outside S(i)
+ * never influence out[b,i,h], whatever values they hold.
+ *
+ * Conventions of every entry point:
+ *   - All tensors are contiguous.  q, k, v, q_g, k_g, v_g and out are
+ *     [B, n, H, D] (token-major: element (b,i,h,d) at ((b*n + i)*H + h)*D + d),
+ *     of the dtype in the parameters.  mask is int8 [B, n].  row_nnz is
+ *     int32 [B, H, n].
+ *   - Device pointers are HIP device memory of the current device.  The
+ *     caller owns every buffer; the library allocates and frees nothing in
+ *     lf_attn_forward and never synchronises the stream there.
+ *   - Every argument is validated on the host before any HIP call, so every
+ *     error code below is returned without touching the GPU.
+ *   - Mask contents are not read on the host.  Under causal = 1 a mask
+ *     value 2 acts as 1 (global attention is not defined for the
+ *     autoregressive case).  Mask values other than 0/1/2 act as 0.
+ */
+#ifndef LF_ATTN_H
+#define LF_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LF_OK = 0,
+  LF_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, bad window/dilation/scale, aliasing */
+  LF_ERR_UNSUPPORTED = 2, /* D != 64, unknown dtype, H or max_global above the limits */
+  LF_ERR_WORKSPACE = 3,   /* workspace missing or smaller than lf_attn_workspace_bytes */
+  LF_ERR_HIP = 4          /* the HIP runtime refused the launch */
+} lf_status;
+
+typedef enum { LF_F32 = 0, LF_BF16 = 1 } lf_dtype;
+
+/* Limits of this build. */
+#define LF_HEAD_DIM 64
+#define LF_MAX_HEADS 64
+#define LF_MAX_GLOBAL 1024   /* global tokens per batch row */
+#define LF_MAX_SEQ (1 << 24)
+
+/* Bits of the device status word (lf_attn_device_status). */
+#define LF_DEV_TOO_MANY_GLOBALS 1 /* a batch row held more than max_global tokens with mask 2 */
+
+typedef struct {
+  int32_t B, n, H, D;        /* B, n, H >= 1; D must be 64 */
+  int32_t window;            /* one-sided w >= 0; the pages' attention_window is 2w */
+  const int32_t* dilation;   /* HOST array [H], each >= 1; NULL means all 1 */
+  int32_t causal;            /* 0 or 1 */
+  float scale;               /* score scale > 0; 0 means 1/sqrt(D) */
+  int32_t max_global;        /* upper bound on mask==2 tokens per batch row, 0..LF_MAX_GLOBAL */
+  int32_t dtype;             /* lf_dtype of q, k, v, q_g, k_g, v_g and out */
+} lf_attn_params;
+
+/* Bytes of device workspace lf_attn_forward needs for these parameters
+ * (status word, per-(b,h) arrival counters, split-sequence partial results
+ * of the global rows).  Returns 0 if the parameters are invalid. */
+size_t lf_attn_workspace_bytes(const lf_attn_params* p);
+
+/* Zero a freshly allocated workspace on `stream` (a hipStream_t; NULL is
+ * the default stream).  Needed once per allocation: every lf_attn_forward
+ * leaves the counters it uses back at zero when its kernel completes.
+ * Also clears the status word. */
+lf_status lf_attn_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Enqueue the forward on `stream` and return.  q_g, k_g, v_g may be NULL,
+ * meaning "the same as q, k, v" (the initial state of the global
+ * projections), and may alias q, k, v.  out must not overlap any input.
+ * row_nnz may be NULL.  out is fully overwritten, and so is row_nnz when
+ * given.  workspace must hold lf_attn_workspace_bytes(p) bytes initialised
+ * by lf_attn_workspace_init; two calls in flight at once must not share a
+ * workspace.  LF_OK means the arguments were valid and the launch was
+ * accepted; faults during execution surface at the caller's next
+ * synchronisation. */
+lf_status lf_attn_forward(const lf_attn_params* p,
+                          const void* q, const void* k, const void* v,
+                          const void* q_g, const void* k_g, const void* v_g,
+                          const int8_t* mask, void* out, int32_t* row_nnz,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Debug helper: synchronise `stream`, then read the device status word of
+ * `workspace` into *status (LF_DEV_* bits; 0 = no condition seen). */
+lf_status lf_attn_device_status(const void* workspace, void* stream, int32_t* status);
+
+/* Static description of a status code. */
+const char* lf_status_str(int32_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LF_ATTN_H */

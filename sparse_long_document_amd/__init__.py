@@ -1,0 +1,288 @@
+"""Longformer combined sliding-window + global attention forward on MI355X.
+
+Thin Python binding over the C ABI of ``include/lf_attn.h`` (library
+``liblf_attn.so`` built in-tree by ``sparse_long_document_amd.build``).  It
+only marshals arguments: every step of the attention runs in the HIP
+kernels.  PyTorch provides device memory and streams.  There is no CPU
+fallback: without the built library, or without a GPU, ``forward`` raises.
+
+Entry points (same names as the C ABI where they wrap it):
+  * ``forward`` -> ``lf_attn_forward``
+  * ``workspace_bytes`` -> ``lf_attn_workspace_bytes``
+  * ``device_status`` -> ``lf_attn_device_status``
+  * ``pad_to_window_size`` and ``merge_masks``: input helpers for the mask
+    conventions of the allenai README ("Usage": pad the sequence to a
+    multiple of the attention window; mask 0/1/2) and of the Hugging Face
+    ``global_attention_mask`` (ultralytics glossary, "Training and results").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = [
+    "forward", "workspace_bytes", "device_status", "pad_to_window_size",
+    "merge_masks", "library", "LfError", "LF_MAX_GLOBAL", "LF_MAX_HEADS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblf_attn.so")
+
+LF_OK, LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED, LF_ERR_WORKSPACE, LF_ERR_HIP = range(5)
+LF_F32, LF_BF16 = 0, 1
+LF_HEAD_DIM = 64
+LF_MAX_HEADS = 64
+LF_MAX_GLOBAL = 1024
+LF_DEV_TOO_MANY_GLOBALS = 1
+
+SYMBOLS = ("lf_attn_workspace_bytes", "lf_attn_workspace_init", "lf_attn_forward",
+           "lf_attn_device_status", "lf_status_str")
+
+
+class LfError(RuntimeError):
+    """A non-OK status from the C ABI."""
+
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {status_str(code)} (status {code})")
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("n", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("D", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("dilation", ctypes.POINTER(ctypes.c_int32)), ("causal", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("max_global", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def library() -> ctypes.CDLL:
+    """Load ``liblf_attn.so``; raise if it has not been built."""
+    global _lib
+    with _lib_lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with "
+                    "`python -m sparse_long_document_amd.build`")
+            lib = ctypes.CDLL(LIB_PATH)
+            vp, sz = ctypes.c_void_p, ctypes.c_size_t
+            lib.lf_attn_workspace_bytes.argtypes = [ctypes.POINTER(Params)]
+            lib.lf_attn_workspace_bytes.restype = sz
+            lib.lf_attn_workspace_init.argtypes = [vp, sz, vp]
+            lib.lf_attn_workspace_init.restype = ctypes.c_int
+            lib.lf_attn_forward.argtypes = [ctypes.POINTER(Params), vp, vp, vp, vp, vp, vp,
+                                            vp, vp, vp, vp, sz, vp]
+            lib.lf_attn_forward.restype = ctypes.c_int
+            lib.lf_attn_device_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
+            lib.lf_attn_device_status.restype = ctypes.c_int
+            lib.lf_status_str.argtypes = [ctypes.c_int32]
+            lib.lf_status_str.restype = ctypes.c_char_p
+            _lib = lib
+    return _lib
+
+
+def status_str(code: int) -> str:
+    return library().lf_status_str(int(code)).decode()
+
+
+def make_params(B: int, n: int, H: int, D: int, window: int,
+                dilation: Optional[Sequence[int]], causal: bool, scale: Optional[float],
+                max_global: int, dtype: torch.dtype):
+    """Build the C parameter block.  Returns (params, keepalive)."""
+    dil = None
+    if dilation is not None:
+        dil = (ctypes.c_int32 * len(dilation))(*[int(x) for x in dilation])
+    p = Params(
+        B=B, n=n, H=H, D=D, window=int(window),
+        dilation=ctypes.cast(dil, ctypes.POINTER(ctypes.c_int32)) if dil is not None else None,
+        causal=int(bool(causal)), scale=0.0 if scale is None else float(scale),
+        max_global=int(max_global),
+        dtype=LF_BF16 if dtype == torch.bfloat16 else (LF_F32 if dtype == torch.float32 else 99),
+    )
+    return p, dil
+
+
+def workspace_bytes(B: int, n: int, H: int, window: int, dilation=None, causal=False,
+                    scale=None, max_global: int = 0, dtype=torch.bfloat16, D: int = LF_HEAD_DIM) -> int:
+    p, _keep = make_params(B, n, H, D, window, dilation, causal, scale, max_global, dtype)
+    return int(library().lf_attn_workspace_bytes(ctypes.byref(p)))
+
+
+_ws_cache = {}
+_ws_lock = threading.Lock()
+
+
+def _workspace(nbytes: int, device: torch.device, stream: int, layout) -> torch.Tensor:
+    """A zero-initialised workspace of at least nbytes, cached per
+    (device, stream): calls on one stream are ordered, so they may share it.
+    Each call leaves its arrival counters at zero, but where they sit depends
+    on (B, H), so a change of layout re-initialises the buffer."""
+    key = (device.index, stream)
+    with _ws_lock:
+        ws, last = _ws_cache.get(key, (None, None))
+        if ws is None or ws.numel() < nbytes or last != layout:
+            if ws is None or ws.numel() < nbytes:
+                ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            st = library().lf_attn_workspace_init(ctypes.c_void_p(ws.data_ptr()),
+                                                  ctypes.c_size_t(ws.numel()),
+                                                  ctypes.c_void_p(stream))
+            if st != LF_OK:
+                raise LfError(st, "lf_attn_workspace_init")
+            _ws_cache[key] = (ws, layout)
+        return ws
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (this library has no CPU path)")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+            q_g: Optional[torch.Tensor] = None, k_g: Optional[torch.Tensor] = None,
+            v_g: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
+            window: int = 256, dilation: Optional[Sequence[int]] = None,
+            causal: bool = False, scale: Optional[float] = None,
+            max_global: Optional[int] = None, return_row_nnz: bool = False,
+            validate: bool = True, out: Optional[torch.Tensor] = None,
+            row_nnz: Optional[torch.Tensor] = None):
+    """Longformer attention forward (``lf_attn_forward``).
+
+    q, k, v, q_g, k_g, v_g: [B, n, H, 64] bf16 or fp32 GPU tensors, contiguous
+    (q_g/k_g/v_g default to q/k/v).  mask: [B, n] int8 (other integer dtypes
+    are converted) with 0 = no attention, 1 = local, 2 = global; None means
+    all local.  window: one-sided w.  dilation: per-head stride.  Returns
+    out (and row_nnz int32 [B, H, n] if asked).
+
+    validate=True checks mask contents on the host (one device sync) and
+    derives max_global from the mask; validate=False trusts the caller
+    (max_global then defaults to the library limit unless given).
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, n, H, D]")
+    B, n, H, D = q.shape
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("q must be a GPU tensor (this library has no CPU path)")
+    dtype = q.dtype
+    q_g = q if q_g is None else q_g
+    k_g = k if k_g is None else k_g
+    v_g = v if v_g is None else v_g
+    for name, t in (("q", q), ("k", k), ("v", v), ("q_g", q_g), ("k_g", k_g), ("v_g", v_g)):
+        _check_tensor(name, t, (B, n, H, D), dtype, device)
+    if mask is None:
+        mask = torch.ones((B, n), dtype=torch.int8, device=device)
+    elif mask.dtype != torch.int8:
+        mask = mask.to(torch.int8)
+    mask = mask.contiguous()
+    _check_tensor("mask", mask, (B, n), torch.int8, device)
+    if validate:
+        bad = ~((mask == 0) | (mask == 1) | (mask == 2))
+        if bool(bad.any()):
+            raise ValueError("mask values must be 0, 1 or 2")
+        g = int((mask == 2).sum(dim=1).max().item())
+        if causal and g > 0:
+            raise ValueError("causal attention with global tokens is undefined")
+        if max_global is None:
+            max_global = g
+        elif g > max_global:
+            raise ValueError(f"mask has {g} global tokens in a row, max_global={max_global}")
+        if max_global > LF_MAX_GLOBAL:
+            raise ValueError(f"at most {LF_MAX_GLOBAL} global tokens per row are supported")
+    if max_global is None:
+        max_global = 0 if causal else min(n, LF_MAX_GLOBAL)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, (B, n, H, D), dtype, device)
+    if return_row_nnz and row_nnz is None:
+        row_nnz = torch.empty((B, H, n), dtype=torch.int32, device=device)
+    if row_nnz is not None:
+        _check_tensor("row_nnz", row_nnz, (B, H, n), torch.int32, device)
+
+    p, _keep = make_params(B, n, H, D, window, dilation, causal, scale, max_global, dtype)
+    lib = library()
+    need = int(lib.lf_attn_workspace_bytes(ctypes.byref(p)))
+    if need == 0:
+        raise LfError(LF_ERR_INVALID_ARG, "lf_attn_workspace_bytes")
+    stream = torch.cuda.current_stream(device).cuda_stream
+    ws = _workspace(need, device, stream, (B, H))
+    vp = ctypes.c_void_p
+    st = lib.lf_attn_forward(
+        ctypes.byref(p), vp(q.data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()),
+        vp(q_g.data_ptr()), vp(k_g.data_ptr()), vp(v_g.data_ptr()), vp(mask.data_ptr()),
+        vp(out.data_ptr()), vp(row_nnz.data_ptr() if row_nnz is not None else None),
+        vp(ws.data_ptr()), ctypes.c_size_t(ws.numel()), vp(stream))
+    if st != LF_OK:
+        raise LfError(st, "lf_attn_forward")
+    if return_row_nnz:
+        return out, row_nnz
+    return out
+
+
+def device_status(device: Optional[torch.device] = None) -> int:
+    """Synchronise and read the device status word of the workspace used on
+    the current stream (``lf_attn_device_status``); 0 = nothing flagged."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    stream = torch.cuda.current_stream(device).cuda_stream
+    ws, _layout = _ws_cache.get((device.index, stream), (None, None))
+    if ws is None:
+        return 0
+    val = ctypes.c_int32(0)
+    st = library().lf_attn_device_status(ctypes.c_void_p(ws.data_ptr()), ctypes.c_void_p(stream),
+                                         ctypes.byref(val))
+    if st != LF_OK:
+        raise LfError(st, "lf_attn_device_status")
+    return int(val.value)
+
+
+def pad_to_window_size(x: torch.Tensor, mask: torch.Tensor, attention_window: int, pad_value=0):
+    """Pad dim 1 of ``x`` (ids [B, n] or tensors [B, n, ...]) and of ``mask``
+    ([B, n]) up to a multiple of ``attention_window`` (the two-sided window,
+    2w).  Padding tokens get ``pad_value`` in x and 0 (no attention) in the
+    mask, as the allenai README's usage step prescribes before the model
+    call.  Returns (x, mask); unchanged if already a multiple."""
+    if attention_window <= 0:
+        raise ValueError("attention_window must be positive")
+    n = x.shape[1]
+    if mask.shape[:2] != x.shape[:2]:
+        raise ValueError("x and mask disagree on [B, n]")
+    pad = (-n) % attention_window
+    if pad == 0:
+        return x, mask
+    xs = list(x.shape)
+    xs[1] = pad
+    x = torch.cat([x, torch.full(xs, pad_value, dtype=x.dtype, device=x.device)], dim=1)
+    ms = list(mask.shape)
+    ms[1] = pad
+    mask = torch.cat([mask, torch.zeros(ms, dtype=mask.dtype, device=mask.device)], dim=1)
+    return x, mask
+
+
+def merge_masks(attention_mask: torch.Tensor, global_attention_mask: torch.Tensor) -> torch.Tensor:
+    """Turn a 0/1 attention mask plus a 0/1 global-attention mask into the
+    0/1/2 mask (int8): padding stays 0, attended tokens are 1, attended
+    global tokens are 2."""
+    if attention_mask.shape != global_attention_mask.shape:
+        raise ValueError("mask shapes differ")
+    a = (attention_mask != 0).to(torch.int8)
+    g = (global_attention_mask != 0).to(torch.int8)
+    return a * (1 + g)

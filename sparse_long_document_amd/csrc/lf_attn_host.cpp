@@ -1,0 +1,181 @@
+// Host side of the C ABI declared in include/lf_attn.h: argument
+// validation (before any HIP call), workspace layout, launch planning.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "lf_attn.h"
+#include "lf_attn_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Plan {
+  int use_globals = 0;
+  int S = 0;
+  int64_t tiles_per_b = 0;
+  int dil[LF_MAX_HEADS];
+  int tile0[LF_MAX_HEADS + 1];
+  size_t elem = 0;
+  size_t tensor_bytes = 0;
+  size_t ws_tickets_off = 0;
+  size_t ws_partials_off = 0;
+  size_t ws_bytes = 0;
+};
+
+// Validates the parameter block and derives the launch plan.  No HIP calls.
+lf_status make_plan(const lf_attn_params* p, Plan& pl) {
+  if (!p) return LF_ERR_INVALID_ARG;
+  if (p->B <= 0 || p->n <= 0 || p->H <= 0 || p->D <= 0) return LF_ERR_INVALID_ARG;
+  if (p->window < 0) return LF_ERR_INVALID_ARG;
+  if (p->causal != 0 && p->causal != 1) return LF_ERR_INVALID_ARG;
+  if (!std::isfinite(p->scale) || p->scale < 0.f) return LF_ERR_INVALID_ARG;
+  if (p->max_global < 0) return LF_ERR_INVALID_ARG;
+  if (p->D != LF_HEAD_DIM) return LF_ERR_UNSUPPORTED;
+  if (p->dtype != LF_F32 && p->dtype != LF_BF16) return LF_ERR_UNSUPPORTED;
+  if (p->H > LF_MAX_HEADS || p->max_global > LF_MAX_GLOBAL || p->n > LF_MAX_SEQ) return LF_ERR_UNSUPPORTED;
+  const int64_t tokens = (int64_t)p->B * p->n;
+  if (tokens > INT32_MAX) return LF_ERR_UNSUPPORTED;
+
+  pl.elem = p->dtype == LF_BF16 ? 2 : 4;
+  pl.tensor_bytes = (size_t)tokens * p->H * p->D * pl.elem;
+
+  int64_t tiles = 0;
+  for (int h = 0; h < p->H; ++h) {
+    const int d = p->dilation ? p->dilation[h] : 1;
+    if (d < 1) return LF_ERR_INVALID_ARG;
+    pl.dil[h] = d;
+    pl.tile0[h] = (int)tiles;
+    // positions r, r+d, ... < n: residues r < n % d have n/d + 1 of them
+    const int64_t qn = p->n / d, rm = p->n % d;
+    const int64_t T1 = (qn + 1 + lf::kTileQ - 1) / lf::kTileQ;
+    const int64_t T0 = (qn + lf::kTileQ - 1) / lf::kTileQ;
+    tiles += rm * T1 + (d - rm) * T0;
+    if (tiles > (int64_t)1 << 26) return LF_ERR_UNSUPPORTED;
+  }
+  pl.tile0[p->H] = (int)tiles;
+  pl.tiles_per_b = tiles;
+  if (tiles * p->B > (int64_t)1 << 30) return LF_ERR_UNSUPPORTED;
+
+  pl.use_globals = (p->causal == 0 && p->max_global > 0) ? 1 : 0;
+  pl.S = (p->n + lf::kGlobalChunk - 1) / lf::kGlobalChunk;
+  const size_t bh = (size_t)p->B * p->H;
+  pl.ws_tickets_off = kAlign;
+  pl.ws_partials_off = pl.ws_tickets_off + align_up(bh * sizeof(int32_t), kAlign);
+  size_t partial_bytes = 0;
+  if (pl.use_globals)
+    partial_bytes = bh * (size_t)p->max_global * (size_t)pl.S * lf::kPartialStride * sizeof(float);
+  pl.ws_bytes = pl.ws_partials_off + align_up(partial_bytes, kAlign);
+  return LF_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lf_attn_workspace_bytes(const lf_attn_params* p) {
+  Plan pl;
+  if (make_plan(p, pl) != LF_OK) return 0;
+  return pl.ws_bytes;
+}
+
+lf_status lf_attn_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || workspace_bytes < kAlign) return LF_ERR_WORKSPACE;
+  const hipError_t e = hipMemsetAsync(workspace, 0, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LF_OK : LF_ERR_HIP;
+}
+
+lf_status lf_attn_forward(const lf_attn_params* p, const void* q, const void* k, const void* v,
+                          const void* q_g, const void* k_g, const void* v_g, const int8_t* mask, void* out,
+                          int32_t* row_nnz, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan pl;
+  const lf_status st = make_plan(p, pl);
+  if (st != LF_OK) return st;
+  if (!q || !k || !v || !mask || !out) return LF_ERR_INVALID_ARG;
+  if (!q_g) q_g = q;
+  if (!k_g) k_g = k;
+  if (!v_g) v_g = v;
+  const size_t tb = pl.tensor_bytes;
+  const size_t mb = (size_t)p->B * p->n;
+  const size_t nb = (size_t)p->B * p->H * p->n * sizeof(int32_t);
+  const void* ins[6] = {q, k, v, q_g, k_g, v_g};
+  for (const void* in : ins)
+    if (overlaps(out, tb, in, tb)) return LF_ERR_INVALID_ARG;
+  if (overlaps(out, tb, mask, mb)) return LF_ERR_INVALID_ARG;
+  if (row_nnz) {
+    for (const void* in : ins)
+      if (overlaps(row_nnz, nb, in, tb)) return LF_ERR_INVALID_ARG;
+    if (overlaps(row_nnz, nb, out, tb) || overlaps(row_nnz, nb, mask, mb)) return LF_ERR_INVALID_ARG;
+  }
+  if (!workspace || workspace_bytes < pl.ws_bytes) return LF_ERR_WORKSPACE;
+  if (overlaps(workspace, pl.ws_bytes, out, tb)) return LF_ERR_INVALID_ARG;
+
+  lf::KernelParams kp;
+  std::memset(&kp, 0, sizeof(kp));
+  kp.q = q;
+  kp.k = k;
+  kp.v = v;
+  kp.qg = q_g;
+  kp.kg = k_g;
+  kp.vg = v_g;
+  kp.mask = mask;
+  kp.out = out;
+  kp.row_nnz = row_nnz;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  kp.status = reinterpret_cast<int32_t*>(ws);
+  kp.tickets = reinterpret_cast<int32_t*>(ws + pl.ws_tickets_off);
+  kp.partials = reinterpret_cast<float*>(ws + pl.ws_partials_off);
+  kp.B = p->B;
+  kp.n = p->n;
+  kp.H = p->H;
+  kp.w = p->window;
+  kp.causal = p->causal;
+  kp.max_global = p->max_global;
+  kp.use_globals = pl.use_globals;
+  const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / std::sqrt((double)p->D);
+  kp.c = (float)(scale * 1.4426950408889634);  // log2(e)
+  kp.tiles_per_b = (int32_t)pl.tiles_per_b;
+  kp.n_band = (int32_t)(pl.tiles_per_b * p->B);
+  kp.n_glob = pl.use_globals ? p->B * p->H * pl.S : 0;
+  kp.n_glob_pad = (kp.n_glob + 7) / 8 * 8;
+  kp.S = pl.S;
+  for (int h = 0; h < p->H; ++h) {
+    kp.dil[h] = pl.dil[h];
+    kp.tile0[h] = pl.tile0[h];
+  }
+  kp.tile0[p->H] = pl.tile0[p->H];
+  const int e = lf::launch_forward(kp, p->dtype, stream);
+  return e == 0 ? LF_OK : LF_ERR_HIP;
+}
+
+lf_status lf_attn_device_status(const void* workspace, void* stream, int32_t* status) {
+  if (!workspace || !status) return LF_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(status, workspace, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess) return LF_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return LF_ERR_HIP;
+  return LF_OK;
+}
+
+const char* lf_status_str(int32_t s) {
+  switch (s) {
+    case LF_OK: return "ok";
+    case LF_ERR_INVALID_ARG: return "invalid argument";
+    case LF_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LF_ERR_WORKSPACE: return "workspace missing or too small";
+    case LF_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

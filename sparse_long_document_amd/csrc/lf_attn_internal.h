@@ -1,0 +1,49 @@
+// Internal interface between the host entry points (lf_attn_host.cpp) and
+// the device code (lf_attn_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lf_attn.h"
+
+namespace lf {
+
+// Tiling constants shared by the host planner and the kernels.
+constexpr int kHeadDim = 64;       // D
+constexpr int kTileQ = 64;         // query rows of one band workgroup
+constexpr int kBlockK = 32;        // keys per inner block (M of the 32x32 MFMA)
+constexpr int kWaves = 4;          // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kGlobalChunk = 512;  // keys per split of a global row
+constexpr int kPartialStride = 68; // floats per partial record: m, l, count, pad, O[64]
+
+// Everything one launch needs, passed by value as the kernel argument.
+struct KernelParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* qg;
+  const void* kg;
+  const void* vg;
+  const int8_t* mask;
+  void* out;
+  int32_t* row_nnz;    // may be null
+  int32_t* status;     // device status word
+  int32_t* tickets;    // [B*H] arrival counters of the global-row splits
+  float* partials;     // [B][H][max_global][S][kPartialStride]
+  int32_t B, n, H, w, causal, max_global, use_globals;
+  float c;             // score scale * log2(e)
+  int32_t tiles_per_b; // band workgroups per batch row
+  int32_t n_band;      // band workgroups in the launch
+  int32_t n_glob;      // global-row workgroups in the launch
+  int32_t n_glob_pad;  // n_glob rounded up to a multiple of 8 (XCD count)
+  int32_t S;           // splits of a global row
+  int32_t dil[LF_MAX_HEADS];
+  int32_t tile0[LF_MAX_HEADS + 1];  // first band tile of each head within a batch row
+};
+
+// Launches the forward kernel.  Returns the hipError_t value as int.
+int launch_forward(const KernelParams& kp, int dtype, void* stream);
+
+}  // namespace lf

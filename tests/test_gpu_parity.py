@@ -1,0 +1,218 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances: max |out - oracle| <= 2e-2 for bf16 inputs and <= 1e-4 for
+fp32 inputs (fp32 accumulation on the GPU); row_nnz (pairs scored per row)
+bit-exact everywhere.  Small problems are compared element by element with
+the full oracle; the five named workloads at full size are checked on
+sampled rows that the oracle computes one by one, in the same launch
+configuration the benchmark times.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_long_document_amd as lf
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lf.library()
+
+
+def _dev(prob):
+    d = torch.device("cuda")
+    t = [x.to(d) for x in (prob.q, prob.k, prob.v)]
+    if prob.aliased_global:
+        g = [None, None, None]
+    else:
+        g = [x.to(d) for x in (prob.q_g, prob.k_g, prob.v_g)]
+    return t, g, prob.mask.to(d)
+
+
+def run_gpu(prob, validate=True, max_global=None):
+    _say(f"[gpu] {prob.name} shape={prob.shape} w={prob.window} dil={prob.dilation} "
+         f"causal={prob.causal} dtype={prob.q.dtype}")
+    t, g, mask = _dev(prob)
+    out, nnz = lf.forward(*t, *g, mask=mask, window=prob.window, dilation=prob.dilation,
+                          causal=prob.causal, scale=prob.scale, return_row_nnz=True,
+                          validate=validate, max_global=max_global)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), nnz.cpu().numpy().astype(np.int64)
+
+
+def _np(prob):
+    return [x.float().numpy() for x in (prob.q, prob.k, prob.v, prob.q_g, prob.k_g, prob.v_g)]
+
+
+def run_oracle(prob):
+    return oracle.forward(*_np(prob), prob.mask.numpy(), prob.window, dilation=prob.dilation,
+                          causal=prob.causal, scale=prob.scale)
+
+
+def check_full(prob):
+    out, nnz = run_gpu(prob)
+    ref, rnnz = run_oracle(prob)
+    np.testing.assert_array_equal(nnz, rnnz)
+    err = np.abs(out - ref).max() if out.size else 0.0
+    _say(f"      max abs err {err:.3e}")
+    assert err <= TOL[prob.q.dtype], err
+    pad = np.broadcast_to((prob.mask.numpy() == 0)[:, :, None, None], out.shape)
+    assert (out[pad] == 0).all()
+    return out, nnz
+
+
+SMALL = [
+    dict(B=1, n=1, H=1, window=0),
+    dict(B=1, n=5, H=2, window=2),
+    dict(B=1, n=63, H=1, window=7),
+    dict(B=1, n=64, H=1, window=64),
+    dict(B=1, n=65, H=2, window=31),
+    dict(B=1, n=200, H=2, window=16, n_global=3),
+    dict(B=2, n=200, H=1, window=100, n_global=1, pad_tail=37),
+    dict(B=1, n=333, H=3, window=40, dilation=[1, 2, 3]),
+    dict(B=1, n=333, H=3, window=40, dilation=[1, 2, 3], n_global=5),
+    dict(B=1, n=300, H=2, window=20, causal=True),
+    dict(B=1, n=301, H=3, window=33, causal=True, dilation=[3, 1, 2]),
+    dict(B=1, n=257, H=1, window=300),
+    dict(B=1, n=190, H=1, window=500, causal=True),
+    dict(B=2, n=520, H=2, window=24, n_global=40, zero_frac=0.05),
+    dict(B=1, n=1100, H=2, window=64, n_global=70),
+    dict(B=1, n=1100, H=1, window=64, n_global=2, pad_tail=300, dilation=[2]),
+    dict(B=3, n=130, H=2, window=9, n_global=2, zero_frac=0.3),
+    dict(B=1, n=700, H=2, window=64, dilation=[5, 7]),
+    dict(B=1, n=96, H=1, window=3, global_positions=[0, 1, 2, 95]),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("idx", range(len(SMALL)))
+def test_small_full_parity(idx, dtype):
+    kw = dict(SMALL[idx])
+    prob = workloads.random_problem(100 + idx, dtype=dtype, name=f"small{idx}", **kw)
+    check_full(prob)
+
+
+def test_aliased_global_projections():
+    prob = workloads.random_problem(7, B=1, n=400, H=2, window=30, n_global=4,
+                                    aliased_global=True, name="aliased")
+    check_full(prob)
+
+
+def test_scale_argument():
+    prob = workloads.random_problem(8, B=1, n=300, H=1, window=30, n_global=2, scale=0.3, name="scale")
+    check_full(prob)
+
+
+def test_single_head_fp32_workload_full():
+    check_full(workloads.single_head_fp32_n512())
+
+
+def test_rows_sum_to_one_through_api():
+    prob = workloads.random_problem(9, B=1, n=500, H=2, window=50, n_global=3, pad_tail=20, name="ones")
+    ones = torch.ones_like(prob.v)
+    prob.v = ones
+    prob.v_g = ones.clone()
+    out, _ = run_gpu(prob)
+    live = (prob.mask.numpy() != 0)[:, :, None, None]
+    ref = np.broadcast_to(np.where(live, 1.0, 0.0), out.shape)
+    assert np.abs(out - ref).max() <= 2e-2
+
+
+def test_deterministic_and_repeatable():
+    prob = workloads.random_problem(10, B=2, n=1500, H=3, window=70, n_global=9, pad_tail=100, name="det")
+    a, na = run_gpu(prob)
+    small = workloads.random_problem(11, B=1, n=600, H=1, window=10, n_global=2, name="other")
+    run_gpu(small)
+    b, nb = run_gpu(prob)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(na, nb)
+
+
+def test_too_many_globals_flagged():
+    prob = workloads.random_problem(12, B=1, n=300, H=1, window=10, n_global=5, name="toomany")
+    torch.cuda.synchronize()
+    # fresh stream => fresh workspace with a clear status word
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        t, g, mask = _dev(prob)
+        lf.forward(*t, *g, mask=mask, window=10, validate=False, max_global=2)
+        assert lf.device_status() & lf.LF_DEV_TOO_MANY_GLOBALS
+    s2 = torch.cuda.Stream()
+    with torch.cuda.stream(s2):
+        lf.forward(*t, *g, mask=mask, window=10, validate=False, max_global=5)
+        assert lf.device_status() == 0
+
+
+# ---------------------------------------------------------------------------
+# Named workloads at full size, sampled rows
+# ---------------------------------------------------------------------------
+
+def _sample_rows(n, w, mask_b, rng, extra=()):
+    base = {0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, w - 1, w, w + 1,
+            n // 2, n - w - 1, n - w, n - 2, n - 1}
+    base |= set(int(x) for x in rng.integers(0, n, size=24))
+    base |= set(int(x) for x in np.flatnonzero(mask_b == 2)[:20])
+    nz = np.flatnonzero(mask_b == 0)
+    if nz.size:
+        base |= {int(nz[0]) - 2, int(nz[0]) - 1, int(nz[0]), int(nz[-1])}
+    base |= set(extra)
+    return sorted(x for x in base if 0 <= x < n)
+
+
+@pytest.mark.parametrize("name", ["longformer_base_n4096", "qa_padded_b2_n4096",
+                                  "charlm_causal_dilated_n23040", "led_large_n16384"])
+def test_workload_sampled_parity(name):
+    prob = workloads.by_name(name)
+    B, n, H, D = prob.shape
+    max_global = prob.max_global()
+    out, nnz = run_gpu(prob, validate=False, max_global=max_global)
+    arrs = _np(prob)
+    mask = prob.mask.numpy()
+    rng = np.random.default_rng(0)
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            rows = _sample_rows(n, prob.window, mask[b], rng)
+            ref, rnnz = oracle.forward_rows(*arrs, mask, prob.window, b, h, rows,
+                                            dilation=prob.dilation, causal=prob.causal,
+                                            scale=prob.scale)
+            np.testing.assert_array_equal(nnz[b, h, rows], rnnz)
+            err = np.abs(out[b, rows, h] - ref).max()
+            worst = max(worst, err)
+            assert err <= TOL[prob.q.dtype], (b, h, err)
+    # pair counts: closed forms where the workload has one
+    if name == "longformer_base_n4096":
+        assert nnz.sum() == 2043134 * 12
+    if name == "charlm_causal_dilated_n23040":
+        assert nnz.sum() == 93242880
+    assert (out[np.broadcast_to((mask == 0)[:, :, None, None], out.shape)] == 0).all()
+    _say(f"      {name}: worst sampled abs err {worst:.3e}")
+
+
+def test_longformer_base_two_heads_full():
+    """The metric workload, every row of two heads against the full oracle."""
+    prob = workloads.longformer_base_n4096()
+    out, nnz = run_gpu(prob, validate=False, max_global=1)
+    arrs = _np(prob)
+    mask = prob.mask.numpy()
+    for h in (0, 11):
+        ref, rnnz = oracle.forward_rows(*arrs, mask, prob.window, 0, h, range(4096))
+        np.testing.assert_array_equal(nnz[0, h], rnnz)
+        err = np.abs(out[0, :, h] - ref).max()
+        _say(f"      head {h}: max abs err {err:.3e}")
+        assert err <= 2e-2
