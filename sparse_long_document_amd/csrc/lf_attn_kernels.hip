@@ -5,10 +5,10 @@
 //     (batch row b, head h, residue class r of the head's dilation d).  A
 //     dilated window over positions {r, r+d, r+2d, ...} is a plain window
 //     over that subsequence, so each residue class is handled as an
-//     undilated sequence with row stride d*H*D (segmentfault Longformer
-//     summary, "Dilated sliding window": the dilated window keeps the cost
-//     of the plain one).  They write local rows (mask 1) and zero rows
-//     (mask 0);
+//     undilated sequence whose neighbours are d tokens apart (segmentfault
+//     Longformer summary, "Dilated sliding window": the dilated window
+//     keeps the cost of the plain one).  They write local rows (mask 1)
+//     and zero rows (mask 0);
 //   * global-row workgroups own one split of kGlobalChunk keys of one
 //     (b, h) for every global token of b: each global token attends to all
 //     tokens with the global projections (segmentfault summary, "Global
@@ -17,18 +17,21 @@
 //     workspace; the last split to arrive merges them and writes the rows.
 //
 // Inner block (both kinds): 32 keys x 64 queries per wave.
-//   S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 key rows, B = 32 query
-//   columns, K-dim = head dim).  In the 32x32 accumulator a lane owns one
-//   column (a query) and 16 of its 32 keys; the other 16 sit in lane ^ 32.
-//   So the softmax row max and row sum are in-lane plus one lane swap.
-//   The accumulator, rounded to bf16, is directly the B operand of
-//   O^T = V^T P^T (A = 32 head-dim rows of V^T read from LDS, B = P^T), with
-//   the key order of P^T as the accumulator holds it and V^T read in the
-//   same order.  Only V goes through LDS, transposed on the way in.
-//   Softmax is online in base 2 (scale*log2e folded into one FMA), fp32,
-//   with a lazy rescale: the running reference max only moves when a block
-//   max exceeds it by more than 2^8, which leaves the result exact while
-//   skipping most accumulator rescales.
+//   S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 key rows straight
+//   from global memory into registers, B = 32 query columns, K-dim = head
+//   dim).  In the 32x32 accumulator a lane owns one column (a query) and 16
+//   of its 32 keys; the other 16 sit in lane ^ 32, so the softmax row max
+//   is in-lane plus one lane exchange.  The accumulator, rounded to
+//   bf16, is directly the B operand of O^T = V^T P^T.  V rows travel from
+//   global memory to LDS with direct-to-LDS loads (no registers, no VALU)
+//   and come back as the V^T A operand through ds_read_b64_tr_b16, whose
+//   16-lane transpose hands each lane 4 keys of one head dim.  Softmax is
+//   online in base 2 (scale*log2e folded into one FMA), fp32, with a lazy
+//   rescale: the running reference max only moves when a block max exceeds
+//   it by more than 2^8, which leaves the result exact while skipping most
+//   accumulator rescales.
+//   Each wave fetches its next block (K into registers, V into the other
+//   half of its LDS double buffer) while it computes the current one.
 //
 // The key range of a band tile (kTileQ + 2w keys) is split over the 4 waves
 // of the workgroup block by block; their partial results are merged
@@ -37,6 +40,9 @@
 // global key already inside the row's window is not counted twice
 // (ultralytics glossary worked example: the window and the global
 // row/column are OR-ed into one boolean pattern).
+//
+// The fp32 instantiation computes in true fp32 (v_mfma_f32_32x32x2_f32, P
+// kept in fp32) with V staged through registers.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,26 +55,50 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+#define LDS_AS __attribute__((address_space(3)))
+
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
 
-// LDS staging of one 32-key V block, per wave.
-//   bf16: V^T [64 head dims][kVtStride keys] (transposed)
-//   f32:  V   [32 keys][kVStrideF32 dims]
-constexpr int kVtStride = 40;      // bf16 elements per V^T row (32 + pad)
-constexpr int kVStrideF32 = 68;    // floats per V row (64 + pad)
-constexpr int kStageBytesBf16 = kHeadDim * kVtStride * 2;
-constexpr int kStageBytesF32 = kBlockK * kVStrideF32 * 4;
-constexpr int kStageBytes = kStageBytesF32 > kStageBytesBf16 ? kStageBytesF32 : kStageBytesBf16;
 // Merge of partial outputs: 2 slots of 64 lanes x 64 floats.
 constexpr int kMergeSlotFloats = 64 * 64;
 constexpr int kMergeBytes = 2 * kMergeSlotFloats * 4;
-constexpr int kBufBytes = (kWaves * kStageBytes > kMergeBytes) ? kWaves * kStageBytes : kMergeBytes;
+
+// Per-wave LDS area: two stages, each holding one key block of K rows then
+// one of V rows (32 rows of 64 head dims each), filled by direct-to-LDS
+// loads while the other stage is consumed.
+template <bool B16>
+struct Lay {
+  static constexpr int kElt = B16 ? 2 : 4;
+  static constexpr int kRowBytes = kHeadDim * kElt;      // 128 | 256
+  static constexpr int kChunks = kRowBytes / 16;         // 16-byte chunks per row
+  static constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows covered by one wave-wide load
+  static constexpr int kLoads = kBlockK / kRowsPerLoad;  // loads per block and tensor
+  static constexpr int kBlockBytes = kBlockK * kRowBytes;
+  static constexpr int kStageBytes = 2 * kBlockBytes;
+  static constexpr int kWaveBytes = 2 * kStageBytes;
+  static constexpr int kBufBytes = kWaves * kWaveBytes > kMergeBytes ? kWaves * kWaveBytes : kMergeBytes;
+};
+
+// Chunk swizzles (the LDS position of 16-byte chunk c of row `row` is
+// c ^ swz(row)).  K: 16 consecutive rows at one chunk index land on
+// distinct banks, for the K fragment reads.  V (bf16): the transposed reads
+// of a half-wave land on distinct banks.  V (fp32) is read along rows.
+template <bool B16>
+__device__ __forceinline__ int kswz(int row) {
+  return B16 ? ((row >> 1) & 7) : (row & 15);
+}
+template <bool B16>
+__device__ __forceinline__ int vswz(int row) {
+  return B16 ? (((row >> 1) & 1) << 2) : 0;
+}
 
 template <bool B16>
 using elem_t = typename std::conditional<B16, __bf16, float>::type;
@@ -93,6 +123,10 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+// Wait until every vector-memory load this wave issued has completed
+// (direct-to-LDS loads included); other counters are left alone.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ void load_frag(Frag<true>& f, const __bf16* row, int hh) {
   const bf16x8* p = reinterpret_cast<const bf16x8*>(row);
@@ -123,56 +157,123 @@ __device__ __forceinline__ void qk(f32x16& acc, const Frag<false>& kf, const Fra
   for (int i = 0; i < 32; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.x[i], qf.x[i], acc, 0, 0, 0);
 }
 
-// Accumulator element r of a lane holds key row kr(r) of the block.
-__device__ __forceinline__ int acc_key(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
+// Accumulator element r of a lane holds key row c_r + 4*(lane/32) of the
+// block, c_r = 8*(r/4) + r%4.
+__host__ __device__ constexpr int acc_c(int r) { return 8 * (r >> 2) + (r & 3); }
 
-// Stage the V rows of one 32-key block into this wave's LDS area.  Keys
-// whose bit is clear in keymask are stored as zeros, so that keys outside a
-// row's key set contribute exactly nothing even if their stored values are
-// not finite.  key_pos is this lane's key row position (row lane % 32).
-__device__ __forceinline__ void stage_v(unsigned char* lds, const __bf16* vbase, size_t rstride,
-                                        int key_pos, uint32_t keymask) {
-  const int lane = lane_id();
-  const int kg = lane & 7;   // keys 4kg .. 4kg+3
-  const int dg = lane >> 3;  // dims 8dg .. 8dg+7
-  u32x4 rows[4];
+// ---------------------------------------------------------------------------
+// One key block through LDS.
+// ---------------------------------------------------------------------------
+
+// Issue the direct-to-LDS loads of a block's K and V rows into `stage`.
+// kpos(row) gives the token position of key row `row` (0..31) of the block,
+// always a valid position (rows outside the key set are clamped here and
+// masked later).  Lane l of load i fetches chunk (l % kChunks) ^ swz(row)
+// of row kRowsPerLoad*i + l / kChunks; it lands at byte 1024i + 16l.
+template <bool B16, class KPos>
+__device__ __forceinline__ void issue_block(const elem_t<B16>* kb, const elem_t<B16>* vb, uint32_t rs, KPos kpos,
+                                            unsigned char* stage, int lane) {
+  using L = Lay<B16>;
+  constexpr int kEltPerChunk = 16 / L::kElt;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int kr = 4 * kg + e;
-    const int pos = __shfl(key_pos, kr);
-    rows[e] = *reinterpret_cast<const u32x4*>(vbase + (size_t)pos * rstride + 8 * dg);
-    if (!((keymask >> kr) & 1u)) rows[e] = u32x4{0u, 0u, 0u, 0u};
-  }
-  __bf16* vt = reinterpret_cast<__bf16*>(lds);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // dword i of a row holds dims 2i (low half) and 2i+1 (high half)
-    u32x2 lo, hi;
-    lo[0] = (rows[0][i] & 0xffffu) | (rows[1][i] << 16);
-    lo[1] = (rows[2][i] & 0xffffu) | (rows[3][i] << 16);
-    hi[0] = (rows[0][i] >> 16) | (rows[1][i] & 0xffff0000u);
-    hi[1] = (rows[2][i] >> 16) | (rows[3][i] & 0xffff0000u);
-    const int d = 8 * dg + 2 * i;
-    *reinterpret_cast<u32x2*>(vt + d * kVtStride + 4 * kg) = lo;
-    *reinterpret_cast<u32x2*>(vt + (d + 1) * kVtStride + 4 * kg) = hi;
+  for (int i = 0; i < L::kLoads; ++i) {
+    const int row = L::kRowsPerLoad * i + lane / L::kChunks;
+    const int c = lane % L::kChunks;
+    const uint32_t base = (uint32_t)kpos(row) * rs;
+    __builtin_amdgcn_global_load_lds(kb + (base + (c ^ kswz<B16>(row)) * kEltPerChunk),
+                                     (LDS_AS void*)(stage + 1024 * i), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb + (base + (c ^ vswz<B16>(row)) * kEltPerChunk),
+                                     (LDS_AS void*)(stage + L::kBlockBytes + 1024 * i), 16, 0, 0);
   }
 }
 
-__device__ __forceinline__ void stage_v(unsigned char* lds, const float* vbase, size_t rstride,
-                                        int key_pos, uint32_t keymask) {
-  const int lane = lane_id();
-  const int kr = lane >> 1;
-  const int half = lane & 1;
-  const int pos = __shfl(key_pos, kr);
-  const bool keep = (keymask >> kr) & 1u;
-  const f32x4* src = reinterpret_cast<const f32x4*>(vbase + (size_t)pos * rstride + 32 * half);
-  float* dst = reinterpret_cast<float*>(lds) + kr * kVStrideF32 + 32 * half;
+// K operand fragment of key row lane % 32.
+__device__ __forceinline__ void read_kfrag(Frag<true>& f, const unsigned char* kbuf, int lane) {
+  const int row = lane & 31;
+  const int hh = lane >> 5;
+  const unsigned char* rp = kbuf + row * Lay<true>::kRowBytes;
+  const int sw = kswz<true>(row);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    f32x4 t = src[i];
-    if (!keep) t = f32x4{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(dst + 4 * i) = t;
+  for (int s = 0; s < 4; ++s) f.x[s] = *reinterpret_cast<const bf16x8*>(rp + (((2 * s + hh) ^ sw) << 4));
+}
+
+__device__ __forceinline__ void read_kfrag(Frag<false>& f, const unsigned char* kbuf, int lane) {
+  const int row = lane & 31;
+  const int hh = lane >> 5;
+  const unsigned char* rp = kbuf + row * Lay<false>::kRowBytes;
+  const int sw = kswz<false>(row);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(rp + (((8 * hh + j) ^ sw) << 4));
+    f.x[4 * j + 0] = t[0];
+    f.x[4 * j + 1] = t[1];
+    f.x[4 * j + 2] = t[2];
+    f.x[4 * j + 3] = t[3];
   }
+}
+
+// Zero the V rows whose key bit is clear in keymask, so keys outside a
+// row's key set contribute exactly nothing to P V even where their stored
+// values are not finite.
+template <bool B16>
+__device__ __forceinline__ void zero_dead_v_rows(unsigned char* vbuf, uint32_t keymask, int lane) {
+  using L = Lay<B16>;
+  const int row = lane >> 1;
+  if (!((keymask >> row) & 1u)) {
+    u32x4* dst = reinterpret_cast<u32x4*>(vbuf + row * L::kRowBytes + (L::kRowBytes / 2) * (lane & 1));
+#pragma unroll
+    for (int j = 0; j < L::kChunks / 2; ++j) dst[j] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// V^T operand of the PV product for one block, in registers.
+//   bf16: a[db][ks] covers head dims 32db + lane%32 and keys 16ks +
+//         {4hh..4hh+3, 8+4hh..8+4hh+3} (hh = lane/32), the key order of the
+//         P^T fragments;
+//   fp32: a[db][r] is V[key c_r + 4hh][32db + lane%32].
+template <bool B16>
+struct VtFrag;
+template <>
+struct VtFrag<true> {
+  bf16x8 a[2][2];
+};
+template <>
+struct VtFrag<false> {
+  float a[2][16];
+};
+
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane j receives element
+// j%4 of the 8-byte chunk addressed by lane 4e + j/4, as its element e.
+// Lane 4e+q of group g points at key row 16ks + 8half + 4(g/2) + e, head
+// dims 32db + 16(g%2) + 4q .. +3, so lane j of the group gets head dim
+// 32db + 16(g%2) + j for keys e = 0..3.
+__device__ __forceinline__ void read_vt(VtFrag<true>& vt, const unsigned char* vbuf, int lane) {
+  const int g = lane >> 4;
+  const int row0 = 4 * (g >> 1) + ((lane & 15) >> 2);
+  const int byte0 = 32 * (g & 1) + 8 * (lane & 3);
+  const int sw = vswz<true>(row0);  // rows 16ks + 8half + row0 share bit 1 with row0
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    const int byte = 64 * db + byte0;
+    const int off = row0 * 128 + (((byte >> 4) ^ sw) << 4) + (byte & 15);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(vbuf + off + 2048 * ks));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(vbuf + off + 2048 * ks + 1024));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+      const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+      vt.a[db][ks] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+    }
+  }
+}
+
+__device__ __forceinline__ void read_vt(VtFrag<false>& vt, const unsigned char* vbuf, int lane) {
+  const float* vs = reinterpret_cast<const float*>(vbuf);
+  const int hh = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) vt.a[db][r] = vs[(acc_c(r) + 4 * hh) * kHeadDim + 32 * db + (lane & 31)];
 }
 
 // Probabilities of one block in the operand form of the PV product.
@@ -187,54 +288,12 @@ struct PFrag<false> {
   float x[16];
 };
 
-__device__ __forceinline__ void to_pfrag(PFrag<true>& pf, const f32x16& p) {
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pf.x[ks][e] = (__bf16)p[8 * ks + e];
-}
-
-__device__ __forceinline__ void to_pfrag(PFrag<false>& pf, const f32x16& p) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) pf.x[r] = p[r];
-}
-
-// O^T (64 dims x 32 queries, as two 32x32 accumulators) += V^T P^T.
-__device__ __forceinline__ void pv(f32x16 (&o)[2], const PFrag<true>& pf, const unsigned char* lds, int lane) {
-  const __bf16* vt = reinterpret_cast<const __bf16*>(lds);
-  const int hh = lane >> 5;
-#pragma unroll
-  for (int db = 0; db < 2; ++db) {
-    const __bf16* row = vt + (32 * db + (lane & 31)) * kVtStride;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x2 a0 = *reinterpret_cast<const u32x2*>(row + 16 * ks + 4 * hh);
-      const u32x2 a1 = *reinterpret_cast<const u32x2*>(row + 16 * ks + 8 + 4 * hh);
-      const u32x4 a = u32x4{a0[0], a0[1], a1[0], a1[1]};
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf.x[ks], o[db], 0, 0, 0);
-    }
-  }
-}
-
-__device__ __forceinline__ void pv(f32x16 (&o)[2], const PFrag<false>& pf, const unsigned char* lds, int lane) {
-  const float* vs = reinterpret_cast<const float*>(lds);
-  const int hh = lane >> 5;
-#pragma unroll
-  for (int db = 0; db < 2; ++db) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float a = vs[acc_key(r, hh) * kVStrideF32 + 32 * db + (lane & 31)];
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pf.x[r], o[db], 0, 0, 0);
-    }
-  }
-}
-
 // Running state of one wave: 64 query columns as two 32-column halves.
 struct WaveState {
-  f32x16 o[2][2];   // [query half nb][dim half db]
-  float m[2];       // reference max (log2 domain) of the lane's query
-  float l[2];       // partial row sum of this lane (16 of the 32 keys per block)
-  int cnt[2];       // partial count of scored keys of this lane
+  f32x16 o[2][2];  // [query half nb][dim half db]
+  float m[2];      // reference max (log2 domain) of the lane's query
+  float l[2];      // partial row sum of this lane (16 of the 32 keys per block)
+  int cnt[2];      // partial count of scored keys of this lane
 };
 
 __device__ __forceinline__ void state_init(WaveState& st) {
@@ -250,139 +309,207 @@ __device__ __forceinline__ void state_init(WaveState& st) {
   }
 }
 
-// One 32-key block against the wave's 64 queries.  keep(nb, r) decides,
-// for edge blocks, whether accumulator element r of query half nb is in
-// the row's key set; on interior blocks every element is.
+__device__ __forceinline__ float max_across_halves(float x) {
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+// Scores of one block for query half nb -> masked, online-softmax
+// probabilities, with that half's running state rescaled if its reference
+// max moves.  keep(r) decides, for edge blocks, whether accumulator element
+// r is in its row's key set (the key bit of keymask is tested here); on
+// interior blocks every element is.
 template <bool B16, class Keep>
-__device__ __forceinline__ void attend_block(WaveState& st, const Frag<B16> (&qf)[2], const elem_t<B16>* kbase,
-                                             const elem_t<B16>* vbase, size_t rstride, int key_pos,
-                                             uint32_t keymask, bool edge, Keep keep, unsigned char* lds,
-                                             float c) {
-  const int lane = lane_id();
+__device__ __forceinline__ void softmax_half(WaveState& st, int nb, f32x16& s, PFrag<B16>& pf, uint32_t keymask,
+                                             bool edge, Keep keep, float c, int lane) {
   const int hh = lane >> 5;
-  Frag<B16> kf;
-  load_frag(kf, kbase + (size_t)key_pos * rstride, hh);
-  stage_v(lds, vbase, rstride, key_pos, keymask);
-
-  f32x16 s[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[nb][r] = 0.f;
-    qk(s[nb], kf, qf[nb]);
-  }
-
   if (edge) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      int kept = 0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = acc_key(r, hh);
-        const bool ok = ((keymask >> kr) & 1u) && keep(nb, kr);
-        kept += ok ? 1 : 0;
-        if (!ok) s[nb][r] = kNegInf;
-      }
-      st.cnt[nb] += kept;
-    }
-  } else {
-    st.cnt[0] += 16;
-    st.cnt[1] += 16;
-  }
-
-  float mb[2];
-  bool need = false;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    float mx = s[nb][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    mb[nb] = mx * c;
-    need |= mb[nb] > st.m[nb] + kRescaleSlack;
-  }
-  if (__any(need)) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const float mn = fmaxf(st.m[nb], mb[nb]);
-      const float alpha = (st.m[nb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(st.m[nb] - mn);
-      st.m[nb] = mn;
-      st.l[nb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st.o[nb][db][r] *= alpha;
-    }
-  }
-
-  PFrag<B16> pf[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const float msub = (st.m[nb] == kNegInf) ? 0.f : st.m[nb];
-    float sum = 0.f;
+    const uint32_t km = keymask >> (4 * hh);
+    int kept = 0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][r], c, -msub));
-      s[nb][r] = pr;
-      sum += pr;
+      const bool ok = ((km >> acc_c(r)) & 1u) && keep(r);
+      kept += ok ? 1 : 0;
+      s[r] = ok ? s[r] : kNegInf;
     }
-    st.l[nb] += sum;
-    to_pfrag(pf[nb], s[nb]);
+    st.cnt[nb] += kept;
+  } else {
+    st.cnt[nb] += 16;
   }
 
-  wave_sync();  // V block staged by all lanes of the wave
+  float mx = s[0];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) pv(st.o[nb], pf[nb], lds, lane);
-  wave_sync();  // reads done before the next block overwrites the staging area
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  const float mb = max_across_halves(mx) * c;
+  if (__any(mb > st.m[nb] + kRescaleSlack)) {
+    const float mn = fmaxf(st.m[nb], mb);
+    const float alpha = (st.m[nb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(st.m[nb] - mn);
+    st.m[nb] = mn;
+    st.l[nb] *= alpha;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[nb][db][r] *= alpha;
+  }
+
+  const float msub = (st.m[nb] == kNegInf) ? 0.f : st.m[nb];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -msub));
+  float sum = 0.f;
+  if constexpr (B16) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf.x[ks][e] = (__bf16)s[8 * ks + e];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += s[r];
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pf.x[r] = s[r];
+      sum += s[r];
+    }
+  }
+  st.l[nb] += sum;
+}
+
+// O^T (64 dims x 32 queries of half nb) += V^T P^T.
+__device__ __forceinline__ void pv(f32x16 (&o)[2], const PFrag<true>& pf, const VtFrag<true>& vt) {
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt.a[db][ks], pf.x[ks], o[db], 0, 0, 0);
+}
+
+__device__ __forceinline__ void pv(f32x16 (&o)[2], const PFrag<false>& pf, const VtFrag<false>& vt) {
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vt.a[db][r], pf.x[r], o[db], 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// A wave's pass over blocks first, first+4, ... < end of one key source.
+// Src provides:
+//   kpos(vb, row) -> int           token position of key row `row` (clamped)
+//   locate(vb, mb&, inr&)          mask byte / existence of key row lane%32
+//   edge(vb, keymask) -> bool      whether masking is needed
+//   keep(vb, nb, r) -> bool        membership of element r (edge blocks)
+// The loads of the wave's next block are in flight while the current one
+// is computed: its K and V^T fragments are read from LDS into registers
+// before the next block's direct-to-LDS loads are issued into the other
+// stage.
+// ---------------------------------------------------------------------------
+template <bool B16, class Src>
+__device__ __forceinline__ void run_blocks(WaveState& st, const Frag<B16> (&qf)[2], const Src& src,
+                                           const elem_t<B16>* kb, const elem_t<B16>* vb, uint32_t rs, int first,
+                                           int end, unsigned char* lds, float c) {
+  using L = Lay<B16>;
+  const int lane = lane_id();
+  int mb = 0;
+  bool inr = false;
+  auto issue = [&](int blk, unsigned char* stage) {
+    src.locate(blk, mb, inr);
+    issue_block<B16>(kb, vb, rs, [&](int row) { return src.kpos(blk, row); }, stage, lane);
+  };
+  if (first < end) issue(first, lds);
+  int it = 0;
+  for (int blk = first; blk < end; blk += kWaves, ++it) {
+    unsigned char* cst = lds + (it & 1) * L::kStageBytes;
+    unsigned char* nst = lds + ((it + 1) & 1) * L::kStageBytes;
+    const bool kval = inr && (mb == 1 || mb == 2);
+    const uint32_t keymask = (uint32_t)__ballot(kval);
+    wait_vmem_all();  // this block's rows have landed in cst
+    if (keymask != 0xffffffffu) {
+      zero_dead_v_rows<B16>(cst + L::kBlockBytes, keymask, lane);
+      wave_sync();
+    }
+    Frag<B16> kf;
+    read_kfrag(kf, cst, lane);
+    VtFrag<B16> vt;
+    read_vt(vt, cst + L::kBlockBytes, lane);
+    if (blk + kWaves < end) issue(blk + kWaves, nst);
+
+    const bool edge = src.edge(blk, keymask);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+      qk(s, kf, qf[nb]);
+      PFrag<B16> pf;
+      softmax_half<B16>(st, nb, s, pf, keymask, edge, [&](int r) { return src.keep(blk, nb, r); }, c, lane);
+      pv(st.o[nb], pf, vt);
+    }
+  }
+}
+
+// Bitmask of the bytes equal to 2 among mrow[p0 .. p0+16) (clipped to n).
+__device__ __forceinline__ uint32_t match16(const int8_t* __restrict__ mrow, int p0, int n) {
+  uint32_t bits = 0;
+  if (p0 + 16 <= n && ((reinterpret_cast<uintptr_t>(mrow + p0) & 15u) == 0)) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(mrow + p0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bits |= (((x[j] >> (8 * e)) & 0xffu) == 2u ? 1u : 0u) << (4 * j + e);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (p0 + e < n && mrow[p0 + e] == 2) bits |= 1u << e;
+  }
+  return bits;
 }
 
 // Ordered list of positions j with mask_row[j] == 2 into G (LDS), at most
 // cap entries; returns the total count.  Every thread of the workgroup
-// calls it and gets the same result.
+// calls it and gets the same result.  Each thread looks at 16 bytes of a
+// 4 KB step; four steps are loaded together.
 __device__ int scan_globals(const int8_t* __restrict__ mrow, int n, int* G, int cap, int* s_wave) {
+  constexpr int kStep = kThreads * 16;
   int total = 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  for (int base = 0; base < n; base += kThreads * 4) {
-    const int p0 = base + tid * 4;
-    unsigned bits = 0;
+  for (int base = 0; base < n; base += 4 * kStep) {
+    uint32_t bits[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int pidx = p0 + e;
-      if (pidx < n && mrow[pidx] == 2) bits |= 1u << e;
-    }
-    if (!__syncthreads_or(bits != 0)) continue;
-    const int cnt = __popc(bits);
-    int x = cnt;
+    for (int u = 0; u < 4; ++u) bits[u] = match16(mrow, base + u * kStep + 16 * tid, n);
+    if (!__syncthreads_or((bits[0] | bits[1] | bits[2] | bits[3]) != 0)) continue;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(x, off);
-      if (lane >= off) x += y;
-    }
-    if (lane == 63) s_wave[wv] = x;
-    __syncthreads();
-    int before = 0, all = 0;
+    for (int u = 0; u < 4; ++u) {
+      if (!__syncthreads_or(bits[u] != 0)) continue;
+      const int cnt = __popc(bits[u]);
+      int x = cnt;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-      const int t = s_wave[i];
-      before += (i < wv) ? t : 0;
-      all += t;
-    }
-    int slot = total + before + x - cnt;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+      }
+      if (lane == 63) s_wave[wv] = x;
+      __syncthreads();
+      int before = 0, all = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if ((bits >> e) & 1u) {
-        if (slot < cap) G[slot] = p0 + e;
+      for (int i = 0; i < kWaves; ++i) {
+        const int t = s_wave[i];
+        before += (i < wv) ? t : 0;
+        all += t;
+      }
+      int slot = total + before + x - cnt;
+      uint32_t b = bits[u];
+      while (b) {
+        const int e = __builtin_ctz(b);
+        b &= b - 1;
+        if (slot < cap) G[slot] = base + u * kStep + 16 * tid + e;
         ++slot;
       }
+      total += all;
     }
-    total += all;
-    __syncthreads();
   }
   return total;
 }
 
+template <bool B16>
 struct Shared {
   int G[LF_MAX_GLOBAL];
   int wave_tmp[kWaves];
@@ -390,11 +517,12 @@ struct Shared {
   float m[kWaves][kTileQ];
   float l[kWaves][kTileQ];
   int cnt[kWaves][kTileQ];
-  __attribute__((aligned(16))) unsigned char buf[kBufBytes];
+  __attribute__((aligned(16))) unsigned char buf[Lay<B16>::kBufBytes];
 };
 
 // Merge the partial results of the 4 waves into wave 0's registers.
-__device__ void merge_waves(WaveState& st, Shared& sh) {
+template <bool B16>
+__device__ void merge_waves(WaveState& st, Shared<B16>& sh) {
   const int lane = lane_id();
   const int hh = lane >> 5;
   const int wv = threadIdx.x >> 6;
@@ -446,7 +574,7 @@ __device__ void merge_waves(WaveState& st, Shared& sh) {
         }
     }
   };
-  __syncthreads();  // all waves done with their staging areas (aliased below)
+  __syncthreads();  // all waves done with their V buffers (aliased below)
   if (wv >= 2) write_slot(wv - 2);
   __syncthreads();
   if (wv < 2) absorb(wv, wv + 2);
@@ -493,10 +621,82 @@ __device__ __forceinline__ int xcd_remap(int x, int N) {
 }
 
 // ---------------------------------------------------------------------------
+// Key sources
+// ---------------------------------------------------------------------------
+
+// Window blocks of a band tile: keys kbase + 32(jlo + vb) + row of the
+// residue sequence (token position r + dil*key), clipped to [0, n_r).
+struct WindowSrc {
+  const int8_t* mrow;
+  int kbase, jlo, n_r, r, dil, t0, w, causal, lane;
+  int A[2], B[2];  // per query half: rows c_r in [A - 32(jlo+vb), B - 32(jlo+vb)] are in the window
+  __device__ int key(int vb, int row) const { return kbase + kBlockK * (jlo + vb) + row; }
+  __device__ int kpos(int vb, int row) const {
+    const int kk = key(vb, row);
+    return r + dil * (kk < 0 ? 0 : (kk >= n_r ? n_r - 1 : kk));
+  }
+  __device__ void locate(int vb, int& mb, bool& inr) const {
+    const int kk = key(vb, lane & 31);
+    inr = kk >= 0 && kk < n_r;
+    mb = mrow[kpos(vb, lane & 31)];
+  }
+  __device__ bool edge(int vb, uint32_t keymask) const {
+    const int kb = key(vb, 0);
+    bool interior = keymask == 0xffffffffu && (t0 + kTileQ - 1 - kb <= w);
+    interior = interior && (causal ? (t0 >= kb + kBlockK - 1) : (kb + kBlockK - 1 - t0 <= w));
+    return !interior;
+  }
+  __device__ bool keep(int vb, int nb, int r) const {
+    const int sh = kBlockK * (jlo + vb);
+    const int c = acc_c(r);
+    return c >= A[nb] - sh && c <= B[nb] - sh;
+  }
+};
+
+// Global-column blocks of a band tile: keys G[32 vb + row].
+struct GlobalColSrc {
+  const int* G;
+  int nG, dil, wd, lane;
+  int qpos[2];
+  __device__ int kpos(int vb, int row) const {
+    const int gi = kBlockK * vb + row;
+    return G[gi < nG ? gi : nG - 1];
+  }
+  __device__ void locate(int vb, int& mb, bool& inr) const {
+    inr = kBlockK * vb + (lane & 31) < nG;
+    mb = 2;
+  }
+  __device__ bool edge(int, uint32_t) const { return true; }
+  __device__ bool keep(int vb, int nb, int r) const {
+    // a global key g joins local row i unless g is already in W(i)
+    const int g = G[kBlockK * vb + acc_c(r) + 4 * (lane >> 5)];
+    const int dd = qpos[nb] - g;
+    const bool in_w = (dd <= wd && dd >= -wd) && (dil == 1 || dd % dil == 0);
+    return !in_w;
+  }
+};
+
+// Blocks of one split of a global row: keys cbeg + 32 j + row.
+struct ChunkSrc {
+  const int8_t* mrow;
+  int cbeg, cend, lane;
+  __device__ int kpos(int j, int row) const {
+    const int kk = cbeg + kBlockK * j + row;
+    return kk < cend ? kk : cend - 1;
+  }
+  __device__ void locate(int j, int& mb, bool& inr) const {
+    inr = cbeg + kBlockK * j + (lane & 31) < cend;
+    mb = mrow[kpos(j, lane & 31)];
+  }
+  __device__ bool edge(int, uint32_t keymask) const { return keymask != 0xffffffffu; }
+  __device__ bool keep(int, int, int) const { return true; }
+};
+
+// ---------------------------------------------------------------------------
 // Band workgroup: one tile of kTileQ query rows of (b, h, residue r).
 // ---------------------------------------------------------------------------
 template <bool B16>
-__device__ void band_tile(const KernelParams& p, int L, Shared& sh) {
+__device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
   using T = elem_t<B16>;
   const int lane = lane_id();
   const int hh = lane >> 5;
@@ -536,10 +736,10 @@ __device__ void band_tile(const KernelParams& p, int L, Shared& sh) {
     }
   }
 
-  // Query rows of this lane: t = t0 + 32nb + lane%32 in the residue sequence.
-  const size_t rstride_pos = (size_t)p.H * kHeadDim;  // elements between tokens
-  const size_t rstride = rstride_pos * dil;           // between residue-sequence neighbours
-  const size_t head_off = (size_t)b * n * rstride_pos + (size_t)h * kHeadDim + (size_t)r * rstride_pos;
+  // Query rows of this lane: t = t0 + 32nb + lane%32 in the residue sequence,
+  // token position r + dil*t.
+  const size_t rs = (size_t)p.H * kHeadDim;  // elements between tokens
+  const size_t head = (size_t)b * n * rs + (size_t)h * kHeadDim;
   bool is_local[2], is_zero[2];
   int qpos[2];
   bool any_local = false;
@@ -564,8 +764,7 @@ __device__ void band_tile(const KernelParams& p, int L, Shared& sh) {
   }
   any_local = __any(any_local);
 
-  T* out = reinterpret_cast<T*>(p.out);
-  const size_t out_head = (size_t)b * n * rstride_pos + (size_t)h * kHeadDim;
+  T* out = reinterpret_cast<T*>(p.out) + head;
 
   if (!any_local) {
     if (wv == 0) {
@@ -573,7 +772,7 @@ __device__ void band_tile(const KernelParams& p, int L, Shared& sh) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         if (!is_zero[nb]) continue;
-        T* orow = out + out_head + (size_t)qpos[nb] * rstride_pos;
+        T* orow = out + (size_t)qpos[nb] * rs;
 #pragma unroll
         for (int g = 0; g < 8; ++g) store4<B16>(orow + 8 * g + 4 * hh, z);
         if (p.row_nnz && hh == 0) p.row_nnz[((size_t)b * p.H + h) * n + qpos[nb]] = 0;
@@ -582,62 +781,63 @@ __device__ void band_tile(const KernelParams& p, int L, Shared& sh) {
     return;
   }
 
-  const T* q = reinterpret_cast<const T*>(p.q);
-  const T* k = reinterpret_cast<const T*>(p.k);
-  const T* v = reinterpret_cast<const T*>(p.v);
+  const T* qh = reinterpret_cast<const T*>(p.q) + head;
+  const T* kh = reinterpret_cast<const T*>(p.k) + head;
+  const T* vh = reinterpret_cast<const T*>(p.v) + head;
   Frag<B16> qf[2];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) load_frag(qf[nb], q + (size_t)b * n * rstride_pos + (size_t)qpos[nb] * rstride_pos + (size_t)h * kHeadDim, hh);
+  for (int nb = 0; nb < 2; ++nb) load_frag(qf[nb], qh + (size_t)qpos[nb] * rs, hh);
 
   WaveState st;
   state_init(st);
-  unsigned char* lds = sh.buf + wv * kStageBytes;
+  unsigned char* lds = sh.buf + wv * Lay<B16>::kWaveBytes;
 
-  // Window blocks: keys t0 - w + 32j of the residue sequence, clipped.
   const int kbase = t0 - w;
   const int t_last = min(t0 + kTileQ, n_r) - 1;
   const int kfirst = max(kbase, 0);
   const int klast = min(n_r - 1, causal ? t_last : t_last + w);
   const int jlo = (kfirst - kbase) / kBlockK;
   const int nblk = (klast - kbase) / kBlockK - jlo + 1;
-  const int ngblk = (nG + kBlockK - 1) / kBlockK;
-  const T* kh = k + head_off;
-  const T* vh = v + head_off;
-  const T* kfull = k + (size_t)b * n * rstride_pos + (size_t)h * kHeadDim;
-  const T* vfull = v + (size_t)b * n * rstride_pos + (size_t)h * kHeadDim;
   const float c = p.c;
 
-  for (int vb = wv; vb < nblk + ngblk; vb += kWaves) {
-    if (vb < nblk) {
-      const int kb = kbase + kBlockK * (jlo + vb);
-      const int kk = kb + (lane & 31);
-      const bool inr = kk >= 0 && kk < n_r;
-      const int kkc = inr ? kk : (kk < 0 ? 0 : n_r - 1);
-      const bool kval = inr && (mrow[r + dil * kkc] == 1 || mrow[r + dil * kkc] == 2);
-      const uint32_t keymask = (uint32_t)__ballot(kval);
-      bool interior = keymask == 0xffffffffu && (t0 + kTileQ - 1 - kb <= w);
-      interior = interior && (causal ? (t0 >= kb + kBlockK - 1) : (kb + kBlockK - 1 - t0 <= w));
-      auto keep = [&](int nb, int kr) {
-        const int d = t0 + 32 * nb + (lane & 31) - (kb + kr);
-        return causal ? (unsigned)d <= (unsigned)w : (unsigned)(d + w) <= (unsigned)(2 * w);
-      };
-      attend_block<B16>(st, qf, kh, vh, rstride, kkc, keymask, !interior, keep, lds, c);
-    } else {
-      const int gi = vb - nblk;
-      const int gidx = kBlockK * gi + (lane & 31);
-      const bool gval = gidx < nG;
-      const int gpos = gval ? sh.G[gidx] : 0;
-      const uint32_t keymask = (uint32_t)__ballot(gval);
-      const int wd = w * dil;
-      auto keep = [&](int nb, int kr) {
-        // global key g is a column of this local row unless g is in W(i)
-        const int g = sh.G[kBlockK * gi + kr];
-        const int dd = qpos[nb] - g;
-        const bool in_w = (dd <= wd && dd >= -wd) && (dil == 1 || dd % dil == 0);
-        return !in_w;
-      };
-      attend_block<B16>(st, qf, kfull, vfull, rstride_pos, gpos, keymask, true, keep, lds, c);
+  {
+    WindowSrc src;
+    src.mrow = mrow;
+    src.kbase = kbase;
+    src.jlo = jlo;
+    src.n_r = n_r;
+    src.r = r;
+    src.dil = dil;
+    src.t0 = t0;
+    src.w = w;
+    src.causal = causal;
+    src.lane = lane;
+    // row key = kbase + sh + kr with sh = 32(jlo+vb) and kr = c_r + 4hh;
+    // query t = t0 + 32nb + lane%32:  t - key in [lo, w]  <=>
+    // c_r in [t - kbase - w - 4hh - sh, t - kbase - lo - 4hh - sh]
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int tq = t0 + 32 * nb + (lane & 31);
+      const int lo = causal ? 0 : -w;
+      src.A[nb] = tq - kbase - w - 4 * hh;
+      src.B[nb] = tq - kbase - lo - 4 * hh;
     }
+    run_blocks<B16>(st, qf, src, kh, vh, rs, wv, nblk, lds, c);
+  }
+
+  const int ngblk = (nG + kBlockK - 1) / kBlockK;
+  if (ngblk > 0) {
+    // global-column blocks continue the round-robin over waves
+    const int first = ((wv - nblk) % kWaves + kWaves) % kWaves;
+    GlobalColSrc src;
+    src.G = sh.G;
+    src.nG = nG;
+    src.dil = dil;
+    src.wd = w * dil;
+    src.lane = lane;
+    src.qpos[0] = qpos[0];
+    src.qpos[1] = qpos[1];
+    run_blocks<B16>(st, qf, src, kh, vh, rs, first, ngblk, lds, c);
   }
 
   merge_waves(st, sh);
@@ -646,7 +846,7 @@ __device__ void band_tile(const KernelParams& p, int L, Shared& sh) {
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     if (!is_local[nb] && !is_zero[nb]) continue;
-    T* orow = out + out_head + (size_t)qpos[nb] * rstride_pos;
+    T* orow = out + (size_t)qpos[nb] * rs;
     const float inv = is_local[nb] ? 1.0f / st.l[nb] : 0.f;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
@@ -665,7 +865,7 @@ __device__ void band_tile(const KernelParams& p, int L, Shared& sh) {
 // Global-row workgroup: split c of (b, h); all global tokens of b.
 // ---------------------------------------------------------------------------
 template <bool B16>
-__device__ void global_split(const KernelParams& p, int gid, Shared& sh) {
+__device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
   using T = elem_t<B16>;
   const int lane = lane_id();
   const int hh = lane >> 5;
@@ -693,9 +893,15 @@ __device__ void global_split(const KernelParams& p, int gid, Shared& sh) {
   const int cbeg = cidx * kGlobalChunk;
   const int cend = min(n, cbeg + kGlobalChunk);
   const int nblk = (cend - cbeg + kBlockK - 1) / kBlockK;
-  unsigned char* lds = sh.buf + wv * kStageBytes;
+  unsigned char* lds = sh.buf + wv * Lay<B16>::kWaveBytes;
   const float c = p.c;
   float* part_bh = p.partials + (size_t)bh * p.max_global * S * kPartialStride;
+
+  ChunkSrc src;
+  src.mrow = mrow;
+  src.cbeg = cbeg;
+  src.cend = cend;
+  src.lane = lane;
 
   for (int g0 = 0; g0 < nG; g0 += kTileQ) {
     Frag<B16> qf[2];
@@ -707,15 +913,7 @@ __device__ void global_split(const KernelParams& p, int gid, Shared& sh) {
     }
     WaveState st;
     state_init(st);
-    for (int j = wv; j < nblk; j += kWaves) {
-      const int kk = cbeg + kBlockK * j + (lane & 31);
-      const bool inr = kk < cend;
-      const int kkc = inr ? kk : cend - 1;
-      const bool kval = inr && (mrow[kkc] == 1 || mrow[kkc] == 2);
-      const uint32_t keymask = (uint32_t)__ballot(kval);
-      auto keep = [](int, int) { return true; };
-      attend_block<B16>(st, qf, kg, vg, rs, kkc, keymask, keymask != 0xffffffffu, keep, lds, c);
-    }
+    run_blocks<B16>(st, qf, src, kg, vg, rs, wv, nblk, lds, c);
     merge_waves(st, sh);
     if (wv == 0) {
 #pragma unroll
@@ -776,8 +974,8 @@ __device__ void global_split(const KernelParams& p, int gid, Shared& sh) {
 }
 
 template <bool B16>
-__global__ __launch_bounds__(kThreads) void lf_attn_fwd(const KernelParams p) {
-  __shared__ Shared sh;
+__device__ __forceinline__ void fwd_body(const KernelParams& p) {
+  __shared__ Shared<B16> sh;
   const int bid = blockIdx.x;
   if (bid < p.n_glob_pad) {
     if (bid < p.n_glob) global_split<B16>(p, bid, sh);
@@ -786,15 +984,24 @@ __global__ __launch_bounds__(kThreads) void lf_attn_fwd(const KernelParams p) {
   band_tile<B16>(p, xcd_remap(bid - p.n_glob_pad, p.n_band), sh);
 }
 
+// bf16: two waves per SIMD, so one wave's softmax overlaps the other's MFMAs.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void lf_attn_fwd_bf16(
+    const KernelParams p) {
+  fwd_body<true>(p);
+}
+
+// fp32: larger operand fragments; one wave per SIMD.
+__global__ __launch_bounds__(kThreads) void lf_attn_fwd_f32(const KernelParams p) { fwd_body<false>(p); }
+
 }  // namespace
 
 int launch_forward(const KernelParams& kp, int dtype, void* stream) {
   const int grid = kp.n_glob_pad + kp.n_band;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == LF_BF16)
-    hipLaunchKernelGGL(lf_attn_fwd<true>, dim3(grid), dim3(kThreads), 0, s, kp);
+    hipLaunchKernelGGL(lf_attn_fwd_bf16, dim3(grid), dim3(kThreads), 0, s, kp);
   else
-    hipLaunchKernelGGL(lf_attn_fwd<false>, dim3(grid), dim3(kThreads), 0, s, kp);
+    hipLaunchKernelGGL(lf_attn_fwd_f32, dim3(grid), dim3(kThreads), 0, s, kp);
   return (int)hipGetLastError();
 }
 
