@@ -11,7 +11,8 @@ namespace lf {
 
 // Tiling constants shared by the host planner and the kernels.
 constexpr int kHeadDim = 64;       // D
-constexpr int kTileQ = 64;         // query rows of one band workgroup
+constexpr int kTileQ = 256;        // query rows of one band workgroup
+constexpr int kWaveQ = 64;         // query rows of one wave
 constexpr int kBlockK = 32;        // keys per inner block (M of the 32x32 MFMA)
 constexpr int kWaves = 4;          // waves per workgroup
 constexpr int kThreads = 64 * kWaves;

@@ -84,7 +84,9 @@ struct Lay {
   static constexpr int kBlockBytes = kBlockK * kRowBytes;
   static constexpr int kStageBytes = 2 * kBlockBytes;
   static constexpr int kWaveBytes = 2 * kStageBytes;
-  static constexpr int kBufBytes = kWaves * kWaveBytes > kMergeBytes ? kWaves * kWaveBytes : kMergeBytes;
+  static constexpr int kRingBytes = 8 * kStageBytes;  // shared ring of a band tile
+  static constexpr int kBufBytes0 = kWaves * kWaveBytes > kMergeBytes ? kWaves * kWaveBytes : kMergeBytes;
+  static constexpr int kBufBytes = kBufBytes0 > kRingBytes ? kBufBytes0 : kRingBytes;
 };
 
 // Chunk swizzles (the LDS position of 16-byte chunk c of row `row` is
@@ -276,6 +278,36 @@ __device__ __forceinline__ void read_vt(VtFrag<false>& vt, const unsigned char* 
     for (int r = 0; r < 16; ++r) vt.a[db][r] = vs[(acc_c(r) + 4 * hh) * kHeadDim + 32 * db + (lane & 31)];
 }
 
+// Zero the V^T operand entries of keys whose bit is clear in keymask, so
+// keys outside a row's key set contribute exactly nothing to P V even where
+// their stored values are not finite.
+__device__ __forceinline__ void zero_dead_keys(VtFrag<true>& vt, uint32_t keymask, int lane) {
+  const uint32_t km = keymask >> (4 * (lane >> 5));
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    u32x4 keep;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      // dword d holds items 2d, 2d+1; item e is key 16ks + 8(e/4) + e%4 (+4hh)
+      const int k0 = 16 * ks + 8 * ((2 * d) >> 2) + ((2 * d) & 3);
+      keep[d] = (((km >> k0) & 1u) ? 0x0000ffffu : 0u) | (((km >> (k0 + 1)) & 1u) ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+      vt.a[db][ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, vt.a[db][ks]) & keep);
+  }
+}
+
+__device__ __forceinline__ void zero_dead_keys(VtFrag<false>& vt, uint32_t keymask, int lane) {
+  const uint32_t km = keymask >> (4 * (lane >> 5));
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (!((km >> acc_c(r)) & 1u)) {
+      vt.a[0][r] = 0.f;
+      vt.a[1][r] = 0.f;
+    }
+}
+
 // Probabilities of one block in the operand form of the PV product.
 template <bool B16>
 struct PFrag;
@@ -315,23 +347,19 @@ __device__ __forceinline__ float max_across_halves(float x) {
 
 // Scores of one block for query half nb -> masked, online-softmax
 // probabilities, with that half's running state rescaled if its reference
-// max moves.  keep(r) decides, for edge blocks, whether accumulator element
-// r is in its row's key set (the key bit of keymask is tested here); on
-// interior blocks every element is.
-template <bool B16, class Keep>
-__device__ __forceinline__ void softmax_half(WaveState& st, int nb, f32x16& s, PFrag<B16>& pf, uint32_t keymask,
-                                             bool edge, Keep keep, float c, int lane) {
-  const int hh = lane >> 5;
+// max moves.  On edge blocks valid() gives this lane's bitmask of elements
+// in their row's key set (bit c_r for element r); on interior blocks every
+// element is.
+template <bool B16, class Valid>
+__device__ __forceinline__ void softmax_half(WaveState& st, int nb, f32x16& s, PFrag<B16>& pf, bool edge,
+                                             Valid valid, float c) {
   if (edge) {
-    const uint32_t km = keymask >> (4 * hh);
-    int kept = 0;
+    // keep the mask work inside the (uniform) branch
+    __asm__ volatile("" ::: "memory");
+    const uint32_t vm = valid();  // bit c_r set <=> element r is in its row's key set
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool ok = ((km >> acc_c(r)) & 1u) && keep(r);
-      kept += ok ? 1 : 0;
-      s[r] = ok ? s[r] : kNegInf;
-    }
-    st.cnt[nb] += kept;
+    for (int r = 0; r < 16; ++r) s[r] = (vm & (1u << acc_c(r))) ? s[r] : kNegInf;
+    st.cnt[nb] += __popc(vm & 0x0f0f0f0fu);
   } else {
     st.cnt[nb] += 16;
   }
@@ -394,7 +422,8 @@ __device__ __forceinline__ void pv(f32x16 (&o)[2], const PFrag<false>& pf, const
 //   kpos(vb, row) -> int           token position of key row `row` (clamped)
 //   locate(vb, mb&, inr&)          mask byte / existence of key row lane%32
 //   edge(vb, keymask) -> bool      whether masking is needed
-//   keep(vb, nb, r) -> bool        membership of element r (edge blocks)
+//   valid_bits(vb, nb) -> uint32   this lane's rows c_r in the key sets (edge blocks)
+//   dstep(), affine(vb, p0&)       evenly spaced in-range blocks: positions p0 + dstep*row
 // The loads of the wave's next block are in flight while the current one
 // is computed: its K and V^T fragments are read from LDS into registers
 // before the next block's direct-to-LDS loads are issued into the other
@@ -406,11 +435,39 @@ __device__ __forceinline__ void run_blocks(WaveState& st, const Frag<B16> (&qf)[
                                            int end, unsigned char* lds, float c) {
   using L = Lay<B16>;
   const int lane = lane_id();
+  const int hh = lane >> 5;
   int mb = 0;
   bool inr = false;
+  // Blocks whose 32 rows are in range and evenly spaced (token positions
+  // p0 + dstep*row) use a wave-uniform base address plus per-lane byte
+  // offsets that do not change from block to block.
+  const int dstep = src.dstep();
+  uint32_t off_k0 = 0, off_k1 = 0, off_v = 0;
+  if constexpr (B16) {
+    const uint32_t row_off = (uint32_t)dstep * (uint32_t)(lane >> 3) * rs;
+    const int ck = (lane & 7) ^ (lane >> 4);  // kswz of rows 8i + lane/8, i even
+    const int cv = (lane & 7) ^ (((lane >> 4) & 1) << 2);
+    off_k0 = 2u * (row_off + 8u * (uint32_t)ck);
+    off_k1 = 2u * (row_off + 8u * (uint32_t)(ck ^ 4));
+    off_v = 2u * (row_off + 8u * (uint32_t)cv);
+  }
   auto issue = [&](int blk, unsigned char* stage) {
     src.locate(blk, mb, inr);
-    issue_block<B16>(kb, vb, rs, [&](int row) { return src.kpos(blk, row); }, stage, lane);
+    int p0;
+    if (B16 && src.affine(blk, p0)) {
+      const size_t step = (size_t)dstep * L::kRowsPerLoad * rs * 2;
+      const char* kbase = reinterpret_cast<const char*>(kb) + (size_t)p0 * rs * 2;
+      const char* vbase = reinterpret_cast<const char*>(vb) + (size_t)p0 * rs * 2;
+#pragma unroll
+      for (int i = 0; i < L::kLoads; ++i) {
+        __builtin_amdgcn_global_load_lds(kbase + i * step + ((i & 1) ? off_k1 : off_k0),
+                                         (LDS_AS void*)(stage + 1024 * i), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vbase + i * step + off_v,
+                                         (LDS_AS void*)(stage + L::kBlockBytes + 1024 * i), 16, 0, 0);
+      }
+    } else {
+      issue_block<B16>(kb, vb, rs, [&](int row) { return src.kpos(blk, row); }, stage, lane);
+    }
   };
   if (first < end) issue(first, lds);
   int it = 0;
@@ -438,7 +495,8 @@ __device__ __forceinline__ void run_blocks(WaveState& st, const Frag<B16> (&qf)[
       for (int r = 0; r < 16; ++r) s[r] = 0.f;
       qk(s, kf, qf[nb]);
       PFrag<B16> pf;
-      softmax_half<B16>(st, nb, s, pf, keymask, edge, [&](int r) { return src.keep(blk, nb, r); }, c, lane);
+      softmax_half<B16>(st, nb, s, pf, edge,
+                        [&]() { return src.valid_bits(blk, nb) & (keymask >> (4 * hh)); }, c);
       pv(st.o[nb], pf, vt);
     }
   }
@@ -509,14 +567,20 @@ __device__ int scan_globals(const int8_t* __restrict__ mrow, int n, int* G, int 
   return total;
 }
 
+// Band tiles keep the key-validity bits of their whole key span in LDS when
+// it has at most this many 32-key blocks.
+constexpr int kMaxSpanBlocks = 512;
+constexpr int kRingSlots = 8;
+
 template <bool B16>
 struct Shared {
   int G[LF_MAX_GLOBAL];
+  uint32_t kmask[kMaxSpanBlocks];
   int wave_tmp[kWaves];
   int flag;
-  float m[kWaves][kTileQ];
-  float l[kWaves][kTileQ];
-  int cnt[kWaves][kTileQ];
+  float m[kWaves][kWaveQ];
+  float l[kWaves][kWaveQ];
+  int cnt[kWaves][kWaveQ];
   __attribute__((aligned(16))) unsigned char buf[Lay<B16>::kBufBytes];
 };
 
@@ -624,58 +688,6 @@ __device__ __forceinline__ int xcd_remap(int x, int N) {
 // Key sources
 // ---------------------------------------------------------------------------
 
-// Window blocks of a band tile: keys kbase + 32(jlo + vb) + row of the
-// residue sequence (token position r + dil*key), clipped to [0, n_r).
-struct WindowSrc {
-  const int8_t* mrow;
-  int kbase, jlo, n_r, r, dil, t0, w, causal, lane;
-  int A[2], B[2];  // per query half: rows c_r in [A - 32(jlo+vb), B - 32(jlo+vb)] are in the window
-  __device__ int key(int vb, int row) const { return kbase + kBlockK * (jlo + vb) + row; }
-  __device__ int kpos(int vb, int row) const {
-    const int kk = key(vb, row);
-    return r + dil * (kk < 0 ? 0 : (kk >= n_r ? n_r - 1 : kk));
-  }
-  __device__ void locate(int vb, int& mb, bool& inr) const {
-    const int kk = key(vb, lane & 31);
-    inr = kk >= 0 && kk < n_r;
-    mb = mrow[kpos(vb, lane & 31)];
-  }
-  __device__ bool edge(int vb, uint32_t keymask) const {
-    const int kb = key(vb, 0);
-    bool interior = keymask == 0xffffffffu && (t0 + kTileQ - 1 - kb <= w);
-    interior = interior && (causal ? (t0 >= kb + kBlockK - 1) : (kb + kBlockK - 1 - t0 <= w));
-    return !interior;
-  }
-  __device__ bool keep(int vb, int nb, int r) const {
-    const int sh = kBlockK * (jlo + vb);
-    const int c = acc_c(r);
-    return c >= A[nb] - sh && c <= B[nb] - sh;
-  }
-};
-
-// Global-column blocks of a band tile: keys G[32 vb + row].
-struct GlobalColSrc {
-  const int* G;
-  int nG, dil, wd, lane;
-  int qpos[2];
-  __device__ int kpos(int vb, int row) const {
-    const int gi = kBlockK * vb + row;
-    return G[gi < nG ? gi : nG - 1];
-  }
-  __device__ void locate(int vb, int& mb, bool& inr) const {
-    inr = kBlockK * vb + (lane & 31) < nG;
-    mb = 2;
-  }
-  __device__ bool edge(int, uint32_t) const { return true; }
-  __device__ bool keep(int vb, int nb, int r) const {
-    // a global key g joins local row i unless g is already in W(i)
-    const int g = G[kBlockK * vb + acc_c(r) + 4 * (lane >> 5)];
-    const int dd = qpos[nb] - g;
-    const bool in_w = (dd <= wd && dd >= -wd) && (dil == 1 || dd % dil == 0);
-    return !in_w;
-  }
-};
-
 // Blocks of one split of a global row: keys cbeg + 32 j + row.
 struct ChunkSrc {
   const int8_t* mrow;
@@ -689,15 +701,32 @@ struct ChunkSrc {
     mb = mrow[kpos(j, lane & 31)];
   }
   __device__ bool edge(int, uint32_t keymask) const { return keymask != 0xffffffffu; }
-  __device__ bool keep(int, int, int) const { return true; }
+  __device__ int dstep() const { return 1; }
+  __device__ bool affine(int j, int& p0) const {
+    p0 = cbeg + kBlockK * j;
+    return p0 + kBlockK - 1 < cend;
+  }
+  __device__ uint32_t valid_bits(int, int) const { return 0xffffffffu; }
 };
 
 // ---------------------------------------------------------------------------
-// Band workgroup: one tile of kTileQ query rows of (b, h, residue r).
+// Band workgroup: one tile of kTileQ = 256 query rows of (b, h, residue r);
+// wave w owns rows t0 + 64w .. t0 + 64w + 63 outright.
+//
+// The tile's key span is cut into 32-key blocks; wave w needs blocks
+// 2w .. 2w + S - 1.  The waves walk their blocks in lockstep, staggered:
+// at step s wave w computes block 2w + s, so the blocks in use at one step
+// are s, s+2, s+4, s+6.  Blocks live in an 8-slot LDS ring shared by the
+// workgroup (slot = block % 8); each block is fetched once per workgroup
+// with direct-to-LDS loads, one part per wave, one step before its first
+// use.  After the window blocks come the global-column blocks (the global
+// keys of the batch row), which every wave computes at the same step.
+// One barrier per step separates the ring's reuse from its reads.
 // ---------------------------------------------------------------------------
 template <bool B16>
 __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
   using T = elem_t<B16>;
+  using Ly = Lay<B16>;
   const int lane = lane_id();
   const int hh = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -723,9 +752,13 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
     n_r = qn;
   }
   const int t0 = tt * kTileQ;
+  const int tw0 = t0 + kWaveQ * wv;  // this wave's first query row
   const int w = p.w;
   const bool causal = p.causal != 0;
+  const int w_hi = causal ? 0 : w;
   const int8_t* mrow = p.mask + (size_t)b * n;
+  const uint32_t rs = (uint32_t)p.H * kHeadDim;  // elements between tokens
+  const size_t head = (size_t)b * n * rs + (size_t)h * kHeadDim;
 
   int nG = 0;
   if (p.use_globals) {
@@ -736,16 +769,13 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
     }
   }
 
-  // Query rows of this lane: t = t0 + 32nb + lane%32 in the residue sequence,
-  // token position r + dil*t.
-  const size_t rs = (size_t)p.H * kHeadDim;  // elements between tokens
-  const size_t head = (size_t)b * n * rs + (size_t)h * kHeadDim;
+  // Query rows of this lane: t = tw0 + 32nb + lane%32, token r + dil*t.
   bool is_local[2], is_zero[2];
   int qpos[2];
   bool any_local = false;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int tq = t0 + 32 * nb + (lane & 31);
+    const int tq = tw0 + 32 * nb + (lane & 31);
     const bool inq = tq < n_r;
     qpos[nb] = r + dil * (inq ? tq : n_r - 1);
     const int qm = inq ? mrow[qpos[nb]] : 0;
@@ -762,87 +792,168 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
     is_zero[nb] = inq && !loc && !glo;
     any_local |= is_local[nb];
   }
-  any_local = __any(any_local);
-
-  T* out = reinterpret_cast<T*>(p.out) + head;
-
-  if (!any_local) {
-    if (wv == 0) {
-      const float z[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        if (!is_zero[nb]) continue;
-        T* orow = out + (size_t)qpos[nb] * rs;
-#pragma unroll
-        for (int g = 0; g < 8; ++g) store4<B16>(orow + 8 * g + 4 * hh, z);
-        if (p.row_nnz && hh == 0) p.row_nnz[((size_t)b * p.H + h) * n + qpos[nb]] = 0;
-      }
-    }
-    return;
-  }
+  const bool wave_active = __any(any_local);
 
   const T* qh = reinterpret_cast<const T*>(p.q) + head;
   const T* kh = reinterpret_cast<const T*>(p.k) + head;
   const T* vh = reinterpret_cast<const T*>(p.v) + head;
+  T* out = reinterpret_cast<T*>(p.out) + head;
+
+  if (!__syncthreads_or(wave_active)) {
+    // nothing local in the tile: only zero rows to write
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      if (!is_zero[nb]) continue;
+      T* orow = out + (size_t)qpos[nb] * rs;
+      const float z[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int g = 0; g < 8; ++g) store4<B16>(orow + 8 * g + 4 * hh, z);
+      if (p.row_nnz && hh == 0) p.row_nnz[((size_t)b * p.H + h) * n + qpos[nb]] = 0;
+    }
+    return;
+  }
+
   Frag<B16> qf[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) load_frag(qf[nb], qh + (size_t)qpos[nb] * rs, hh);
 
+  // Key span: keys kbase + 32*blk + row of the residue sequence.
+  const int kbase = t0 - w;
+  const int S = (kWaveQ - 1 + w + w_hi) / kBlockK + 1;  // blocks per wave
+  const int nbt = 2 * (kWaves - 1) + S;                  // window blocks of the tile
+  const int ngb = (nG + kBlockK - 1) / kBlockK;         // global-column blocks
+  const int total = nbt + ngb;                           // blocks through the ring
+  const bool mask_in_lds = nbt <= kMaxSpanBlocks;
+
+  // Validity bits of window block blk: key in [0, n_r) with mask 1 or 2.
+  auto window_keymask = [&](int blk) -> uint32_t {
+    const int kk = kbase + kBlockK * blk + (lane & 31);
+    const bool inr = kk >= 0 && kk < n_r;
+    const int m = inr ? mrow[r + dil * kk] : 0;
+    return (uint32_t)__ballot(m == 1 || m == 2);
+  };
+  if (mask_in_lds) {
+    for (int blk = wv; blk < nbt; blk += kWaves) {
+      const uint32_t km = window_keymask(blk);
+      if (lane == 0) sh.kmask[blk] = km;
+    }
+  }
+
+  // Direct-to-LDS loads of ring block idx (window block idx, or global
+  // block idx - nbt): this wave fetches its parts of the K and V rows.
+  unsigned char* ring = sh.buf;
+  auto row_pos = [&](int idx, int row) -> int {
+    if (idx < nbt) {
+      const int kk = kbase + kBlockK * idx + row;
+      return r + dil * (kk < 0 ? 0 : (kk >= n_r ? n_r - 1 : kk));
+    }
+    const int gi = kBlockK * (idx - nbt) + row;
+    return sh.G[gi < nG ? gi : nG - 1];
+  };
+  auto block_empty = [&](int idx) {
+    const int k0 = kbase + kBlockK * idx;
+    return idx < nbt && (k0 + kBlockK - 1 < 0 || k0 >= n_r);
+  };
+  auto issue = [&](int idx) {
+    if (block_empty(idx)) return;
+    unsigned char* slot = ring + (idx % kRingSlots) * Ly::kStageBytes;
+    constexpr int kEltPerChunk = 16 / Ly::kElt;
+#pragma unroll
+    for (int part = wv; part < Ly::kLoads; part += kWaves) {
+      const int row = Ly::kRowsPerLoad * part + lane / Ly::kChunks;
+      const int c = lane % Ly::kChunks;
+      const uint32_t base = (uint32_t)row_pos(idx, row) * rs;
+      __builtin_amdgcn_global_load_lds(kh + (base + (c ^ kswz<B16>(row)) * kEltPerChunk),
+                                       (LDS_AS void*)(slot + 1024 * part), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vh + (base + (c ^ vswz<B16>(row)) * kEltPerChunk),
+                                       (LDS_AS void*)(slot + Ly::kBlockBytes + 1024 * part), 16, 0, 0);
+    }
+  };
+  for (int idx = 0; idx < kRingSlots && idx < total; ++idx) issue(idx);
+
   WaveState st;
   state_init(st);
-  unsigned char* lds = sh.buf + wv * Lay<B16>::kWaveBytes;
-
-  const int kbase = t0 - w;
-  const int t_last = min(t0 + kTileQ, n_r) - 1;
-  const int kfirst = max(kbase, 0);
-  const int klast = min(n_r - 1, causal ? t_last : t_last + w);
-  const int jlo = (kfirst - kbase) / kBlockK;
-  const int nblk = (klast - kbase) / kBlockK - jlo + 1;
   const float c = p.c;
+  const int wd = w * dil;
+  // window rows c in [A - 32 blk, B - 32 blk] hold keys in the query's window
+  int A[2], B[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int tq = tw0 + 32 * nb + (lane & 31);
+    A[nb] = tq - kbase - w - 4 * hh;
+    B[nb] = tq - kbase + w_hi - 4 * hh;
+  }
 
-  {
-    WindowSrc src;
-    src.mrow = mrow;
-    src.kbase = kbase;
-    src.jlo = jlo;
-    src.n_r = n_r;
-    src.r = r;
-    src.dil = dil;
-    src.t0 = t0;
-    src.w = w;
-    src.causal = causal;
-    src.lane = lane;
-    // row key = kbase + sh + kr with sh = 32(jlo+vb) and kr = c_r + 4hh;
-    // query t = t0 + 32nb + lane%32:  t - key in [lo, w]  <=>
-    // c_r in [t - kbase - w - 4hh - sh, t - kbase - lo - 4hh - sh]
+  const int steps = S + ngb;
+  for (int s = 0; s < steps; ++s) {
+    wait_vmem_all();   // this wave's parts of the blocks of step s have landed
+    __syncthreads();   // ... and every other wave's; step s-1 is done everywhere
+    if (s >= 1 && s + kRingSlots - 1 < total) issue(s + kRingSlots - 1);
+    if (!wave_active) continue;
+
+    const bool win = s < S;
+    const int idx = win ? 2 * wv + s : nbt + (s - S);
+    if (block_empty(idx)) continue;
+    uint32_t keymask;
+    if (win) {
+      keymask = mask_in_lds ? sh.kmask[idx] : window_keymask(idx);
+    } else {
+      const int left = nG - kBlockK * (s - S);
+      keymask = left >= kBlockK ? 0xffffffffu : ((1u << left) - 1u);
+    }
+    const unsigned char* slot = ring + (idx % kRingSlots) * Ly::kStageBytes;
+    Frag<B16> kf;
+    read_kfrag(kf, slot, lane);
+    VtFrag<B16> vt;
+    read_vt(vt, slot + Ly::kBlockBytes, lane);
+    if (keymask != 0xffffffffu) zero_dead_keys(vt, keymask, lane);
+
+    bool edge = true;
+    const int kb = kbase + kBlockK * idx;
+    if (win) {
+      bool interior = keymask == 0xffffffffu && (tw0 + kWaveQ - 1 - kb <= w);
+      interior = interior && (causal ? (tw0 >= kb + kBlockK - 1) : (kb + kBlockK - 1 - tw0 <= w));
+      edge = !interior;
+    }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const int tq = t0 + 32 * nb + (lane & 31);
-      const int lo = causal ? 0 : -w;
-      src.A[nb] = tq - kbase - w - 4 * hh;
-      src.B[nb] = tq - kbase - lo - 4 * hh;
+      f32x16 sc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+      qk(sc, kf, qf[nb]);
+      PFrag<B16> pf;
+      softmax_half<B16>(st, nb, sc, pf, edge,
+                        [&]() -> uint32_t {
+                          uint32_t vb;
+                          if (win) {
+                            const int sh32 = kBlockK * idx;
+                            const int lo = max(A[nb] - sh32, 0);
+                            const int hi = min(B[nb] - sh32, 31);
+                            vb = lo > hi ? 0u : ((0xffffffffu >> (31 - hi)) & (0xffffffffu << lo));
+                          } else {
+                            // a global key g joins local row i unless g is already in W(i)
+                            vb = 0;
+                            const int* gl = sh.G + kBlockK * (s - S) + 4 * hh;
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) {
+                              const int dd = qpos[nb] - gl[acc_c(e)];
+                              const bool in_w = (dd <= wd && dd >= -wd) && (dil == 1 || dd % dil == 0);
+                              vb |= in_w ? 0u : (1u << acc_c(e));
+                            }
+                          }
+                          return vb & (keymask >> (4 * hh));
+                        },
+                        c);
+      pv(st.o[nb], pf, vt);
     }
-    run_blocks<B16>(st, qf, src, kh, vh, rs, wv, nblk, lds, c);
   }
 
-  const int ngblk = (nG + kBlockK - 1) / kBlockK;
-  if (ngblk > 0) {
-    // global-column blocks continue the round-robin over waves
-    const int first = ((wv - nblk) % kWaves + kWaves) % kWaves;
-    GlobalColSrc src;
-    src.G = sh.G;
-    src.nG = nG;
-    src.dil = dil;
-    src.wd = w * dil;
-    src.lane = lane;
-    src.qpos[0] = qpos[0];
-    src.qpos[1] = qpos[1];
-    run_blocks<B16>(st, qf, src, kh, vh, rs, first, ngblk, lds, c);
+  // a wave without local rows still writes its zero (padding) rows
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    st.l[nb] += __shfl_xor(st.l[nb], 32);
+    st.cnt[nb] += __shfl_xor(st.cnt[nb], 32);
   }
-
-  merge_waves(st, sh);
-  if (wv != 0) return;
-
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     if (!is_local[nb] && !is_zero[nb]) continue;
@@ -903,7 +1014,7 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
   src.cend = cend;
   src.lane = lane;
 
-  for (int g0 = 0; g0 < nG; g0 += kTileQ) {
+  for (int g0 = 0; g0 < nG; g0 += kWaveQ) {
     Frag<B16> qf[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
