@@ -148,7 +148,6 @@ lf_status lf_attn_forward(const lf_attn_params* p, const void* q, const void* k,
   kp.tiles_per_b = (int32_t)pl.tiles_per_b;
   kp.n_band = (int32_t)(pl.tiles_per_b * p->B);
   kp.n_glob = pl.use_globals ? p->B * p->H * pl.S : 0;
-  kp.n_glob_pad = (kp.n_glob + 7) / 8 * 8;
   kp.S = pl.S;
   for (int h = 0; h < p->H; ++h) {
     kp.dil[h] = pl.dil[h];

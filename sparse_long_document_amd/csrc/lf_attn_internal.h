@@ -11,7 +11,7 @@ namespace lf {
 
 // Tiling constants shared by the host planner and the kernels.
 constexpr int kHeadDim = 64;       // D
-constexpr int kTileQ = 256;        // query rows of one band workgroup
+constexpr int kTileQ = 64;         // query rows of one band workgroup
 constexpr int kWaveQ = 64;         // query rows of one wave
 constexpr int kBlockK = 32;        // keys per inner block (M of the 32x32 MFMA)
 constexpr int kWaves = 4;          // waves per workgroup
@@ -38,7 +38,6 @@ struct KernelParams {
   int32_t tiles_per_b; // band workgroups per batch row
   int32_t n_band;      // band workgroups in the launch
   int32_t n_glob;      // global-row workgroups in the launch
-  int32_t n_glob_pad;  // n_glob rounded up to a multiple of 8 (XCD count)
   int32_t S;           // splits of a global row
   int32_t dil[LF_MAX_HEADS];
   int32_t tile0[LF_MAX_HEADS + 1];  // first band tile of each head within a batch row

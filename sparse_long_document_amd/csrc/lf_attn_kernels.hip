@@ -46,6 +46,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+
 #include <type_traits>
 
 #include "lf_attn_internal.h"
@@ -65,11 +66,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kNegInf = -__builtin_inff();
+// Initial reference max: finite and far below any score, so that
+// exp2(x - m) needs no special case (it is 0 for x = -inf or x = kMInit
+// against a real max, and the first scored block always moves m).
+constexpr float kMInit = -1.0e30f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
-
-// Merge of partial outputs: 2 slots of 64 lanes x 64 floats.
-constexpr int kMergeSlotFloats = 64 * 64;
-constexpr int kMergeBytes = 2 * kMergeSlotFloats * 4;
 
 // Per-wave LDS area: two stages, each holding one key block of K rows then
 // one of V rows (32 rows of 64 head dims each), filled by direct-to-LDS
@@ -84,9 +85,6 @@ struct Lay {
   static constexpr int kBlockBytes = kBlockK * kRowBytes;
   static constexpr int kStageBytes = 2 * kBlockBytes;
   static constexpr int kWaveBytes = 2 * kStageBytes;
-  static constexpr int kRingBytes = 8 * kStageBytes;  // shared ring of a band tile
-  static constexpr int kBufBytes0 = kWaves * kWaveBytes > kMergeBytes ? kWaves * kWaveBytes : kMergeBytes;
-  static constexpr int kBufBytes = kBufBytes0 > kRingBytes ? kBufBytes0 : kRingBytes;
 };
 
 // Chunk swizzles (the LDS position of 16-byte chunk c of row `row` is
@@ -331,7 +329,7 @@ struct WaveState {
 __device__ __forceinline__ void state_init(WaveState& st) {
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    st.m[nb] = kNegInf;
+    st.m[nb] = kMInit;
     st.l[nb] = 0.f;
     st.cnt[nb] = 0;
 #pragma unroll
@@ -341,9 +339,6 @@ __device__ __forceinline__ void state_init(WaveState& st) {
   }
 }
 
-__device__ __forceinline__ float max_across_halves(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
-}
 
 // Scores of one block for query half nb -> masked, online-softmax
 // probabilities, with that half's running state rescaled if its reference
@@ -364,13 +359,17 @@ __device__ __forceinline__ void softmax_half(WaveState& st, int nb, f32x16& s, P
     st.cnt[nb] += 16;
   }
 
-  float mx = s[0];
+  // Local max of this lane's 16 scores (a tree, to keep the chain short).
+  // Lanes l and l^32 hold the same query's other 16 keys, but the exchange
+  // is only needed when the reference max moves: the test "some score
+  // exceeds the reference by more than the slack" is a wave-wide vote.
+  float m4[4];
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  const float mb = max_across_halves(mx) * c;
-  if (__any(mb > st.m[nb] + kRescaleSlack)) {
-    const float mn = fmaxf(st.m[nb], mb);
-    const float alpha = (st.m[nb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(st.m[nb] - mn);
+  for (int g = 0; g < 4; ++g) m4[g] = fmaxf(fmaxf(s[4 * g], s[4 * g + 1]), fmaxf(s[4 * g + 2], s[4 * g + 3]));
+  const float mloc = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])) * c;
+  if (__any(mloc > st.m[nb] + kRescaleSlack)) {
+    const float mn = fmaxf(st.m[nb], fmaxf(mloc, __shfl_xor(mloc, 32)));
+    const float alpha = __builtin_amdgcn_exp2f(st.m[nb] - mn);
     st.m[nb] = mn;
     st.l[nb] *= alpha;
 #pragma unroll
@@ -379,23 +378,20 @@ __device__ __forceinline__ void softmax_half(WaveState& st, int nb, f32x16& s, P
       for (int r = 0; r < 16; ++r) st.o[nb][db][r] *= alpha;
   }
 
-  const float msub = (st.m[nb] == kNegInf) ? 0.f : st.m[nb];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -msub));
-  float sum = 0.f;
+  for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -st.m[nb]));
+  float t8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t8[i] = s[2 * i] + s[2 * i + 1];
+  const float sum = ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
   if constexpr (B16) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pf.x[ks][e] = (__bf16)s[8 * ks + e];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sum += s[r];
   } else {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      pf.x[r] = s[r];
-      sum += s[r];
-    }
+    for (int r = 0; r < 16; ++r) pf.x[r] = s[r];
   }
   st.l[nb] += sum;
 }
@@ -417,90 +413,105 @@ __device__ __forceinline__ void pv(f32x16 (&o)[2], const PFrag<false>& pf, const
 }
 
 // ---------------------------------------------------------------------------
-// A wave's pass over blocks first, first+4, ... < end of one key source.
+// A wave's stream of 32-key blocks first, first + 4, ... < end of one key
+// source, staged through the wave's own two-stage LDS area.  A block's K
+// and V^T fragments are read into registers before the direct-to-LDS loads
+// of the wave's next block are issued into the other stage, so those loads
+// are in flight while the current block is computed.
 // Src provides:
-//   kpos(vb, row) -> int           token position of key row `row` (clamped)
-//   locate(vb, mb&, inr&)          mask byte / existence of key row lane%32
-//   edge(vb, keymask) -> bool      whether masking is needed
-//   valid_bits(vb, nb) -> uint32   this lane's rows c_r in the key sets (edge blocks)
-//   dstep(), affine(vb, p0&)       evenly spaced in-range blocks: positions p0 + dstep*row
-// The loads of the wave's next block are in flight while the current one
-// is computed: its K and V^T fragments are read from LDS into registers
-// before the next block's direct-to-LDS loads are issued into the other
-// stage.
+//   kpos(i, row) -> int           token position of key row `row` (clamped)
+//   locate(i, mb&, inr&)          mask byte / existence of key row lane%32
+//   edge(i, keymask) -> bool      whether masking is needed
+//   valid_bits(i, nb) -> uint32   this lane's rows c_r in the key sets (edge blocks)
+//   dstep(), affine(i, p0&)       evenly spaced in-range blocks: positions p0 + dstep*row
 // ---------------------------------------------------------------------------
 template <bool B16, class Src>
-__device__ __forceinline__ void run_blocks(WaveState& st, const Frag<B16> (&qf)[2], const Src& src,
-                                           const elem_t<B16>* kb, const elem_t<B16>* vb, uint32_t rs, int first,
-                                           int end, unsigned char* lds, float c) {
+struct BlockPipe {
+  using T = elem_t<B16>;
   using L = Lay<B16>;
-  const int lane = lane_id();
-  const int hh = lane >> 5;
-  int mb = 0;
-  bool inr = false;
-  // Blocks whose 32 rows are in range and evenly spaced (token positions
-  // p0 + dstep*row) use a wave-uniform base address plus per-lane byte
-  // offsets that do not change from block to block.
-  const int dstep = src.dstep();
-  uint32_t off_k0 = 0, off_k1 = 0, off_v = 0;
-  if constexpr (B16) {
-    const uint32_t row_off = (uint32_t)dstep * (uint32_t)(lane >> 3) * rs;
-    const int ck = (lane & 7) ^ (lane >> 4);  // kswz of rows 8i + lane/8, i even
-    const int cv = (lane & 7) ^ (((lane >> 4) & 1) << 2);
-    off_k0 = 2u * (row_off + 8u * (uint32_t)ck);
-    off_k1 = 2u * (row_off + 8u * (uint32_t)(ck ^ 4));
-    off_v = 2u * (row_off + 8u * (uint32_t)cv);
+  const Src& src;
+  const T* kb;
+  const T* vb;
+  uint32_t rs;
+  unsigned char* lds;
+  int lane;
+  // Blocks whose 32 rows are in range and evenly spaced use a wave-uniform
+  // base address plus per-lane byte offsets that do not change from block
+  // to block.
+  uint32_t off_k0, off_k1, off_v;
+  int mb;    // mask byte of key row lane%32 of the last issued block
+  bool inr;  // whether that row exists
+
+  __device__ BlockPipe(const Src& s, const T* k, const T* v, uint32_t rs_, unsigned char* area)
+      : src(s), kb(k), vb(v), rs(rs_), lds(area), lane(lane_id()), off_k0(0), off_k1(0), off_v(0), mb(0),
+        inr(false) {
+    if constexpr (B16) {
+      const uint32_t row_off = (uint32_t)src.dstep() * (uint32_t)(lane >> 3) * rs;
+      const int ck = (lane & 7) ^ (lane >> 4);  // kswz of rows 8i + lane/8, i even
+      const int cv = (lane & 7) ^ (((lane >> 4) & 1) << 2);
+      off_k0 = 2u * (row_off + 8u * (uint32_t)ck);
+      off_k1 = 2u * (row_off + 8u * (uint32_t)(ck ^ 4));
+      off_v = 2u * (row_off + 8u * (uint32_t)cv);
+    }
   }
-  auto issue = [&](int blk, unsigned char* stage) {
+
+  __device__ void issue(int blk, int stage) {
+    unsigned char* dst = lds + stage * L::kStageBytes;
     src.locate(blk, mb, inr);
     int p0;
     if (B16 && src.affine(blk, p0)) {
-      const size_t step = (size_t)dstep * L::kRowsPerLoad * rs * 2;
+      const size_t step = (size_t)src.dstep() * L::kRowsPerLoad * rs * 2;
       const char* kbase = reinterpret_cast<const char*>(kb) + (size_t)p0 * rs * 2;
       const char* vbase = reinterpret_cast<const char*>(vb) + (size_t)p0 * rs * 2;
 #pragma unroll
       for (int i = 0; i < L::kLoads; ++i) {
         __builtin_amdgcn_global_load_lds(kbase + i * step + ((i & 1) ? off_k1 : off_k0),
-                                         (LDS_AS void*)(stage + 1024 * i), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vbase + i * step + off_v,
-                                         (LDS_AS void*)(stage + L::kBlockBytes + 1024 * i), 16, 0, 0);
+                                         (LDS_AS void*)(dst + 1024 * i), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vbase + i * step + off_v, (LDS_AS void*)(dst + L::kBlockBytes + 1024 * i),
+                                         16, 0, 0);
       }
     } else {
-      issue_block<B16>(kb, vb, rs, [&](int row) { return src.kpos(blk, row); }, stage, lane);
-    }
-  };
-  if (first < end) issue(first, lds);
-  int it = 0;
-  for (int blk = first; blk < end; blk += kWaves, ++it) {
-    unsigned char* cst = lds + (it & 1) * L::kStageBytes;
-    unsigned char* nst = lds + ((it + 1) & 1) * L::kStageBytes;
-    const bool kval = inr && (mb == 1 || mb == 2);
-    const uint32_t keymask = (uint32_t)__ballot(kval);
-    wait_vmem_all();  // this block's rows have landed in cst
-    if (keymask != 0xffffffffu) {
-      zero_dead_v_rows<B16>(cst + L::kBlockBytes, keymask, lane);
-      wave_sync();
-    }
-    Frag<B16> kf;
-    read_kfrag(kf, cst, lane);
-    VtFrag<B16> vt;
-    read_vt(vt, cst + L::kBlockBytes, lane);
-    if (blk + kWaves < end) issue(blk + kWaves, nst);
-
-    const bool edge = src.edge(blk, keymask);
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      f32x16 s;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
-      qk(s, kf, qf[nb]);
-      PFrag<B16> pf;
-      softmax_half<B16>(st, nb, s, pf, edge,
-                        [&]() { return src.valid_bits(blk, nb) & (keymask >> (4 * hh)); }, c);
-      pv(st.o[nb], pf, vt);
+      issue_block<B16>(kb, vb, rs, [&](int row) { return src.kpos(blk, row); }, dst, lane);
     }
   }
-}
+
+  // Blocks first, first + 4, ... < end into st; `primed`: block `first` has
+  // already been issued into stage 0.  halves: query halves holding rows.
+  __device__ void run(WaveState& st, const Frag<B16> (&qf)[2], int first, int end, float c, int halves,
+                      bool primed) {
+    const int hh = lane >> 5;
+    if (first < end && !primed) issue(first, 0);
+    int it = 0;
+    for (int blk = first; blk < end; blk += kWaves, ++it) {
+      const unsigned char* cst = lds + (it & 1) * L::kStageBytes;
+      const bool kval = inr && (mb == 1 || mb == 2);
+      const uint32_t keymask = (uint32_t)__ballot(kval);
+      wait_vmem_all();  // this block's rows have landed
+      Frag<B16> kf;
+      read_kfrag(kf, cst, lane);
+      VtFrag<B16> vt;
+      read_vt(vt, cst + L::kBlockBytes, lane);
+      if (blk + kWaves < end) issue(blk + kWaves, (it + 1) & 1);
+      if (keymask == 0u) continue;  // no key of the block is in any key set
+      if (keymask != 0xffffffffu) zero_dead_keys(vt, keymask, lane);
+
+      const bool edge = src.edge(blk, keymask);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        if (nb >= halves) break;  // query half without rows
+        f32x16 s;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+        qk(s, kf, qf[nb]);
+        PFrag<B16> pf;
+        softmax_half<B16>(st, nb, s, pf, edge,
+                          [&]() { return src.valid_bits(blk, nb) & (keymask >> (4 * hh)); }, c);
+        pv(st.o[nb], pf, vt);
+      }
+    }
+  }
+};
+
 
 // Bitmask of the bytes equal to 2 among mrow[p0 .. p0+16) (clipped to n).
 __device__ __forceinline__ uint32_t match16(const int8_t* __restrict__ mrow, int p0, int n) {
@@ -519,11 +530,24 @@ __device__ __forceinline__ uint32_t match16(const int8_t* __restrict__ mrow, int
   return bits;
 }
 
+// Exclusive prefix sum over the wave of a per-lane count in [0, 31],
+// from one ballot per bit (no lane exchange through LDS).
+__device__ __forceinline__ int wave_prefix(int cnt) {
+  int pre = 0;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const unsigned long long m = __ballot((cnt >> i) & 1);
+    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+    pre += below << i;
+  }
+  return pre;
+}
+
 // Ordered list of positions j with mask_row[j] == 2 into G (LDS), at most
 // cap entries; returns the total count.  Every thread of the workgroup
-// calls it and gets the same result.  Each thread looks at 16 bytes of a
-// 4 KB step; four steps are loaded together.
-__device__ int scan_globals(const int8_t* __restrict__ mrow, int n, int* G, int cap, int* s_wave) {
+// calls it and gets the same result.  Each thread looks at 16 bytes of each
+// 4 KB step; four steps are loaded together and ranked with one barrier.
+__device__ int scan_globals(const int8_t* __restrict__ mrow, int n, int* G, int cap, int (*s_tot)[kWaves]) {
   constexpr int kStep = kThreads * 16;
   int total = 0;
   const int tid = threadIdx.x;
@@ -534,128 +558,110 @@ __device__ int scan_globals(const int8_t* __restrict__ mrow, int n, int* G, int 
 #pragma unroll
     for (int u = 0; u < 4; ++u) bits[u] = match16(mrow, base + u * kStep + 16 * tid, n);
     if (!__syncthreads_or((bits[0] | bits[1] | bits[2] | bits[3]) != 0)) continue;
+    int pre[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (!__syncthreads_or(bits[u] != 0)) continue;
       const int cnt = __popc(bits[u]);
-      int x = cnt;
+      pre[u] = wave_prefix(cnt);
+      if (lane == 63) s_tot[u][wv] = pre[u] + cnt;
+    }
+    __syncthreads();
+    int off = total;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-      }
-      if (lane == 63) s_wave[wv] = x;
-      __syncthreads();
-      int before = 0, all = 0;
+    for (int u = 0; u < 4; ++u) {
+      int slot = off + pre[u];
 #pragma unroll
       for (int i = 0; i < kWaves; ++i) {
-        const int t = s_wave[i];
-        before += (i < wv) ? t : 0;
-        all += t;
+        const int t = s_tot[u][i];
+        slot += (i < wv) ? t : 0;
+        off += t;
       }
-      int slot = total + before + x - cnt;
-      uint32_t b = bits[u];
-      while (b) {
-        const int e = __builtin_ctz(b);
-        b &= b - 1;
+      uint32_t bm = bits[u];
+      while (bm) {
+        const int e = __builtin_ctz(bm);
+        bm &= bm - 1;
         if (slot < cap) G[slot] = base + u * kStep + 16 * tid + e;
         ++slot;
       }
-      total += all;
     }
+    total = off;
+    __syncthreads();  // s_tot is reused by the next steps
   }
-  return total;
+  return __builtin_amdgcn_readfirstlane(total);  // the same in every lane
 }
-
-// Band tiles keep the key-validity bits of their whole key span in LDS when
-// it has at most this many 32-key blocks.
-constexpr int kMaxSpanBlocks = 512;
-constexpr int kRingSlots = 8;
 
 template <bool B16>
 struct Shared {
   int G[LF_MAX_GLOBAL];
-  uint32_t kmask[kMaxSpanBlocks];
-  int wave_tmp[kWaves];
+  int wave_tmp[4][kWaves];
   int flag;
   float m[kWaves][kWaveQ];
   float l[kWaves][kWaveQ];
   int cnt[kWaves][kWaveQ];
-  __attribute__((aligned(16))) unsigned char buf[Lay<B16>::kBufBytes];
+  __attribute__((aligned(16))) unsigned char buf[kWaves * Lay<B16>::kWaveBytes];
 };
 
-// Merge the partial results of the 4 waves into wave 0's registers.
-template <bool B16>
-__device__ void merge_waves(WaveState& st, Shared<B16>& sh) {
+// The four waves of a workgroup hold partial results for the same 64 query
+// columns over disjoint key subsets.  Each wave parks its state in its own
+// LDS area (all its loads have landed, and no other wave touches that
+// area); after one barrier, wave w merges quadrant (query half w/2, head-dim
+// half w%2) of the four partials and passes, per lane, the merged max M
+// (log2 domain), row sum L, key count and the 16 unnormalised outputs of
+// head dims 32db + 8g + 4(lane/32) + i (in o[4g + i]) to
+// emit(nb, db, M, L, cnt, o).
+template <bool B16, class Emit>
+__device__ void combine_waves(const WaveState& st, Shared<B16>& sh, Emit emit) {
+  static_assert(Lay<B16>::kWaveBytes >= 64 * 64 * 4, "a wave's area holds its 64 x 64 fp32 partial");
   const int lane = lane_id();
   const int hh = lane >> 5;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  f32x4* mine = reinterpret_cast<f32x4*>(sh.buf + wv * Lay<B16>::kWaveBytes);
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    st.l[nb] += __shfl_xor(st.l[nb], 32);
-    st.cnt[nb] += __shfl_xor(st.cnt[nb], 32);
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        mine[((nb * 2 + db) * 4 + g) * 64 + lane] = f32x4{st.o[nb][db][4 * g], st.o[nb][db][4 * g + 1],
+                                                          st.o[nb][db][4 * g + 2], st.o[nb][db][4 * g + 3]};
+    const float l = st.l[nb] + __shfl_xor(st.l[nb], 32);
+    const int cnt = st.cnt[nb] + __shfl_xor(st.cnt[nb], 32);
     if (hh == 0) {
       sh.m[wv][32 * nb + lane] = st.m[nb];
-      sh.l[wv][32 * nb + lane] = st.l[nb];
-      sh.cnt[wv][32 * nb + lane] = st.cnt[nb];
+      sh.l[wv][32 * nb + lane] = l;
+      sh.cnt[wv][32 * nb + lane] = cnt;
     }
   }
-  float* slots = reinterpret_cast<float*>(sh.buf);
-  auto write_slot = [&](int slot) {
-    f32x4* dst = reinterpret_cast<f32x4*>(slots + slot * kMergeSlotFloats);
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 t = f32x4{st.o[nb][db][4 * g], st.o[nb][db][4 * g + 1], st.o[nb][db][4 * g + 2],
-                                st.o[nb][db][4 * g + 3]};
-          dst[((nb * 2 + db) * 4 + g) * 64 + lane] = t;
-        }
-  };
-  auto absorb = [&](int slot, int other) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(slots + slot * kMergeSlotFloats);
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int q = 32 * nb + (lane & 31);
-      const float mo = sh.m[other][q];
-      const float lo = sh.l[other][q];
-      const int co = sh.cnt[other][q];
-      const float mn = fmaxf(st.m[nb], mo);
-      const float fs = (st.m[nb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(st.m[nb] - mn);
-      const float fo = (mo == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
-      st.m[nb] = mn;
-      st.l[nb] = st.l[nb] * fs + lo * fo;
-      st.cnt[nb] += co;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 t = src[((nb * 2 + db) * 4 + g) * 64 + lane];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) st.o[nb][db][4 * g + i] = st.o[nb][db][4 * g + i] * fs + t[i] * fo;
-        }
-    }
-  };
-  __syncthreads();  // all waves done with their V buffers (aliased below)
-  if (wv >= 2) write_slot(wv - 2);
   __syncthreads();
-  if (wv < 2) absorb(wv, wv + 2);
-  __syncthreads();
-  if (wv == 1) {
-    write_slot(0);
+  const int nb = wv >> 1, db = wv & 1;
+  const int q = 32 * nb + (lane & 31);
+  float mw[kWaves];
+  float M = kNegInf;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      if (hh == 0) {
-        sh.m[1][32 * nb + lane] = st.m[nb];
-        sh.l[1][32 * nb + lane] = st.l[nb];
-        sh.cnt[1][32 * nb + lane] = st.cnt[nb];
-      }
+  for (int w = 0; w < kWaves; ++w) {
+    mw[w] = sh.m[w][q];
+    M = fmaxf(M, mw[w]);
   }
-  __syncthreads();
-  if (wv == 0) absorb(0, 1);
+  float Lsum = 0.f, o[16];
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) o[i] = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float f = __builtin_amdgcn_exp2f(mw[w] - M);
+    Lsum = __builtin_fmaf(sh.l[w][q], f, Lsum);
+    cnt += sh.cnt[w][q];
+    const f32x4* part = reinterpret_cast<const f32x4*>(sh.buf + w * Lay<B16>::kWaveBytes);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 t = part[((nb * 2 + db) * 4 + g) * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[4 * g + i] = __builtin_fmaf(t[i], f, o[4 * g + i]);
+    }
+  }
+  emit(nb, db, M, Lsum, cnt, o);
 }
+
 
 template <bool B16>
 __device__ __forceinline__ void store4(elem_t<B16>* dst, const float* v);
@@ -675,6 +681,18 @@ __device__ __forceinline__ void store4<false>(float* dst, const float* v) {
   *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
 }
 
+// Partial records of the global-row splits cross XCDs, whose L2 caches are
+// not coherent with each other.  They are written with agent-scope atomic
+// stores and read back with agent-scope atomic loads, both of which go to
+// the device-wide coherence point; this avoids an agent-scope release
+// fence, which would write back every dirty line of the XCD's L2.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ int xcd_remap(int x, int N) {
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous range of tiles so neighbouring tiles (which share K/V
@@ -682,6 +700,20 @@ __device__ __forceinline__ int xcd_remap(int x, int N) {
   const int per = N / 8, rem = N % 8;
   const int xcd = x % 8, y = x / 8;
   return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + y;
+}
+
+// Output values of one quadrant of a row: head dims 32db + 8g + 4hh + i
+// from o[4g + i], times inv (or zeros).
+template <bool B16>
+__device__ __forceinline__ void store_quadrant(elem_t<B16>* row, int db, int hh, const float* o, float inv,
+                                               bool zero) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = zero ? 0.f : o[4 * g + i] * inv;
+    store4<B16>(row + 32 * db + 8 * g + 4 * hh, t);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -709,19 +741,267 @@ struct ChunkSrc {
   __device__ uint32_t valid_bits(int, int) const { return 0xffffffffu; }
 };
 
+// Blocks of a band tile: first the non-empty 32-key blocks of the tile's
+// window span (residue-sequence keys kbase + 32 (jlo + i) + row, tokens
+// r + dil * key), then the blocks of the row's global tokens G[32 (i - nwin) + row].
+struct BandSrc {
+  const int8_t* mrow;
+  const int* G;
+  int kbase, jlo, nwin;
+  int n_r, r, dil, nG, lane;
+  int t0, w, wd;
+  bool causal;
+  int A[2], B[2];  // window rows c in [A - 32 j, B - 32 j] of block j hold keys in the query's window
+  int qpos[2];     // token position of the lane's query of each half
+  __device__ int key(int i, int row) const { return kbase + kBlockK * (jlo + i) + row; }
+  __device__ int kpos(int i, int row) const {
+    if (i < nwin) {
+      const int kk = key(i, row);
+      return r + dil * (kk < 0 ? 0 : (kk >= n_r ? n_r - 1 : kk));
+    }
+    const int gi = kBlockK * (i - nwin) + row;
+    return G[gi < nG ? gi : nG - 1];
+  }
+  __device__ void locate(int i, int& mb, bool& inr) const {
+    const int row = lane & 31;
+    if (i < nwin) {
+      const int kk = key(i, row);
+      inr = kk >= 0 && kk < n_r;
+    } else {
+      inr = kBlockK * (i - nwin) + row < nG;
+    }
+    mb = mrow[kpos(i, row)];
+  }
+  __device__ int dstep() const { return dil; }
+  __device__ bool affine(int i, int& p0) const {
+    if (i >= nwin) return false;
+    const int k0 = key(i, 0);
+    p0 = r + dil * k0;
+    return k0 >= 0 && k0 + kBlockK - 1 < n_r;
+  }
+  __device__ uint32_t valid_bits(int i, int nb) const {
+    if (i < nwin) {
+      const int sh32 = kBlockK * (jlo + i);
+      const int lo = max(A[nb] - sh32, 0);
+      const int hi = min(B[nb] - sh32, 31);
+      return lo > hi ? 0u : ((0xffffffffu >> (31 - hi)) & (0xffffffffu << lo));
+    }
+    // A global key g joins local row i unless g is already in W(i):
+    // |i - g| <= w d and d divides i - g (no causal rows have global columns).
+    const int4* gl = reinterpret_cast<const int4*>(G + kBlockK * (i - nwin) + 4 * (lane >> 5));
+    const uint32_t span = 2u * (uint32_t)wd;
+    uint32_t vb = 0;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int4 x = gl[2 * g4];  // rows 8 g4 + 4 hh + [0, 4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int dd = qpos[nb] - x[e];
+        bool in_w = (uint32_t)(dd + wd) <= span;
+        if (dil != 1) in_w = in_w && (dd % dil == 0);
+        vb |= in_w ? 0u : (1u << (8 * g4 + e));
+      }
+    }
+    return vb;
+  }
+};
+
 // ---------------------------------------------------------------------------
-// Band workgroup: one tile of kTileQ = 256 query rows of (b, h, residue r);
-// wave w owns rows t0 + 64w .. t0 + 64w + 63 outright.
-//
-// The tile's key span is cut into 32-key blocks; wave w needs blocks
-// 2w .. 2w + S - 1.  The waves walk their blocks in lockstep, staggered:
-// at step s wave w computes block 2w + s, so the blocks in use at one step
-// are s, s+2, s+4, s+6.  Blocks live in an 8-slot LDS ring shared by the
-// workgroup (slot = block % 8); each block is fetched once per workgroup
-// with direct-to-LDS loads, one part per wave, one step before its first
-// use.  After the window blocks come the global-column blocks (the global
-// keys of the batch row), which every wave computes at the same step.
-// One barrier per step separates the ring's reuse from its reads.
+// Band tile block loop.
+// ---------------------------------------------------------------------------
+
+// Raw (untyped) buffer resource over `bytes` bytes at `base`; accesses past
+// the end read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ float max16(const f32x16& s) {
+  const float a = fmaxf(fmaxf(s[0], s[1]), s[2]);
+  const float b = fmaxf(fmaxf(s[3], s[4]), s[5]);
+  const float d = fmaxf(fmaxf(s[6], s[7]), s[8]);
+  const float e = fmaxf(fmaxf(s[9], s[10]), s[11]);
+  const float f = fmaxf(fmaxf(s[12], s[13]), s[14]);
+  return fmaxf(fmaxf(fmaxf(a, b), d), fmaxf(fmaxf(e, f), s[15]));
+}
+
+// Both query halves of a block, after masking (masked scores are -inf):
+// online softmax (same arithmetic as softmax_half); counts 16 scored keys
+// per lane and half.
+template <bool B16>
+__device__ __forceinline__ void softmax_full2(WaveState& st, f32x16 (&s)[2], PFrag<B16> (&pf)[2], float c) {
+  float ml[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) ml[nb] = max16(s[nb]) * c;
+  if (__any((ml[0] > st.m[0] + kRescaleSlack) | (ml[1] > st.m[1] + kRescaleSlack))) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float mn = fmaxf(st.m[nb], fmaxf(ml[nb], __shfl_xor(ml[nb], 32)));
+      const float alpha = __builtin_amdgcn_exp2f(st.m[nb] - mn);
+      st.m[nb] = mn;
+      st.l[nb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.o[nb][db][r] *= alpha;
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[nb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][r], c, -st.m[nb]));
+    float t8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t8[i] = s[nb][2 * i] + s[nb][2 * i + 1];
+    st.l[nb] += ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
+    st.cnt[nb] += 16;
+    if constexpr (B16) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[nb].x[ks][e] = (__bf16)s[nb][8 * ks + e];
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pf[nb].x[r] = s[nb][r];
+    }
+  }
+}
+
+// A wave's blocks i = first, first + 4, ... < end of a band tile: window
+// blocks (i < nwin) then global-column blocks, staged through the wave's
+// two-stage LDS area.  Every (block, query half) pair is classified on the
+// scalar unit as full (all 32 keys in every row's key set), partial (masked
+// per element) or empty; only blocks with a full half on both sides skip
+// the masking, and blocks empty on both sides are skipped.
+template <bool B16>
+struct BandLoop {
+  using T = elem_t<B16>;
+  using L = Lay<B16>;
+  const BandSrc& src;
+  const T* kb;
+  const T* vb;
+  uint32_t rs;
+  unsigned char* lds;
+  int lane;
+  int t0, w, w_hi;
+  // buffer resources and per-lane offsets of the evenly spaced (affine) fast path
+  __amdgpu_buffer_rsrc_t rk, rv, rm;
+  uint32_t vk0, vk1, vv, vm;
+  int mb;    // mask byte of key row lane%32 of the last issued block
+  bool inr;  // whether that row exists
+
+  __device__ BandLoop(const BandSrc& s, const T* k, const T* v, uint32_t rs_, unsigned char* area, int n, int t0_,
+                      int w_, int w_hi_)
+      : src(s), kb(k), vb(v), rs(rs_), lds(area), lane(lane_id()), t0(t0_), w(w_), w_hi(w_hi_), mb(0),
+        inr(false) {
+    const uint32_t bytes = (uint32_t)(((size_t)(n - 1) * rs + kHeadDim) * sizeof(T));
+    rk = make_rsrc(k, bytes);
+    rv = make_rsrc(v, bytes);
+    rm = make_rsrc(src.mrow, (uint32_t)n);
+    const uint32_t row_off = (uint32_t)src.dil * (uint32_t)(lane >> 3) * rs;
+    const int ck = (lane & 7) ^ (lane >> 4);  // kswz of rows 8t + lane/8, t even
+    const int cv = (lane & 7) ^ (((lane >> 4) & 1) << 2);
+    vk0 = 2u * (row_off + 8u * (uint32_t)ck);
+    vk1 = 2u * (row_off + 8u * (uint32_t)(ck ^ 4));
+    vv = 2u * (row_off + 8u * (uint32_t)cv);
+    vm = (uint32_t)src.dil * (uint32_t)(lane & 31);
+  }
+
+  __device__ void issue(int i, unsigned char* dst) {
+    int p0;
+    if (B16 && src.affine(i, p0)) {
+      const uint32_t so = (uint32_t)p0 * rs * 2u;
+      const uint32_t step = (uint32_t)src.dil * (uint32_t)L::kRowsPerLoad * rs * 2u;
+      mb = (int)(signed char)__builtin_amdgcn_raw_buffer_load_b8(rm, vm, (uint32_t)p0, 0);
+      inr = true;
+#pragma unroll
+      for (int t = 0; t < L::kLoads; ++t) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)(dst + 1024 * t), 16, (t & 1) ? vk1 : vk0,
+                                                 so + t * step, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS_AS void*)(dst + L::kBlockBytes + 1024 * t), 16, vv,
+                                                 so + t * step, 0, 0);
+      }
+    } else {
+      src.locate(i, mb, inr);
+      issue_block<B16>(kb, vb, rs, [&](int row) { return src.kpos(i, row); }, dst, lane);
+    }
+  }
+
+  // 0 = empty, 1 = partial, 2 = full for query half nb of window block i.
+  __device__ int classify(int i, int nb, uint32_t keymask) const {
+    const int k0 = src.key(i, 0);
+    const int qlo = t0 + 32 * nb, qhi = qlo + 31;
+    if (k0 > qhi + w_hi || k0 + kBlockK - 1 < qlo - w) return 0;
+    if (qlo >= src.n_r) return 0;  // no rows in this half
+    const bool full = keymask == 0xffffffffu && k0 >= qhi - w && k0 + kBlockK - 1 <= qlo + w_hi;
+    return full ? 2 : 1;
+  }
+
+  template <int kStage>
+  __device__ __forceinline__ void step(WaveState& st, const Frag<B16> (&qf)[2], int i, int end, float c) {
+    const int hh = lane >> 5;
+    const unsigned char* cst = lds + kStage * L::kStageBytes;
+    const bool kval = inr && (mb == 1 || mb == 2);
+    const uint32_t keymask = (uint32_t)__ballot(kval);
+    wait_vmem_all();  // this block's rows have landed
+    Frag<B16> kf;
+    read_kfrag(kf, cst, lane);
+    VtFrag<B16> vt;
+    read_vt(vt, cst + L::kBlockBytes, lane);
+    if (i + kWaves < end) issue(i + kWaves, lds + (kStage ^ 1) * L::kStageBytes);
+    if (keymask == 0u) return;  // no key of the block is in any key set
+    if (keymask != 0xffffffffu) zero_dead_keys(vt, keymask, lane);
+
+    const bool win = i < src.nwin;
+    int cls[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) cls[nb] = win ? classify(i, nb, keymask) : (t0 + 32 * nb < src.n_r ? 1 : 0);
+    if (cls[0] == 0 && cls[1] == 0) return;
+
+    f32x16 s[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[nb][r] = 0.f;
+      qk(s[nb], kf, qf[nb]);
+    }
+    if (cls[0] != 2 || cls[1] != 2) {
+      // keep the mask work inside the (uniform) branch
+      __asm__ volatile("" ::: "memory");
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        uint32_t vmk = 0xffffffffu;  // bit c_r set <=> element r is in its row's key set
+        if (cls[nb] == 0)
+          vmk = 0u;
+        else if (cls[nb] == 1)
+          vmk = src.valid_bits(i, nb) & (keymask >> (4 * hh));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[nb][r] = (vmk & (1u << acc_c(r))) ? s[nb][r] : kNegInf;
+        st.cnt[nb] += __popc(vmk & 0x0f0f0f0fu) - 16;  // the softmax below adds 16
+      }
+    }
+    PFrag<B16> pf[2];
+    softmax_full2<B16>(st, s, pf, c);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) pv(st.o[nb], pf[nb], vt);
+  }
+
+  // first: the wave's first block, already issued into stage 0.
+  __device__ void run(WaveState& st, const Frag<B16> (&qf)[2], int first, int end, float c) {
+    for (int i = first; i < end; i += 2 * kWaves) {
+      step<0>(st, qf, i, end, c);
+      if (i + kWaves >= end) break;
+      step<1>(st, qf, i + kWaves, end, c);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Band workgroup: one tile of kTileQ = 64 query rows t0 .. t0 + 63 of the
+// residue sequence r of (b, h).  Its key blocks (window span, then the
+// global columns) are dealt to the 4 waves round-robin; every wave scores
+// all 64 queries against its own blocks, and the partials are merged
+// through LDS at the end.  Writes local rows (mask 1) and zero rows (mask 0).
 // ---------------------------------------------------------------------------
 template <bool B16>
 __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
@@ -733,8 +1013,15 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
 
   const int b = L / p.tiles_per_b;
   const int rem = L - b * p.tiles_per_b;
+  // head: tile0 is non-decreasing; count entries <= rem, 8 loads per round
   int h = 0;
-  while (h + 1 < p.H && p.tile0[h + 1] <= rem) ++h;
+  for (int k0 = 1; k0 < p.H; k0 += 8) {
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) cnt += (k0 + k < p.H && p.tile0[k0 + k] <= rem) ? 1 : 0;
+    h += cnt;
+    if (cnt < 8) break;
+  }
   const int id = rem - p.tile0[h];
   const int dil = p.dil[h];
   const int n = p.n;
@@ -752,224 +1039,111 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
     n_r = qn;
   }
   const int t0 = tt * kTileQ;
-  const int tw0 = t0 + kWaveQ * wv;  // this wave's first query row
   const int w = p.w;
   const bool causal = p.causal != 0;
   const int w_hi = causal ? 0 : w;
   const int8_t* mrow = p.mask + (size_t)b * n;
   const uint32_t rs = (uint32_t)p.H * kHeadDim;  // elements between tokens
   const size_t head = (size_t)b * n * rs + (size_t)h * kHeadDim;
+  const T* qh = reinterpret_cast<const T*>(p.q) + head;
+  T* out = reinterpret_cast<T*>(p.out) + head;
 
-  int nG = 0;
+  // Window span: residue-sequence keys kbase + 32 j + row, j < S; only
+  // blocks jlo .. jhi - 1 hold keys in [0, n_r).
+  const int kbase = t0 - w;
+  const int S = (kTileQ - 1 + w + w_hi) / kBlockK + 1;
+  const int jlo = kbase >= 0 ? 0 : (-kbase) / kBlockK;
+  const int jhi = min(S, (n_r - kbase + kBlockK - 1) / kBlockK);
+
+  // Query rows of this lane: t = t0 + 32nb + lane%32, token r + dil*t.
+  BandSrc src;
+  int qm[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int tq = t0 + 32 * nb + (lane & 31);
+    const bool inq = tq < n_r;
+    src.qpos[nb] = r + dil * (inq ? tq : n_r - 1);
+    qm[nb] = inq ? mrow[src.qpos[nb]] : 0;
+    src.A[nb] = tq - kbase - w - 4 * hh;
+    src.B[nb] = tq - kbase + w_hi - 4 * hh;
+  }
+  Frag<B16> qf[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) load_frag(qf[nb], qh + (size_t)src.qpos[nb] * rs, hh);
+
+  src.mrow = mrow;
+  src.G = sh.G;
+  src.kbase = kbase;
+  src.jlo = jlo;
+  src.nwin = jhi - jlo;
+  src.n_r = n_r;
+  src.r = r;
+  src.dil = dil;
+  src.nG = 0;
+  src.lane = lane;
+  src.t0 = t0;
+  src.w = w;
+  src.wd = w * dil;
+  src.causal = causal;
+  unsigned char* area = sh.buf + wv * Ly::kWaveBytes;
+  BandLoop<B16> loop(src, reinterpret_cast<const T*>(p.k) + head, reinterpret_cast<const T*>(p.v) + head, rs, area, n,
+                     t0, w, w_hi);
+  const bool primed = wv < src.nwin;
+  if (primed) loop.issue(wv, area);  // the wave's first window block flies during the scan
+
   if (p.use_globals) {
-    nG = scan_globals(mrow, n, sh.G, LF_MAX_GLOBAL, sh.wave_tmp);
+    int nG = scan_globals(mrow, n, sh.G, LF_MAX_GLOBAL, sh.wave_tmp);
     if (nG > p.max_global) {
       if (threadIdx.x == 0) atomicOr(p.status, LF_DEV_TOO_MANY_GLOBALS);
       nG = p.max_global;
     }
+    src.nG = __builtin_amdgcn_readfirstlane(nG);  // uniform (the status write above diverges)
   }
+  const int end = src.nwin + (src.nG + kBlockK - 1) / kBlockK;
+  if (!primed && wv < end) loop.issue(wv, area);  // the wave starts on a global-column block
 
-  // Query rows of this lane: t = tw0 + 32nb + lane%32, token r + dil*t.
   bool is_local[2], is_zero[2];
-  int qpos[2];
   bool any_local = false;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int tq = tw0 + 32 * nb + (lane & 31);
+    const int tq = t0 + 32 * nb + (lane & 31);
     const bool inq = tq < n_r;
-    qpos[nb] = r + dil * (inq ? tq : n_r - 1);
-    const int qm = inq ? mrow[qpos[nb]] : 0;
     bool loc, glo;
     if (p.use_globals) {
-      loc = qm == 1;
-      glo = qm == 2;
+      loc = qm[nb] == 1;
+      glo = qm[nb] == 2;
     } else {
-      loc = qm == 1 || qm == 2;
+      loc = qm[nb] == 1 || qm[nb] == 2;
       glo = false;
-      if (qm == 2 && !causal && p.max_global == 0) atomicOr(p.status, LF_DEV_TOO_MANY_GLOBALS);
+      if (qm[nb] == 2 && !causal && p.max_global == 0) atomicOr(p.status, LF_DEV_TOO_MANY_GLOBALS);
     }
     is_local[nb] = inq && loc;
     is_zero[nb] = inq && !loc && !glo;
     any_local |= is_local[nb];
   }
-  const bool wave_active = __any(any_local);
-
-  const T* qh = reinterpret_cast<const T*>(p.q) + head;
-  const T* kh = reinterpret_cast<const T*>(p.k) + head;
-  const T* vh = reinterpret_cast<const T*>(p.v) + head;
-  T* out = reinterpret_cast<T*>(p.out) + head;
-
-  if (!__syncthreads_or(wave_active)) {
-    // nothing local in the tile: only zero rows to write
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      if (!is_zero[nb]) continue;
-      T* orow = out + (size_t)qpos[nb] * rs;
-      const float z[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int g = 0; g < 8; ++g) store4<B16>(orow + 8 * g + 4 * hh, z);
-      if (p.row_nnz && hh == 0) p.row_nnz[((size_t)b * p.H + h) * n + qpos[nb]] = 0;
+  // every wave holds the same queries, so this test agrees across the workgroup
+  if (!__any(any_local)) {
+    wait_vmem_all();  // the primed loads land before the workgroup's LDS is released
+    const int nb = wv >> 1, db = wv & 1;
+    if (nb ? is_zero[1] : is_zero[0]) {
+      const int qp = nb ? src.qpos[1] : src.qpos[0];
+      store_quadrant<B16>(out + (size_t)qp * rs, db, hh, nullptr, 0.f, true);
+      if (p.row_nnz && db == 0 && hh == 0) p.row_nnz[((size_t)b * p.H + h) * n + qp] = 0;
     }
     return;
   }
 
-  Frag<B16> qf[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) load_frag(qf[nb], qh + (size_t)qpos[nb] * rs, hh);
-
-  // Key span: keys kbase + 32*blk + row of the residue sequence.
-  const int kbase = t0 - w;
-  const int S = (kWaveQ - 1 + w + w_hi) / kBlockK + 1;  // blocks per wave
-  const int nbt = 2 * (kWaves - 1) + S;                  // window blocks of the tile
-  const int ngb = (nG + kBlockK - 1) / kBlockK;         // global-column blocks
-  const int total = nbt + ngb;                           // blocks through the ring
-  const bool mask_in_lds = nbt <= kMaxSpanBlocks;
-
-  // Validity bits of window block blk: key in [0, n_r) with mask 1 or 2.
-  auto window_keymask = [&](int blk) -> uint32_t {
-    const int kk = kbase + kBlockK * blk + (lane & 31);
-    const bool inr = kk >= 0 && kk < n_r;
-    const int m = inr ? mrow[r + dil * kk] : 0;
-    return (uint32_t)__ballot(m == 1 || m == 2);
-  };
-  if (mask_in_lds) {
-    for (int blk = wv; blk < nbt; blk += kWaves) {
-      const uint32_t km = window_keymask(blk);
-      if (lane == 0) sh.kmask[blk] = km;
-    }
-  }
-
-  // Direct-to-LDS loads of ring block idx (window block idx, or global
-  // block idx - nbt): this wave fetches its parts of the K and V rows.
-  unsigned char* ring = sh.buf;
-  auto row_pos = [&](int idx, int row) -> int {
-    if (idx < nbt) {
-      const int kk = kbase + kBlockK * idx + row;
-      return r + dil * (kk < 0 ? 0 : (kk >= n_r ? n_r - 1 : kk));
-    }
-    const int gi = kBlockK * (idx - nbt) + row;
-    return sh.G[gi < nG ? gi : nG - 1];
-  };
-  auto block_empty = [&](int idx) {
-    const int k0 = kbase + kBlockK * idx;
-    return idx < nbt && (k0 + kBlockK - 1 < 0 || k0 >= n_r);
-  };
-  auto issue = [&](int idx) {
-    if (block_empty(idx)) return;
-    unsigned char* slot = ring + (idx % kRingSlots) * Ly::kStageBytes;
-    constexpr int kEltPerChunk = 16 / Ly::kElt;
-#pragma unroll
-    for (int part = wv; part < Ly::kLoads; part += kWaves) {
-      const int row = Ly::kRowsPerLoad * part + lane / Ly::kChunks;
-      const int c = lane % Ly::kChunks;
-      const uint32_t base = (uint32_t)row_pos(idx, row) * rs;
-      __builtin_amdgcn_global_load_lds(kh + (base + (c ^ kswz<B16>(row)) * kEltPerChunk),
-                                       (LDS_AS void*)(slot + 1024 * part), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vh + (base + (c ^ vswz<B16>(row)) * kEltPerChunk),
-                                       (LDS_AS void*)(slot + Ly::kBlockBytes + 1024 * part), 16, 0, 0);
-    }
-  };
-  for (int idx = 0; idx < kRingSlots && idx < total; ++idx) issue(idx);
-
   WaveState st;
   state_init(st);
-  const float c = p.c;
-  const int wd = w * dil;
-  // window rows c in [A - 32 blk, B - 32 blk] hold keys in the query's window
-  int A[2], B[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int tq = tw0 + 32 * nb + (lane & 31);
-    A[nb] = tq - kbase - w - 4 * hh;
-    B[nb] = tq - kbase + w_hi - 4 * hh;
-  }
-
-  const int steps = S + ngb;
-  for (int s = 0; s < steps; ++s) {
-    wait_vmem_all();   // this wave's parts of the blocks of step s have landed
-    __syncthreads();   // ... and every other wave's; step s-1 is done everywhere
-    if (s >= 1 && s + kRingSlots - 1 < total) issue(s + kRingSlots - 1);
-    if (!wave_active) continue;
-
-    const bool win = s < S;
-    const int idx = win ? 2 * wv + s : nbt + (s - S);
-    if (block_empty(idx)) continue;
-    uint32_t keymask;
-    if (win) {
-      keymask = mask_in_lds ? sh.kmask[idx] : window_keymask(idx);
-    } else {
-      const int left = nG - kBlockK * (s - S);
-      keymask = left >= kBlockK ? 0xffffffffu : ((1u << left) - 1u);
-    }
-    const unsigned char* slot = ring + (idx % kRingSlots) * Ly::kStageBytes;
-    Frag<B16> kf;
-    read_kfrag(kf, slot, lane);
-    VtFrag<B16> vt;
-    read_vt(vt, slot + Ly::kBlockBytes, lane);
-    if (keymask != 0xffffffffu) zero_dead_keys(vt, keymask, lane);
-
-    bool edge = true;
-    const int kb = kbase + kBlockK * idx;
-    if (win) {
-      bool interior = keymask == 0xffffffffu && (tw0 + kWaveQ - 1 - kb <= w);
-      interior = interior && (causal ? (tw0 >= kb + kBlockK - 1) : (kb + kBlockK - 1 - tw0 <= w));
-      edge = !interior;
-    }
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      f32x16 sc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] = 0.f;
-      qk(sc, kf, qf[nb]);
-      PFrag<B16> pf;
-      softmax_half<B16>(st, nb, sc, pf, edge,
-                        [&]() -> uint32_t {
-                          uint32_t vb;
-                          if (win) {
-                            const int sh32 = kBlockK * idx;
-                            const int lo = max(A[nb] - sh32, 0);
-                            const int hi = min(B[nb] - sh32, 31);
-                            vb = lo > hi ? 0u : ((0xffffffffu >> (31 - hi)) & (0xffffffffu << lo));
-                          } else {
-                            // a global key g joins local row i unless g is already in W(i)
-                            vb = 0;
-                            const int* gl = sh.G + kBlockK * (s - S) + 4 * hh;
-#pragma unroll
-                            for (int e = 0; e < 16; ++e) {
-                              const int dd = qpos[nb] - gl[acc_c(e)];
-                              const bool in_w = (dd <= wd && dd >= -wd) && (dil == 1 || dd % dil == 0);
-                              vb |= in_w ? 0u : (1u << acc_c(e));
-                            }
-                          }
-                          return vb & (keymask >> (4 * hh));
-                        },
-                        c);
-      pv(st.o[nb], pf, vt);
-    }
-  }
-
-  // a wave without local rows still writes its zero (padding) rows
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    st.l[nb] += __shfl_xor(st.l[nb], 32);
-    st.cnt[nb] += __shfl_xor(st.cnt[nb], 32);
-  }
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    if (!is_local[nb] && !is_zero[nb]) continue;
-    T* orow = out + (size_t)qpos[nb] * rs;
-    const float inv = is_local[nb] ? 1.0f / st.l[nb] : 0.f;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float t[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) t[i] = st.o[nb][db][4 * g + i] * inv;
-        store4<B16>(orow + 32 * db + 8 * g + 4 * hh, t);
-      }
-    if (p.row_nnz && hh == 0) p.row_nnz[((size_t)b * p.H + h) * n + qpos[nb]] = is_local[nb] ? st.cnt[nb] : 0;
-  }
+  loop.run(st, qf, wv, end, p.c);
+  combine_waves<B16>(st, sh, [&](int nb, int db, float, float Lsum, int cnt, const float* o) {
+    const bool loc = nb ? is_local[1] : is_local[0];
+    const bool zer = nb ? is_zero[1] : is_zero[0];
+    if (!loc && !zer) return;
+    const int qp = nb ? src.qpos[1] : src.qpos[0];
+    store_quadrant<B16>(out + (size_t)qp * rs, db, hh, o, loc ? 1.0f / Lsum : 0.f, !loc);
+    if (p.row_nnz && db == 0 && hh == 0) p.row_nnz[((size_t)b * p.H + h) * n + qp] = loc ? cnt : 0;
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -989,30 +1163,33 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
   const int n = p.n;
   const int8_t* mrow = p.mask + (size_t)b * n;
 
+  const uint32_t rs = (uint32_t)p.H * kHeadDim;
+  const size_t head = (size_t)b * n * rs + (size_t)h * kHeadDim;
+  const T* qg = reinterpret_cast<const T*>(p.qg) + head;
+  ChunkSrc src;
+  src.mrow = mrow;
+  src.cbeg = cidx * kGlobalChunk;
+  src.cend = min(n, src.cbeg + kGlobalChunk);
+  src.lane = lane;
+  const int nblk = (src.cend - src.cbeg + kBlockK - 1) / kBlockK;
+  BlockPipe<B16, ChunkSrc> pipe(src, reinterpret_cast<const T*>(p.kg) + head,
+                                reinterpret_cast<const T*>(p.vg) + head, rs,
+                                sh.buf + wv * Lay<B16>::kWaveBytes);
+  bool primed = wv < nblk;
+  if (primed) pipe.issue(wv, 0);  // the split's keys do not depend on the scan
+
   int nG = scan_globals(mrow, n, sh.G, LF_MAX_GLOBAL, sh.wave_tmp);
   if (nG > p.max_global) {
     if (threadIdx.x == 0) atomicOr(p.status, LF_DEV_TOO_MANY_GLOBALS);
     nG = p.max_global;
   }
-  if (nG == 0) return;
-
-  const size_t rs = (size_t)p.H * kHeadDim;
-  const size_t head = (size_t)b * n * rs + (size_t)h * kHeadDim;
-  const T* qg = reinterpret_cast<const T*>(p.qg) + head;
-  const T* kg = reinterpret_cast<const T*>(p.kg) + head;
-  const T* vg = reinterpret_cast<const T*>(p.vg) + head;
-  const int cbeg = cidx * kGlobalChunk;
-  const int cend = min(n, cbeg + kGlobalChunk);
-  const int nblk = (cend - cbeg + kBlockK - 1) / kBlockK;
-  unsigned char* lds = sh.buf + wv * Lay<B16>::kWaveBytes;
+  nG = __builtin_amdgcn_readfirstlane(nG);  // uniform (the status write above diverges)
+  if (nG == 0) {
+    wait_vmem_all();
+    return;
+  }
   const float c = p.c;
   float* part_bh = p.partials + (size_t)bh * p.max_global * S * kPartialStride;
-
-  ChunkSrc src;
-  src.mrow = mrow;
-  src.cbeg = cbeg;
-  src.cend = cend;
-  src.lane = lane;
 
   for (int g0 = 0; g0 < nG; g0 += kWaveQ) {
     Frag<B16> qf[2];
@@ -1024,57 +1201,67 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
     }
     WaveState st;
     state_init(st);
-    run_blocks<B16>(st, qf, src, kg, vg, rs, wv, nblk, lds, c);
-    merge_waves(st, sh);
-    if (wv == 0) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int gi = g0 + 32 * nb + (lane & 31);
-        if (gi >= nG) continue;
-        float* rec = part_bh + ((size_t)gi * S + cidx) * kPartialStride;
-        if (hh == 0) {
-          rec[0] = st.m[nb];
-          rec[1] = st.l[nb];
-          rec[2] = __builtin_bit_cast(float, st.cnt[nb]);
-        }
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            *reinterpret_cast<f32x4*>(rec + 4 + 32 * db + 8 * g + 4 * hh) =
-                f32x4{st.o[nb][db][4 * g], st.o[nb][db][4 * g + 1], st.o[nb][db][4 * g + 2],
-                      st.o[nb][db][4 * g + 3]};
+    pipe.run(st, qf, wv, nblk, c, nG - g0 > 32 ? 2 : 1, primed);
+    primed = false;
+    combine_waves<B16>(st, sh, [&](int nb, int db, float M, float Lsum, int cnt, const float* o) {
+      const int gi = g0 + 32 * nb + (lane & 31);
+      if (gi >= nG) return;
+      float* rec = part_bh + ((size_t)gi * S + cidx) * kPartialStride;
+      if (db == 0 && hh == 0) {
+        st_agent(rec, M);
+        st_agent(rec + 1, Lsum);
+        st_agent(rec + 2, __builtin_bit_cast(float, cnt));
       }
-    }
-    __syncthreads();  // merge buffers are reused by the next group of globals
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st_agent(rec + 4 + 32 * db + 8 * g + 4 * hh + e, o[4 * g + e]);
+    });
+    __syncthreads();  // LDS areas and merge arrays are reused by the next group of globals
   }
 
-  // Arrival: the last split of (b, h) merges all partials.
-  __threadfence();
+  // Arrival: the last split of (b, h) merges all partials.  Every thread's
+  // record stores have completed (at the coherence point) before the
+  // barrier that precedes the ticket increment.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  wait_vmem_all();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int t = __hip_atomic_fetch_add(p.tickets + bh, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const int t = __hip_atomic_fetch_add(p.tickets + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sh.flag = (t == S - 1);
   }
   __syncthreads();
   if (!sh.flag) return;
-  __threadfence();
 
   T* out = reinterpret_cast<T*>(p.out) + head;
   const int d = threadIdx.x & 63;
   for (int gi = wv; gi < nG; gi += kWaves) {
+    // online log-sum-exp merge of the S partials; loads issued 8 at a time
     const float* recs = part_bh + (size_t)gi * S * kPartialStride;
-    float M = kNegInf;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, __builtin_nontemporal_load(recs + s * kPartialStride));
-    float Lsum = 0.f, acc = 0.f;
+    float M = kNegInf, Lsum = 0.f, acc = 0.f;
     int cnt = 0;
-    for (int s = 0; s < S; ++s) {
-      const float* rec = recs + s * kPartialStride;
-      const float ms = __builtin_nontemporal_load(rec);
-      const float f = (ms == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-      Lsum += __builtin_nontemporal_load(rec + 1) * f;
-      acc += __builtin_nontemporal_load(rec + 4 + d) * f;
-      cnt += __builtin_bit_cast(int, __builtin_nontemporal_load(rec + 2));
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      float ms[8], ls[8], os[8];
+      int cs[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float* rec = recs + (size_t)min(s0 + j, S - 1) * kPartialStride;
+        ms[j] = ld_agent(rec);
+        ls[j] = ld_agent(rec + 1);
+        cs[j] = __builtin_bit_cast(int, ld_agent(rec + 2));
+        os[j] = ld_agent(rec + 4 + d);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (s0 + j >= S) break;
+        const float mn = fmaxf(M, ms[j]);
+        const float fa = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M - mn);
+        const float fb = (ms[j] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ms[j] - mn);
+        M = mn;
+        Lsum = Lsum * fa + ls[j] * fb;
+        acc = acc * fa + os[j] * fb;
+        cnt += cs[j];
+      }
     }
     const int pos = sh.G[gi];
     out[(size_t)pos * rs + d] = (T)(acc / Lsum);
@@ -1088,14 +1275,14 @@ template <bool B16>
 __device__ __forceinline__ void fwd_body(const KernelParams& p) {
   __shared__ Shared<B16> sh;
   const int bid = blockIdx.x;
-  if (bid < p.n_glob_pad) {
-    if (bid < p.n_glob) global_split<B16>(p, bid, sh);
+  if (bid < p.n_glob) {
+    global_split<B16>(p, bid, sh);  // first: their merge waits for the last split
     return;
   }
-  band_tile<B16>(p, xcd_remap(bid - p.n_glob_pad, p.n_band), sh);
+  band_tile<B16>(p, xcd_remap(bid - p.n_glob, p.n_band), sh);
 }
 
-// bf16: two waves per SIMD, so one wave's softmax overlaps the other's MFMAs.
+// bf16: two waves per SIMD (two workgroups per CU).
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void lf_attn_fwd_bf16(
     const KernelParams p) {
   fwd_body<true>(p);
@@ -1107,7 +1294,7 @@ __global__ __launch_bounds__(kThreads) void lf_attn_fwd_f32(const KernelParams p
 }  // namespace
 
 int launch_forward(const KernelParams& kp, int dtype, void* stream) {
-  const int grid = kp.n_glob_pad + kp.n_band;
+  const int grid = kp.n_band + kp.n_glob;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == LF_BF16)
     hipLaunchKernelGGL(lf_attn_fwd_bf16, dim3(grid), dim3(kThreads), 0, s, kp);
