@@ -57,7 +57,7 @@ extern "C" {
 typedef enum {
   LF_OK = 0,
   LF_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, bad window/dilation/scale, aliasing */
-  LF_ERR_UNSUPPORTED = 2, /* D != 64, unknown dtype, H or max_global above the limits */
+  LF_ERR_UNSUPPORTED = 2, /* D != 64, unknown dtype, a size above the limits below */
   LF_ERR_WORKSPACE = 3,   /* workspace missing or smaller than lf_attn_workspace_bytes */
   LF_ERR_HIP = 4          /* the HIP runtime refused the launch */
 } lf_status;
@@ -69,6 +69,7 @@ typedef enum { LF_F32 = 0, LF_BF16 = 1 } lf_dtype;
 #define LF_MAX_HEADS 64
 #define LF_MAX_GLOBAL 1024   /* global tokens per batch row */
 #define LF_MAX_SEQ (1 << 24)
+#define LF_MAX_ROW_BYTES 0x7fffffff /* n * H * D * element size of one batch row */
 
 /* Bits of the device status word (lf_attn_device_status). */
 #define LF_DEV_TOO_MANY_GLOBALS 1 /* a batch row held more than max_global tokens with mask 2 */

@@ -34,6 +34,11 @@ pattern, so the definition is the oracle):
   keys everywhere and their own output row is exactly zero.
 * Scale: 1/sqrt(D) unless given (the pages are silent).
 
+Parity unpinned (no page fixes them; conventions this oracle and the HIP
+path both follow): the projections that score a local row's global columns
+(Q_s K_s and V_s), the exactly-zero output row of a mask-0 token, and mask
+2 under a causal window (rejected here).
+
 ``forward`` gathers each row's key set (window keys by arithmetic plus the
 global columns outside the window) and runs a softmax per row in fp64.
 ``dense_bruteforce`` builds the full n x n boolean pattern the way the

@@ -30,6 +30,20 @@ __all__ = [
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblf_attn.so")
+KERNEL_SOURCES = ("csrc/lf_attn_kernels.hip", "csrc/lf_attn_internal.h")
+
+
+def kernel_source_hash() -> str:
+    """Short digest of the device-code sources; counter measurements are
+    tagged with it so that a later kernel change invalidates them."""
+    import hashlib
+
+    h = hashlib.sha256()
+    base = os.path.dirname(os.path.abspath(__file__))
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(base, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 LF_OK, LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED, LF_ERR_WORKSPACE, LF_ERR_HIP = range(5)
 LF_F32, LF_BF16 = 0, 1

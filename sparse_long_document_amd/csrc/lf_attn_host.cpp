@@ -44,6 +44,8 @@ lf_status make_plan(const lf_attn_params* p, Plan& pl) {
 
   pl.elem = p->dtype == LF_BF16 ? 2 : 4;
   pl.tensor_bytes = (size_t)tokens * p->H * p->D * pl.elem;
+  // The kernels address one batch row of a tensor with 32-bit byte offsets.
+  if ((int64_t)p->n * p->H * p->D * pl.elem > (int64_t)LF_MAX_ROW_BYTES) return LF_ERR_UNSUPPORTED;
 
   int64_t tiles = 0;
   for (int h = 0; h < p->H; ++h) {

@@ -1,48 +1,44 @@
 // Longformer combined sliding-window + global attention forward for gfx950.
 //
-// One launch computes every output row:
-//   * band workgroups own a tile of kTileQ consecutive query rows of one
-//     (batch row b, head h, residue class r of the head's dilation d).  A
-//     dilated window over positions {r, r+d, r+2d, ...} is a plain window
-//     over that subsequence, so each residue class is handled as an
-//     undilated sequence whose neighbours are d tokens apart (segmentfault
-//     Longformer summary, "Dilated sliding window": the dilated window
-//     keeps the cost of the plain one).  They write local rows (mask 1)
-//     and zero rows (mask 0);
-//   * global-row workgroups own one split of kGlobalChunk keys of one
-//     (b, h) for every global token of b: each global token attends to all
-//     tokens with the global projections (segmentfault summary, "Global
+// One launch computes every output row with two kinds of workgroups:
+//   * global-row splits (dispatched first): split c of one (batch row b,
+//     head h) scores every global token of b against keys
+//     [512c, 512c + 512) with the global projections (each global token
+//     attends to every token: segmentfault Longformer summary, "Global
 //     attention" and "Linear projections for global attention").  Each
-//     split leaves a partial (max, sum, unnormalised output) in the
-//     workspace; the last split to arrive merges them and writes the rows.
+//     split leaves a partial (max, sum, unnormalised output) record in the
+//     workspace; the last split of (b, h) to arrive merges them and writes
+//     the global rows;
+//   * band tiles: 64 consecutive query rows of one (b, h, residue class r
+//     of the head's dilation d).  A dilated window over positions
+//     {r, r+d, r+2d, ...} is a plain window over that subsequence, so each
+//     residue class is an undilated sequence whose neighbours are d tokens
+//     apart (segmentfault summary, "Dilated sliding window").  The tile's
+//     keys are its window span (64 + 2w keys, or 64 + w when causal) plus
+//     the row's global tokens as extra columns, masked so that a global key
+//     already inside a row's window is not counted twice (ultralytics
+//     glossary worked example: window and global row/column are OR-ed into
+//     one pattern).  They write local rows (mask 1) and zero rows (mask 0).
 //
-// Inner block (both kinds): 32 keys x 64 queries per wave.
-//   S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 key rows straight
-//   from global memory into registers, B = 32 query columns, K-dim = head
-//   dim).  In the 32x32 accumulator a lane owns one column (a query) and 16
-//   of its 32 keys; the other 16 sit in lane ^ 32, so the softmax row max
-//   is in-lane plus one lane exchange.  The accumulator, rounded to
-//   bf16, is directly the B operand of O^T = V^T P^T.  V rows travel from
-//   global memory to LDS with direct-to-LDS loads (no registers, no VALU)
-//   and come back as the V^T A operand through ds_read_b64_tr_b16, whose
-//   16-lane transpose hands each lane 4 keys of one head dim.  Softmax is
-//   online in base 2 (scale*log2e folded into one FMA), fp32, with a lazy
-//   rescale: the running reference max only moves when a block max exceeds
-//   it by more than 2^8, which leaves the result exact while skipping most
-//   accumulator rescales.
-//   Each wave fetches its next block (K into registers, V into the other
-//   half of its LDS double buffer) while it computes the current one.
+// Inner block: 32 keys x 64 queries per wave, as two 32-query halves.
+//   S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 key rows, B = 32
+//   query columns, K-dim = head dim), so a lane owns one query column and
+//   16 of its 32 keys (the other 16 sit in lane ^ 32).  K and V rows travel
+//   from HBM to LDS by direct-to-LDS buffer loads (no registers, no VALU),
+//   K comes back as the A fragment and V as the V^T A operand of
+//   O^T = V^T P^T through ds_read_b64_tr_b16; the accumulator rounded to
+//   bf16 is directly the P^T operand.  Softmax is online in base 2 (score
+//   scale * log2e folded into one FMA), fp32, with a lazy rescale: the
+//   reference max only moves when a block max exceeds it by more than 2^8,
+//   which keeps the result exact while skipping most accumulator rescales.
 //
-// The key range of a band tile (kTileQ + 2w keys) is split over the 4 waves
-// of the workgroup block by block; their partial results are merged
-// through LDS at the end.  Global columns of local rows (the symmetric half
-// of global attention) are extra gathered key blocks, masked so that a
-// global key already inside the row's window is not counted twice
-// (ultralytics glossary worked example: the window and the global
-// row/column are OR-ed into one boolean pattern).
+// A band tile's key blocks are dealt to its 4 waves round-robin; each wave
+// streams its blocks through its own two-stage LDS area (the next block's
+// loads fly while the current one is computed) and the four partial
+// states are merged through LDS with one barrier.
 //
 // The fp32 instantiation computes in true fp32 (v_mfma_f32_32x32x2_f32, P
-// kept in fp32) with V staged through registers.
+// kept in fp32).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

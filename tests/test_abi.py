@@ -94,6 +94,7 @@ def test_workspace_bytes_layout():
     (dict(H=65, dilation=None), lf.LF_ERR_UNSUPPORTED),
     (dict(max_global=2000), lf.LF_ERR_UNSUPPORTED),
     (dict(n=(1 << 24) + 1), lf.LF_ERR_UNSUPPORTED),
+    (dict(n=1 << 20, H=16, dilation=None), lf.LF_ERR_UNSUPPORTED),  # one batch row of q is 2 GiB
 ])
 def test_invalid_params_rejected_before_hip(kw, code):
     p, _k = _params(**kw)
