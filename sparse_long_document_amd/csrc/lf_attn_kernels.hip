@@ -597,14 +597,14 @@ struct Shared {
   __attribute__((aligned(16))) unsigned char buf[kWaves * Lay<B16>::kWaveBytes];
 };
 
-// The four waves of a workgroup hold partial results for the same 64 query
+// The waves of a workgroup hold partial results for the same 64 query
 // columns over disjoint key subsets.  Each wave parks its state in its own
 // LDS area (all its loads have landed, and no other wave touches that
-// area); after one barrier, wave w merges quadrant (query half w/2, head-dim
-// half w%2) of the four partials and passes, per lane, the merged max M
-// (log2 domain), row sum L, key count and the 16 unnormalised outputs of
-// head dims 32db + 8g + 4(lane/32) + i (in o[4g + i]) to
-// emit(nb, db, M, L, cnt, o).
+// area); after one barrier, each wave merges its share of the quadrants
+// (query half nb, head-dim half db) of all partials and passes, per lane,
+// the merged max M (log2 domain), row sum L, key count and the 16
+// unnormalised outputs of head dims 32db + 8g + 4(lane/32) + i (in
+// o[4g + i]) to emit(nb, db, M, L, cnt, o).
 template <bool B16, class Emit>
 __device__ void combine_waves(const WaveState& st, Shared<B16>& sh, Emit emit) {
   static_assert(Lay<B16>::kWaveBytes >= 64 * 64 * 4, "a wave's area holds its 64 x 64 fp32 partial");
@@ -629,33 +629,39 @@ __device__ void combine_waves(const WaveState& st, Shared<B16>& sh, Emit emit) {
     }
   }
   __syncthreads();
-  const int nb = wv >> 1, db = wv & 1;
-  const int q = 32 * nb + (lane & 31);
-  float mw[kWaves];
-  float M = kNegInf;
+  // wave w takes quadrants w * kQuads .. (w + 1) * kQuads - 1 (index 2 nb + db)
+  constexpr int kQuads = 4 / kWaves;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    mw[w] = sh.m[w][q];
-    M = fmaxf(M, mw[w]);
-  }
-  float Lsum = 0.f, o[16];
-  int cnt = 0;
+  for (int k = 0; k < kQuads; ++k) {
+    const int quad = wv * kQuads + k;
+    const int nb = quad >> 1, db = quad & 1;
+    const int q = 32 * nb + (lane & 31);
+    float mw[kWaves];
+    float M = kNegInf;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) o[i] = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const float f = __builtin_amdgcn_exp2f(mw[w] - M);
-    Lsum = __builtin_fmaf(sh.l[w][q], f, Lsum);
-    cnt += sh.cnt[w][q];
-    const f32x4* part = reinterpret_cast<const f32x4*>(sh.buf + w * Lay<B16>::kWaveBytes);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 t = part[((nb * 2 + db) * 4 + g) * 64 + lane];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[4 * g + i] = __builtin_fmaf(t[i], f, o[4 * g + i]);
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = sh.m[w][q];
+      M = fmaxf(M, mw[w]);
     }
+    float Lsum = 0.f, o[16];
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[i] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = __builtin_amdgcn_exp2f(mw[w] - M);
+      Lsum = __builtin_fmaf(sh.l[w][q], f, Lsum);
+      cnt += sh.cnt[w][q];
+      const f32x4* part = reinterpret_cast<const f32x4*>(sh.buf + w * Lay<B16>::kWaveBytes);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 t = part[((nb * 2 + db) * 4 + g) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[4 * g + i] = __builtin_fmaf(t[i], f, o[4 * g + i]);
+      }
+    }
+    emit(nb, db, M, Lsum, cnt, o);
   }
-  emit(nb, db, M, Lsum, cnt, o);
 }
 
 
@@ -1120,11 +1126,16 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
   // every wave holds the same queries, so this test agrees across the workgroup
   if (!__any(any_local)) {
     wait_vmem_all();  // the primed loads land before the workgroup's LDS is released
-    const int nb = wv >> 1, db = wv & 1;
-    if (nb ? is_zero[1] : is_zero[0]) {
-      const int qp = nb ? src.qpos[1] : src.qpos[0];
-      store_quadrant<B16>(out + (size_t)qp * rs, db, hh, nullptr, 0.f, true);
-      if (p.row_nnz && db == 0 && hh == 0) p.row_nnz[((size_t)b * p.H + h) * n + qp] = 0;
+    constexpr int kQuads = 4 / kWaves;
+#pragma unroll
+    for (int k = 0; k < kQuads; ++k) {
+      const int quad = wv * kQuads + k;
+      const int nb = quad >> 1, db = quad & 1;
+      if (nb ? is_zero[1] : is_zero[0]) {
+        const int qp = nb ? src.qpos[1] : src.qpos[0];
+        store_quadrant<B16>(out + (size_t)qp * rs, db, hh, nullptr, 0.f, true);
+        if (p.row_nnz && db == 0 && hh == 0) p.row_nnz[((size_t)b * p.H + h) * n + qp] = 0;
+      }
     }
     return;
   }
