@@ -124,6 +124,17 @@ __device__ __forceinline__ void wave_sync() {
 // (direct-to-LDS loads included); other counters are left alone.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until at most N vector-memory instructions of this wave are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Wait until every LDS (and scalar-memory) access of this wave has completed.
+__device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 __device__ __forceinline__ void load_frag(Frag<true>& f, const __bf16* row, int hh) {
   const bf16x8* p = reinterpret_cast<const bf16x8*>(row);
 #pragma unroll
@@ -263,6 +274,46 @@ __device__ __forceinline__ void read_vt(VtFrag<true>& vt, const unsigned char* v
   }
 }
 
+// The same reads in one asm block that waits for them before it ends.  The
+// band loop uses it while the next block's direct-to-LDS loads (into the
+// other stage) are in flight: the compiler cannot tell the transposed reads
+// from those writes and would otherwise wait for every outstanding load
+// first.  The caller has already waited for this stage's loads.
+__device__ __forceinline__ void read_vt_now(VtFrag<true>& vt, const unsigned char* vbuf, int lane) {
+  const int g = lane >> 4;
+  const int row0 = 4 * (g >> 1) + ((lane & 15) >> 2);
+  const int byte0 = 32 * (g & 1) + 8 * (lane & 3);
+  const int sw = vswz<true>(row0);
+  const uint32_t base = (uint32_t)(uintptr_t)(LDS_AS const void*)vbuf;
+  uint32_t a[2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    const int byte = 64 * db + byte0;
+    a[db] = base + (uint32_t)(row0 * 128 + (((byte >> 4) ^ sw) << 4) + (byte & 15));
+  }
+  u32x2 r[8];  // [db][ks][lo, hi]: key rows 16ks + 8half at +2048ks + 1024half
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n"
+      "ds_read_b64_tr_b16 %1, %8 offset:1024\n"
+      "ds_read_b64_tr_b16 %2, %8 offset:2048\n"
+      "ds_read_b64_tr_b16 %3, %8 offset:3072\n"
+      "ds_read_b64_tr_b16 %4, %9\n"
+      "ds_read_b64_tr_b16 %5, %9 offset:1024\n"
+      "ds_read_b64_tr_b16 %6, %9 offset:2048\n"
+      "ds_read_b64_tr_b16 %7, %9 offset:3072\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1])
+      : "memory");
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x2 lo = r[4 * db + 2 * ks], hi = r[4 * db + 2 * ks + 1];
+      vt.a[db][ks] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
+}
+
 __device__ __forceinline__ void read_vt(VtFrag<false>& vt, const unsigned char* vbuf, int lane) {
   const float* vs = reinterpret_cast<const float*>(vbuf);
   const int hh = lane >> 5;
@@ -270,6 +321,10 @@ __device__ __forceinline__ void read_vt(VtFrag<false>& vt, const unsigned char* 
   for (int db = 0; db < 2; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) vt.a[db][r] = vs[(acc_c(r) + 4 * hh) * kHeadDim + 32 * db + (lane & 31)];
+}
+
+__device__ __forceinline__ void read_vt_now(VtFrag<false>& vt, const unsigned char* vbuf, int lane) {
+  read_vt(vt, vbuf, lane);
 }
 
 // Zero the V^T operand entries of keys whose bit is clear in keymask, so
@@ -594,6 +649,7 @@ struct Shared {
   float m[kWaves][kWaveQ];
   float l[kWaves][kWaveQ];
   int cnt[kWaves][kWaveQ];
+  uint32_t ktab[kWaves][32];  // band tiles: validity bits of each wave's window blocks
   __attribute__((aligned(16))) unsigned char buf[kWaves * Lay<B16>::kWaveBytes];
 };
 
@@ -764,15 +820,14 @@ struct BandSrc {
     const int gi = kBlockK * (i - nwin) + row;
     return G[gi < nG ? gi : nG - 1];
   }
-  __device__ void locate(int i, int& mb, bool& inr) const {
-    const int row = lane & 31;
+  // whether key row `row` of block i exists (a window key in [0, n_r) or
+  // one of the nG global keys)
+  __device__ bool exists(int i, int row) const {
     if (i < nwin) {
       const int kk = key(i, row);
-      inr = kk >= 0 && kk < n_r;
-    } else {
-      inr = kBlockK * (i - nwin) + row < nG;
+      return kk >= 0 && kk < n_r;
     }
-    mb = mrow[kpos(i, row)];
+    return kBlockK * (i - nwin) + row < nG;
   }
   __device__ int dstep() const { return dil; }
   __device__ bool affine(int i, int& p0) const {
@@ -827,45 +882,37 @@ __device__ __forceinline__ float max16(const f32x16& s) {
   return fmaxf(fmaxf(fmaxf(a, b), d), fmaxf(fmaxf(e, f), s[15]));
 }
 
-// Both query halves of a block, after masking (masked scores are -inf):
+// One query half of a block, after masking (masked scores are -inf):
 // online softmax (same arithmetic as softmax_half); counts 16 scored keys
-// per lane and half.
+// per lane.
 template <bool B16>
-__device__ __forceinline__ void softmax_full2(WaveState& st, f32x16 (&s)[2], PFrag<B16> (&pf)[2], float c) {
-  float ml[2];
+__device__ __forceinline__ void softmax_core(WaveState& st, int nb, f32x16& s, PFrag<B16>& pf, float c) {
+  const float ml = max16(s) * c;
+  if (__any(ml > st.m[nb] + kRescaleSlack)) {
+    const float mn = fmaxf(st.m[nb], fmaxf(ml, __shfl_xor(ml, 32)));
+    const float alpha = __builtin_amdgcn_exp2f(st.m[nb] - mn);
+    st.m[nb] = mn;
+    st.l[nb] *= alpha;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) ml[nb] = max16(s[nb]) * c;
-  if (__any((ml[0] > st.m[0] + kRescaleSlack) | (ml[1] > st.m[1] + kRescaleSlack))) {
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const float mn = fmaxf(st.m[nb], fmaxf(ml[nb], __shfl_xor(ml[nb], 32)));
-      const float alpha = __builtin_amdgcn_exp2f(st.m[nb] - mn);
-      st.m[nb] = mn;
-      st.l[nb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st.o[nb][db][r] *= alpha;
-    }
+      for (int r = 0; r < 16; ++r) st.o[nb][db][r] *= alpha;
   }
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -st.m[nb]));
+  float t8[8];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[nb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][r], c, -st.m[nb]));
-    float t8[8];
+  for (int i = 0; i < 8; ++i) t8[i] = s[2 * i] + s[2 * i + 1];
+  st.l[nb] += ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
+  st.cnt[nb] += 16;
+  if constexpr (B16) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) t8[i] = s[nb][2 * i] + s[nb][2 * i + 1];
-    st.l[nb] += ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
-    st.cnt[nb] += 16;
-    if constexpr (B16) {
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int e = 0; e < 8; ++e) pf.x[ks][e] = (__bf16)s[8 * ks + e];
+  } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf[nb].x[ks][e] = (__bf16)s[nb][8 * ks + e];
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pf[nb].x[r] = s[nb][r];
-    }
+    for (int r = 0; r < 16; ++r) pf.x[r] = s[r];
   }
 }
 
@@ -887,46 +934,95 @@ struct BandLoop {
   int lane;
   int t0, w, w_hi;
   // buffer resources and per-lane offsets of the evenly spaced (affine) fast path
-  __amdgpu_buffer_rsrc_t rk, rv, rm;
-  uint32_t vk0, vk1, vv, vm;
-  int mb;    // mask byte of key row lane%32 of the last issued block
-  bool inr;  // whether that row exists
+  __amdgpu_buffer_rsrc_t rk, rv;
+  uint32_t vk0, vk1, vv;
+  // key-validity bits of this wave's window blocks (entry k: block
+  // first + kWaves k), filled in the prologue; null when the window has
+  // more blocks than the table holds
+  const uint32_t* ktab;
+  // vector-memory instructions one issue() emits (K and V rows)
+  static constexpr int kIssueLoads = 2 * L::kLoads;
 
   __device__ BandLoop(const BandSrc& s, const T* k, const T* v, uint32_t rs_, unsigned char* area, int n, int t0_,
                       int w_, int w_hi_)
-      : src(s), kb(k), vb(v), rs(rs_), lds(area), lane(lane_id()), t0(t0_), w(w_), w_hi(w_hi_), mb(0),
-        inr(false) {
+      : src(s), kb(k), vb(v), rs(rs_), lds(area), lane(lane_id()), t0(t0_), w(w_), w_hi(w_hi_), ktab(nullptr) {
     const uint32_t bytes = (uint32_t)(((size_t)(n - 1) * rs + kHeadDim) * sizeof(T));
     rk = make_rsrc(k, bytes);
     rv = make_rsrc(v, bytes);
-    rm = make_rsrc(src.mrow, (uint32_t)n);
     const uint32_t row_off = (uint32_t)src.dil * (uint32_t)(lane >> 3) * rs;
     const int ck = (lane & 7) ^ (lane >> 4);  // kswz of rows 8t + lane/8, t even
     const int cv = (lane & 7) ^ (((lane >> 4) & 1) << 2);
     vk0 = 2u * (row_off + 8u * (uint32_t)ck);
     vk1 = 2u * (row_off + 8u * (uint32_t)(ck ^ 4));
     vv = 2u * (row_off + 8u * (uint32_t)cv);
-    vm = (uint32_t)src.dil * (uint32_t)(lane & 31);
   }
 
-  __device__ void issue(int i, unsigned char* dst) {
+  // Loads of block i into stage st (exactly kIssueLoads vector-memory
+  // instructions on every path, and nothing else: the loop's waits count
+  // them).
+  __device__ void issue(int i, int st) {
+    unsigned char* dst = lds + st * L::kStageBytes;
     int p0;
     if (B16 && src.affine(i, p0)) {
+      // scalar offsets: wave-uniform by construction; readfirstlane keeps
+      // them in SGPRs even where register pressure moved a term to a VGPR
       const uint32_t so = (uint32_t)p0 * rs * 2u;
       const uint32_t step = (uint32_t)src.dil * (uint32_t)L::kRowsPerLoad * rs * 2u;
-      mb = (int)(signed char)__builtin_amdgcn_raw_buffer_load_b8(rm, vm, (uint32_t)p0, 0);
-      inr = true;
 #pragma unroll
       for (int t = 0; t < L::kLoads; ++t) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)(dst + 1024 * t), 16, (t & 1) ? vk1 : vk0,
-                                                 so + t * step, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS_AS void*)(dst + L::kBlockBytes + 1024 * t), 16, vv,
-                                                 so + t * step, 0, 0);
+        const uint32_t sot = __builtin_amdgcn_readfirstlane(so + t * step);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)(dst + 1024 * t), 16, (t & 1) ? vk1 : vk0, sot,
+                                                 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS_AS void*)(dst + L::kBlockBytes + 1024 * t), 16, vv, sot,
+                                                 0, 0);
       }
     } else {
-      src.locate(i, mb, inr);
-      issue_block<B16>(kb, vb, rs, [&](int row) { return src.kpos(i, row); }, dst, lane);
+      issue_block<B16>(kb, vb, rs, [&](int r) { return src.kpos(i, r); }, dst, lane);
     }
+  }
+
+  // Validity bits of window block i read from the mask now (rows in
+  // [0, n_r) with mask 1 or 2).
+  __device__ uint32_t window_keymask(int i) const {
+    const int row = lane & 31;
+    const int m = src.exists(i, row) ? (int)src.mrow[src.kpos(i, row)] : 0;
+    return (uint32_t)__ballot(m == 1 || m == 2);
+  }
+
+  // This wave's table of window-block validity bits (blocks first,
+  // first + kWaves, ... < nwin): tab_load issues the mask-byte loads (two
+  // blocks per load, lanes 32-63 take the second) and tab_commit, after the
+  // caller has issued its first K/V loads, turns them into bits.  Windows
+  // with more than 2 kTabPairs blocks per wave go without the table.
+  static constexpr int kTabPairs = 12;
+  int tabv[kTabPairs];
+  int tab_cnt = 0;
+  int first_ = 0;
+  __device__ void tab_load(int first) {
+    first_ = first;
+    tab_cnt = first < src.nwin ? (src.nwin - first + kWaves - 1) / kWaves : 0;
+    if (tab_cnt > 2 * kTabPairs) return;
+    const int row = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int p = 0; p < kTabPairs; ++p) {
+      const int k = 2 * p + half;
+      const int i = first + kWaves * k;
+      const bool ok = k < tab_cnt && src.exists(i, row);
+      tabv[p] = ok ? (int)src.mrow[src.kpos(i, row)] : 0;
+    }
+  }
+  __device__ void tab_commit(uint32_t* tab) {
+    if (tab_cnt > 2 * kTabPairs) return;  // ktab stays null
+#pragma unroll
+    for (int p = 0; p < kTabPairs; ++p) {
+      if (2 * p >= tab_cnt) break;
+      const unsigned long long bits = __ballot(tabv[p] == 1 || tabv[p] == 2);
+      if (lane == 0) {
+        tab[2 * p] = (uint32_t)bits;
+        tab[2 * p + 1] = (uint32_t)(bits >> 32);
+      }
+    }
+    ktab = tab;
   }
 
   // 0 = empty, 1 = partial, 2 = full for query half nb of window block i.
@@ -943,14 +1039,30 @@ struct BandLoop {
   __device__ __forceinline__ void step(WaveState& st, const Frag<B16> (&qf)[2], int i, int end, float c) {
     const int hh = lane >> 5;
     const unsigned char* cst = lds + kStage * L::kStageBytes;
-    const bool kval = inr && (mb == 1 || mb == 2);
-    const uint32_t keymask = (uint32_t)__ballot(kval);
-    wait_vmem_all();  // this block's rows have landed
+    // Block i landed in this stage; block i + kWaves (other stage) may still
+    // be in flight: wait for all but its loads.
+    uint32_t keymask;
+    if (i >= src.nwin) {
+      // global-column rows: key rows up to nG exist and are global (mask 2)
+      const int left = src.nG - kBlockK * (i - src.nwin);
+      keymask = left >= kBlockK ? 0xffffffffu : ((1u << left) - 1u);
+    } else if (ktab) {
+      keymask = ktab[(i - first_) / kWaves];
+    } else {
+      keymask = window_keymask(i);  // waits for every outstanding load: wide windows only
+    }
+    if (i + kWaves < end)
+      wait_vmem_but<kIssueLoads>();
+    else
+      wait_vmem_all();
     Frag<B16> kf;
     read_kfrag(kf, cst, lane);
     VtFrag<B16> vt;
-    read_vt(vt, cst + L::kBlockBytes, lane);
-    if (i + kWaves < end) issue(i + kWaves, lds + (kStage ^ 1) * L::kStageBytes);
+    read_vt_now(vt, cst + L::kBlockBytes, lane);
+    if (i + 2 * kWaves < end) {
+      wait_lds_all();  // the fragment reads of this stage are done before it is refilled
+      issue(i + 2 * kWaves, kStage);
+    }
     if (keymask == 0u) return;  // no key of the block is in any key set
     if (keymask != 0xffffffffu) zero_dead_keys(vt, keymask, lane);
 
@@ -982,13 +1094,18 @@ struct BandLoop {
         st.cnt[nb] += __popc(vmk & 0x0f0f0f0fu) - 16;  // the softmax below adds 16
       }
     }
-    PFrag<B16> pf[2];
-    softmax_full2<B16>(st, s, pf, c);
+    // half 0's softmax runs while half 1's QK products are in flight, and
+    // half 0's PV products while half 1's softmax runs
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) pv(st.o[nb], pf[nb], vt);
+    for (int nb = 0; nb < 2; ++nb) {
+      PFrag<B16> pf;
+      softmax_core<B16>(st, nb, s[nb], pf, c);
+      pv(st.o[nb], pf, vt);
+    }
   }
 
-  // first: the wave's first block, already issued into stage 0.
+  // first: the wave's first block; blocks first and first + kWaves must
+  // already be issued into stages 0 and 1 (those that exist).
   __device__ void run(WaveState& st, const Frag<B16> (&qf)[2], int first, int end, float c) {
     for (int i = first; i < end; i += 2 * kWaves) {
       step<0>(st, qf, i, end, c);
@@ -1090,8 +1207,12 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
   unsigned char* area = sh.buf + wv * Ly::kWaveBytes;
   BandLoop<B16> loop(src, reinterpret_cast<const T*>(p.k) + head, reinterpret_cast<const T*>(p.v) + head, rs, area, n,
                      t0, w, w_hi);
-  const bool primed = wv < src.nwin;
-  if (primed) loop.issue(wv, area);  // the wave's first window block flies during the scan
+  // validity bytes of the wave's window blocks, then its first two window
+  // blocks: all of them fly during the scan
+  loop.tab_load(wv);
+  if (wv < src.nwin) loop.issue(wv, 0);
+  if (wv + kWaves < src.nwin) loop.issue(wv + kWaves, 1);
+  loop.tab_commit(sh.ktab[wv]);
 
   if (p.use_globals) {
     int nG = scan_globals(mrow, n, sh.G, LF_MAX_GLOBAL, sh.wave_tmp);
@@ -1102,7 +1223,9 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
     src.nG = __builtin_amdgcn_readfirstlane(nG);  // uniform (the status write above diverges)
   }
   const int end = src.nwin + (src.nG + kBlockK - 1) / kBlockK;
-  if (!primed && wv < end) loop.issue(wv, area);  // the wave starts on a global-column block
+  // first blocks that are global-column blocks go after the scan
+  if (wv >= src.nwin && wv < end) loop.issue(wv, 0);
+  if (wv + kWaves >= src.nwin && wv + kWaves < end) loop.issue(wv + kWaves, 1);
 
   bool is_local[2], is_zero[2];
   bool any_local = false;
