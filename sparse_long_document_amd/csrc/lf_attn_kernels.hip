@@ -114,6 +114,15 @@ struct Frag<false> {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// The lane index computed where it is used: values derived from it in a
+// rarely taken branch are then recomputed there instead of being hoisted
+// out of the loop and kept live (or spilled) through every iteration.
+__device__ __forceinline__ int lane_id_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -355,6 +364,38 @@ __device__ __forceinline__ void zero_dead_keys(VtFrag<false>& vt, uint32_t keyma
       vt.a[0][r] = 0.f;
       vt.a[1][r] = 0.f;
     }
+}
+
+// -1 where bit `pos` of x is set, else 0 (one v_bfe_i32; written out so
+// the compiler keeps it instead of a compare-and-select chain through VCC).
+template <int pos>
+__device__ __forceinline__ int bit_as_mask(uint32_t x) {
+  int r;
+  asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(r) : "v"(x), "i"(pos));
+  return r;
+}
+
+// 1 where u > span, else 0: med3(u, span, span + 1) - span (span < 2^32 - 1).
+__device__ __forceinline__ uint32_t above_span(uint32_t u, uint32_t span) {
+  uint32_t m;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(m) : "v"(u), "s"(span), "v"(span + 1u));  // one scalar operand per VALU op
+  return m - span;
+}
+
+// Zero this lane's K fragment when its key row (lane % 32) is clear in
+// keymask, so that row's scores are exactly 0 before the mask is added.
+__device__ __forceinline__ void zero_dead_krow(Frag<true>& kf, uint32_t keymask, int lane) {
+  if (!((keymask >> (lane & 31)) & 1u)) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kf.x[s] = bf16x8{};
+  }
+}
+
+__device__ __forceinline__ void zero_dead_krow(Frag<false>& kf, uint32_t keymask, int lane) {
+  if (!((keymask >> (lane & 31)) & 1u)) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) kf.x[j] = 0.f;
+  }
 }
 
 // Probabilities of one block in the operand form of the PV product.
@@ -809,8 +850,15 @@ struct BandSrc {
   int n_r, r, dil, nG, lane;
   int t0, w, wd;
   bool causal;
-  int A[2], B[2];  // window rows c in [A - 32 j, B - 32 j] of block j hold keys in the query's window
-  int qpos[2];     // token position of the lane's query of each half
+  int w_hi;  // w, or 0 when causal
+  // Query row of this lane in half nb (residue-sequence index, clamped to
+  // the last row) and its token position; recomputed where needed rather
+  // than held in registers through the block loop.
+  __device__ int qrow(int nb) const {
+    const int tq = t0 + 32 * nb + (lane & 31);
+    return tq < n_r ? tq : n_r - 1;
+  }
+  __device__ int qpos(int nb) const { return r + dil * qrow(nb); }
   __device__ int key(int i, int row) const { return kbase + kBlockK * (jlo + i) + row; }
   __device__ int kpos(int i, int row) const {
     if (i < nwin) {
@@ -839,21 +887,54 @@ struct BandSrc {
   __device__ uint32_t valid_bits(int i, int nb) const {
     if (i < nwin) {
       const int sh32 = kBlockK * (jlo + i);
-      const int lo = max(A[nb] - sh32, 0);
-      const int hi = min(B[nb] - sh32, 31);
+      // window rows c (block-relative, minus 4 (lane/32)) in [lo, hi] hold keys
+      // in the query's window
+      const int ln = lane_id_here();
+      const int tq = t0 + 32 * nb + (ln & 31);
+      const int a = tq - kbase - w - 4 * (ln >> 5), b = tq - kbase + w_hi - 4 * (ln >> 5);
+      const int lo = max(a - sh32, 0);
+      const int hi = min(b - sh32, 31);
       return lo > hi ? 0u : ((0xffffffffu >> (31 - hi)) & (0xffffffffu << lo));
     }
     // A global key g joins local row i unless g is already in W(i):
     // |i - g| <= w d and d divides i - g (no causal rows have global columns).
-    const int4* gl = reinterpret_cast<const int4*>(G + kBlockK * (i - nwin) + 4 * (lane >> 5));
+    // rows 8 g4 + 4 hh + [0, 4) of the block: one asm block that waits for
+    // its reads (the compiler would otherwise wait for the key loads in
+    // flight into the staging area first)
+    const int ln = lane_id_here();
+    const uint32_t ga = (uint32_t)(uintptr_t)(LDS_AS const void*)(G + kBlockK * (i - nwin) + 4 * (ln >> 5));
+    u32x4 xs[4];
+    asm volatile(
+        "ds_read_b128 %0, %4\n"
+        "ds_read_b128 %1, %4 offset:32\n"
+        "ds_read_b128 %2, %4 offset:64\n"
+        "ds_read_b128 %3, %4 offset:96\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(xs[0]), "=&v"(xs[1]), "=&v"(xs[2]), "=&v"(xs[3])
+        : "v"(ga)
+        : "memory");
     const uint32_t span = 2u * (uint32_t)wd;
+    const int tq = t0 + 32 * nb + (ln & 31);
+    const int qp = r + dil * (tq < n_r ? tq : n_r - 1);
     uint32_t vb = 0;
+    if (dil == 1) {
+      // bit = 1 when u = qp - g + wd exceeds span (g outside the window):
+      // med3(u, span, span + 1) - span, without a compare through VCC
+      const uint32_t qpw = (uint32_t)(qp + wd);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vb |= above_span(qpw - xs[g4][e], span) << (8 * g4 + e);
+        }
+      return vb;
+    }
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const int4 x = gl[2 * g4];  // rows 8 g4 + 4 hh + [0, 4)
+      const u32x4 x = xs[g4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int dd = qpos[nb] - x[e];
+        const int dd = qp - (int)x[e];
         bool in_w = (uint32_t)(dd + wd) <= span;
         if (dil != 1) in_w = in_w && (dd % dil == 0);
         vb |= in_w ? 0u : (1u << (8 * g4 + e));
@@ -984,7 +1065,7 @@ struct BandLoop {
   // Validity bits of window block i read from the mask now (rows in
   // [0, n_r) with mask 1 or 2).
   __device__ uint32_t window_keymask(int i) const {
-    const int row = lane & 31;
+    const int row = lane_id_here() & 31;
     const int m = src.exists(i, row) ? (int)src.mrow[src.kpos(i, row)] : 0;
     return (uint32_t)__ballot(m == 1 || m == 2);
   }
@@ -1012,7 +1093,7 @@ struct BandLoop {
     }
   }
   __device__ void tab_commit(uint32_t* tab) {
-    if (tab_cnt > 2 * kTabPairs) return;  // ktab stays null
+    if (tab_cnt > 2 * kTabPairs) return;  // ktab stays null, no block is taken as full
 #pragma unroll
     for (int p = 0; p < kTabPairs; ++p) {
       if (2 * p >= tab_cnt) break;
@@ -1021,8 +1102,64 @@ struct BandLoop {
         tab[2 * p] = (uint32_t)bits;
         tab[2 * p + 1] = (uint32_t)(bits >> 32);
       }
+      full_keys |= ((uint32_t)bits == 0xffffffffu ? 1u : 0u) << (2 * p);
+      full_keys |= ((uint32_t)(bits >> 32) == 0xffffffffu ? 1u : 0u) << (2 * p + 1);
     }
     ktab = tab;
+  }
+
+  // Window blocks (list index) whose 32 keys exist and lie in the window of
+  // every query of both halves: [fast_lo, fast_hi).  Among them, those whose
+  // keys all carry mask 1 or 2 (bit k of full_keys for block first + kWaves k)
+  // take fast_step.
+  int fast_lo = 0, fast_hi = 0;
+  uint32_t full_keys = 0;
+  __device__ void set_fast_range() {
+    // block j holds keys kbase + 32 j ..: 32 j - w >= 63 - w and 32 j - w + 31 <= w_hi
+    int jl = (kTileQ - 1 + kBlockK - 1) / kBlockK;
+    int jh = w + w_hi - (kBlockK - 1) >= 0 ? (w + w_hi - (kBlockK - 1)) / kBlockK + 1 : 0;  // exclusive
+    // keys in [0, n_r): kbase + 32 j >= 0 and kbase + 32 j + 31 < n_r
+    const int kb0 = src.kbase;
+    jl = max(jl, kb0 >= 0 ? 0 : (-kb0 + kBlockK - 1) / kBlockK);
+    jh = min(jh, src.n_r - kb0 - kBlockK >= 0 ? (src.n_r - kb0 - kBlockK) / kBlockK + 1 : 0);
+    if (t0 + 32 >= src.n_r) jh = jl;  // the second half has no rows
+    fast_lo = max(jl - src.jlo, 0);
+    fast_hi = max(min(jh - src.jlo, src.nwin), fast_lo);
+  }
+  __device__ bool is_fast(int i) const {
+    const int k = (i - first_) / kWaves;
+    return i >= fast_lo && i < fast_hi && k < 32 && ((full_keys >> k) & 1u);
+  }
+
+  // A block known full for both halves: no classification, no masks.
+  template <int kStage>
+  __device__ __forceinline__ void fast_step(WaveState& st, const Frag<B16> (&qf)[2], int i, int end, float c) {
+    const unsigned char* cst = lds + kStage * L::kStageBytes;
+    if (i + kWaves < end)
+      wait_vmem_but<kIssueLoads>();
+    else
+      wait_vmem_all();
+    Frag<B16> kf;
+    read_kfrag(kf, cst, lane);
+    VtFrag<B16> vt;
+    read_vt_now(vt, cst + L::kBlockBytes, lane);
+    if (i + 2 * kWaves < end) {
+      wait_lds_all();  // the fragment reads of this stage are done before it is refilled
+      issue(i + 2 * kWaves, kStage);
+    }
+    f32x16 s[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[nb][r] = 0.f;
+      qk(s[nb], kf, qf[nb]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      PFrag<B16> pf;
+      softmax_core<B16>(st, nb, s[nb], pf, c);
+      pv(st.o[nb], pf, vt);
+    }
   }
 
   // 0 = empty, 1 = partial, 2 = full for query half nb of window block i.
@@ -1035,8 +1172,9 @@ struct BandLoop {
     return full ? 2 : 1;
   }
 
-  template <int kStage>
-  __device__ __forceinline__ void step(WaveState& st, const Frag<B16> (&qf)[2], int i, int end, float c) {
+  // A general block (window edge, padded keys, global columns).
+  __device__ __forceinline__ void step(WaveState& st, const Frag<B16> (&qf)[2], int i, int end, float c,
+                                       int kStage) {
     const int hh = lane >> 5;
     const unsigned char* cst = lds + kStage * L::kStageBytes;
     // Block i landed in this stage; block i + kWaves (other stage) may still
@@ -1064,7 +1202,12 @@ struct BandLoop {
       issue(i + 2 * kWaves, kStage);
     }
     if (keymask == 0u) return;  // no key of the block is in any key set
-    if (keymask != 0xffffffffu) zero_dead_keys(vt, keymask, lane);
+    if (keymask != 0xffffffffu) {
+      // rows of keys outside every key set contribute exactly nothing, even
+      // where their stored values are not finite
+      zero_dead_keys(vt, keymask, lane);
+      zero_dead_krow(kf, keymask, lane);
+    }
 
     const bool win = i < src.nwin;
     int cls[2];
@@ -1072,28 +1215,32 @@ struct BandLoop {
     for (int nb = 0; nb < 2; ++nb) cls[nb] = win ? classify(i, nb, keymask) : (t0 + 32 * nb < src.n_r ? 1 : 0);
     if (cls[0] == 0 && cls[1] == 0) return;
 
+    // The mask enters through the accumulators' starting values: 0 where
+    // the key is scored, -inf where it is not, so the QK products come out
+    // masked (-inf + finite = -inf) with no pass over the scores after them.
     f32x16 s[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
+      if (cls[nb] == 2) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[nb][r] = 0.f;
-      qk(s[nb], kf, qf[nb]);
-    }
-    if (cls[0] != 2 || cls[1] != 2) {
-      // keep the mask work inside the (uniform) branch
-      __asm__ volatile("" ::: "memory");
+        for (int r = 0; r < 16; ++r) s[nb][r] = 0.f;
+      } else if (cls[nb] == 0) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        uint32_t vmk = 0xffffffffu;  // bit c_r set <=> element r is in its row's key set
-        if (cls[nb] == 0)
-          vmk = 0u;
-        else if (cls[nb] == 1)
-          vmk = src.valid_bits(i, nb) & (keymask >> (4 * hh));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[nb][r] = (vmk & (1u << acc_c(r))) ? s[nb][r] : kNegInf;
-        st.cnt[nb] += __popc(vmk & 0x0f0f0f0fu) - 16;  // the softmax below adds 16
+        for (int r = 0; r < 16; ++r) s[nb][r] = kNegInf;
+        st.cnt[nb] -= 16;  // softmax_core adds 16
+      } else {
+        const uint32_t vmk = src.valid_bits(i, nb) & (keymask >> (4 * hh));  // bit c_r: element r scored
+        const uint32_t inv = ~vmk;
+        // all ones where element r is not scored, then the bits of -inf
+#define LF_BIAS(r) s[nb][r] = __builtin_bit_cast(float, (uint32_t)bit_as_mask<acc_c(r)>(inv) & 0xff800000u)
+        LF_BIAS(0); LF_BIAS(1); LF_BIAS(2); LF_BIAS(3); LF_BIAS(4); LF_BIAS(5); LF_BIAS(6); LF_BIAS(7);
+        LF_BIAS(8); LF_BIAS(9); LF_BIAS(10); LF_BIAS(11); LF_BIAS(12); LF_BIAS(13); LF_BIAS(14); LF_BIAS(15);
+#undef LF_BIAS
+        st.cnt[nb] += __popc(vmk & 0x0f0f0f0fu) - 16;  // softmax_core adds 16
       }
     }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) qk(s[nb], kf, qf[nb]);
     // half 0's softmax runs while half 1's QK products are in flight, and
     // half 0's PV products while half 1's softmax runs
 #pragma unroll
@@ -1108,9 +1255,15 @@ struct BandLoop {
   // already be issued into stages 0 and 1 (those that exist).
   __device__ void run(WaveState& st, const Frag<B16> (&qf)[2], int first, int end, float c) {
     for (int i = first; i < end; i += 2 * kWaves) {
-      step<0>(st, qf, i, end, c);
+      if (is_fast(i))
+        fast_step<0>(st, qf, i, end, c);
+      else
+        step(st, qf, i, end, c, 0);
       if (i + kWaves >= end) break;
-      step<1>(st, qf, i + kWaves, end, c);
+      if (is_fast(i + kWaves))
+        fast_step<1>(st, qf, i + kWaves, end, c);
+      else
+        step(st, qf, i + kWaves, end, c, 1);
     }
   }
 };
@@ -1174,22 +1327,7 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
   const int jlo = kbase >= 0 ? 0 : (-kbase) / kBlockK;
   const int jhi = min(S, (n_r - kbase + kBlockK - 1) / kBlockK);
 
-  // Query rows of this lane: t = t0 + 32nb + lane%32, token r + dil*t.
   BandSrc src;
-  int qm[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int tq = t0 + 32 * nb + (lane & 31);
-    const bool inq = tq < n_r;
-    src.qpos[nb] = r + dil * (inq ? tq : n_r - 1);
-    qm[nb] = inq ? mrow[src.qpos[nb]] : 0;
-    src.A[nb] = tq - kbase - w - 4 * hh;
-    src.B[nb] = tq - kbase + w_hi - 4 * hh;
-  }
-  Frag<B16> qf[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) load_frag(qf[nb], qh + (size_t)src.qpos[nb] * rs, hh);
-
   src.mrow = mrow;
   src.G = sh.G;
   src.kbase = kbase;
@@ -1202,14 +1340,24 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
   src.lane = lane;
   src.t0 = t0;
   src.w = w;
+  src.w_hi = w_hi;
   src.wd = w * dil;
   src.causal = causal;
+
+  // Query rows of this lane: t = t0 + 32nb + lane%32, token r + dil*t.
+  int qm[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) qm[nb] = t0 + 32 * nb + (lane & 31) < n_r ? mrow[src.qpos(nb)] : 0;
+  Frag<B16> qf[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) load_frag(qf[nb], qh + (size_t)src.qpos(nb) * rs, hh);
   unsigned char* area = sh.buf + wv * Ly::kWaveBytes;
   BandLoop<B16> loop(src, reinterpret_cast<const T*>(p.k) + head, reinterpret_cast<const T*>(p.v) + head, rs, area, n,
                      t0, w, w_hi);
   // validity bytes of the wave's window blocks, then its first two window
   // blocks: all of them fly during the scan
   loop.tab_load(wv);
+  loop.set_fast_range();
   if (wv < src.nwin) loop.issue(wv, 0);
   if (wv + kWaves < src.nwin) loop.issue(wv + kWaves, 1);
   loop.tab_commit(sh.ktab[wv]);
@@ -1255,7 +1403,7 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
       const int quad = wv * kQuads + k;
       const int nb = quad >> 1, db = quad & 1;
       if (nb ? is_zero[1] : is_zero[0]) {
-        const int qp = nb ? src.qpos[1] : src.qpos[0];
+        const int qp = src.qpos(nb);
         store_quadrant<B16>(out + (size_t)qp * rs, db, hh, nullptr, 0.f, true);
         if (p.row_nnz && db == 0 && hh == 0) p.row_nnz[((size_t)b * p.H + h) * n + qp] = 0;
       }
@@ -1270,7 +1418,7 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
     const bool loc = nb ? is_local[1] : is_local[0];
     const bool zer = nb ? is_zero[1] : is_zero[0];
     if (!loc && !zer) return;
-    const int qp = nb ? src.qpos[1] : src.qpos[0];
+    const int qp = src.qpos(nb);
     store_quadrant<B16>(out + (size_t)qp * rs, db, hh, o, loc ? 1.0f / Lsum : 0.f, !loc);
     if (p.row_nnz && db == 0 && hh == 0) p.row_nnz[((size_t)b * p.H + h) * n + qp] = loc ? cnt : 0;
   });
