@@ -981,17 +981,29 @@ __device__ __forceinline__ void softmax_core(WaveState& st, int nb, f32x16& s, P
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -st.m[nb]));
-  float t8[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) t8[i] = s[2 * i] + s[2 * i + 1];
-  st.l[nb] += ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
   st.cnt[nb] += 16;
   if constexpr (B16) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pf.x[ks][e] = (__bf16)s[8 * ks + e];
+    // row sum of the rounded probabilities that enter P V (two bf16 at a
+    // time with fp32 accumulation), in two chains
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    float la = 0.f, lb = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x2 p0 = {pf.x[0][2 * j], pf.x[0][2 * j + 1]};
+      const bf16x2 p1 = {pf.x[1][2 * j], pf.x[1][2 * j + 1]};
+      la = __builtin_amdgcn_fdot2_f32_bf16(p0, one, la, false);
+      lb = __builtin_amdgcn_fdot2_f32_bf16(p1, one, lb, false);
+    }
+    st.l[nb] += la + lb;
   } else {
+    float t8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t8[i] = s[2 * i] + s[2 * i + 1];
+    st.l[nb] += ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
 #pragma unroll
     for (int r = 0; r < 16; ++r) pf.x[r] = s[r];
   }
