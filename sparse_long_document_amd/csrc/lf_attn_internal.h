@@ -11,10 +11,9 @@ namespace lf {
 
 // Tiling constants shared by the host planner and the kernels.
 constexpr int kHeadDim = 64;       // D
-constexpr int kTileQ = 64;         // query rows of one band workgroup
-constexpr int kWaveQ = 64;         // query rows of one wave
+constexpr int kTileQ = 64;         // query rows of one band workgroup (two halves of 32)
 constexpr int kBlockK = 32;        // keys per inner block (M of the 32x32 MFMA)
-constexpr int kWaves = 2;          // waves per workgroup (they split a tile's keys)
+constexpr int kWaves = 4;          // waves per workgroup: query half x key parity
 constexpr int kThreads = 64 * kWaves;
 constexpr int kGlobalChunk = 512;  // keys per split of a global row
 constexpr int kPartialStride = 68; // floats per partial record: m, l, count, pad, O[64]
