@@ -229,58 +229,69 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(LDS_AS const void*)p;
 }
 
-// K fragment (key row lane % 32) and V^T operand of the block in `stage`,
-// read in one asm block that waits for its reads before it ends.  The
-// compiler cannot tell these reads from the direct-to-LDS loads still in
-// flight into other stages and would otherwise wait for all of them first;
-// the caller has waited for this stage's loads (and the barrier after which
-// the other wave's share is visible).
-//
-// ds_read_b64_tr_b16: in each group of 16 lanes, lane j receives element
-// j%4 of the 8-byte chunk addressed by lane 4e + j/4, as its element e.
-// Lane 4e+q of group g points at key row 16ks + 8half + 4(g/2) + e, head
-// dims 32db + 16(g%2) + 4q .. +3, so lane j of the group gets head dim
-// 32db + 16(g%2) + j for keys e = 0..3.
-__device__ __forceinline__ void read_frags_now(Frag<true>& kf, VtFrag<true>& vt, const unsigned char* stage) {
+// Per-lane LDS addresses of the fragment reads of stage 0 of a ring (the
+// other stage is kStageBytes further, an immediate offset).
+//   K: key row lane % 32, 16-byte chunks 2s + lane/32 (s = 0..3), swizzled;
+//   V: ds_read_b64_tr_b16: in each group of 16 lanes, lane j receives
+//   element j%4 of the 8-byte chunk addressed by lane 4e + j/4, as its
+//   element e.  Lane 4e+q of group g points at key row 16ks + 8half +
+//   4(g/2) + e, head dims 32db + 16(g%2) + 4q .. +3, so lane j of the group
+//   gets head dim 32db + 16(g%2) + j for keys e = 0..3.
+struct FragAddr {
+  uint32_t k[4];
+  uint32_t v[2];
+};
+
+__device__ __forceinline__ FragAddr frag_addr(const unsigned char* ring, int lane) {
   using L = Lay<true>;
-  const int lane = lane_id_here();
+  FragAddr fa;
   const int row = lane & 31;
   const int hh = lane >> 5;
-  const uint32_t kbase = lds_addr(stage) + (uint32_t)(row * L::kRowBytes);
+  const uint32_t kbase = lds_addr(ring) + (uint32_t)(row * L::kRowBytes);
   const int sw = kswz<true>(row);
-  uint32_t ka[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) ka[s] = kbase + (uint32_t)(((2 * s + hh) ^ sw) << 4);
+  for (int s = 0; s < 4; ++s) fa.k[s] = kbase + (uint32_t)(((2 * s + hh) ^ sw) << 4);
   const int g = lane >> 4;
   const int row0 = 4 * (g >> 1) + ((lane & 15) >> 2);
   const int byte0 = 32 * (g & 1) + 8 * (lane & 3);
   const int vsw = vswz<true>(row0);  // rows 16ks + 8half + row0 share bit 1 with row0
-  const uint32_t vbase = lds_addr(stage + L::kBlockBytes);
-  uint32_t va[2];
+  const uint32_t vbase = lds_addr(ring + L::kBlockBytes);
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
     const int byte = 64 * db + byte0;
-    va[db] = vbase + (uint32_t)(row0 * 128 + (((byte >> 4) ^ vsw) << 4) + (byte & 15));
+    fa.v[db] = vbase + (uint32_t)(row0 * 128 + (((byte >> 4) ^ vsw) << 4) + (byte & 15));
   }
+  return fa;
+}
+
+// K fragment and V^T operand of the block in the stage kOff bytes into the
+// ring, read in one asm block that waits for its reads before it ends.  The
+// compiler cannot tell these reads from the direct-to-LDS loads still in
+// flight into the other stage and would otherwise wait for all of them
+// first; the caller has waited for this stage's loads (and the barrier
+// after which the other wave's share is visible).
+template <int kOff>
+__device__ __forceinline__ void read_frags_at(Frag<true>& kf, VtFrag<true>& vt, const FragAddr& fa) {
   u32x4 k[4];
   u32x2 r[8];  // [db][ks][lo, hi]: key rows 16ks + 8half at +2048ks + 1024half
   asm volatile(
-      "ds_read_b128 %0, %12\n"
-      "ds_read_b128 %1, %13\n"
-      "ds_read_b128 %2, %14\n"
-      "ds_read_b128 %3, %15\n"
-      "ds_read_b64_tr_b16 %4, %16\n"
-      "ds_read_b64_tr_b16 %5, %16 offset:1024\n"
-      "ds_read_b64_tr_b16 %6, %16 offset:2048\n"
-      "ds_read_b64_tr_b16 %7, %16 offset:3072\n"
-      "ds_read_b64_tr_b16 %8, %17\n"
-      "ds_read_b64_tr_b16 %9, %17 offset:1024\n"
-      "ds_read_b64_tr_b16 %10, %17 offset:2048\n"
-      "ds_read_b64_tr_b16 %11, %17 offset:3072\n"
+      "ds_read_b128 %0, %12 offset:%18\n"
+      "ds_read_b128 %1, %13 offset:%18\n"
+      "ds_read_b128 %2, %14 offset:%18\n"
+      "ds_read_b128 %3, %15 offset:%18\n"
+      "ds_read_b64_tr_b16 %4, %16 offset:%18\n"
+      "ds_read_b64_tr_b16 %5, %16 offset:%19\n"
+      "ds_read_b64_tr_b16 %6, %16 offset:%20\n"
+      "ds_read_b64_tr_b16 %7, %16 offset:%21\n"
+      "ds_read_b64_tr_b16 %8, %17 offset:%18\n"
+      "ds_read_b64_tr_b16 %9, %17 offset:%19\n"
+      "ds_read_b64_tr_b16 %10, %17 offset:%20\n"
+      "ds_read_b64_tr_b16 %11, %17 offset:%21\n"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]),
         "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1])
+      : "v"(fa.k[0]), "v"(fa.k[1]), "v"(fa.k[2]), "v"(fa.k[3]), "v"(fa.v[0]), "v"(fa.v[1]), "i"(kOff),
+        "i"(kOff + 1024), "i"(kOff + 2048), "i"(kOff + 3072)
       : "memory");
 #pragma unroll
   for (int s = 0; s < 4; ++s) kf.x[s] = __builtin_bit_cast(bf16x8, k[s]);
@@ -293,9 +304,19 @@ __device__ __forceinline__ void read_frags_now(Frag<true>& kf, VtFrag<true>& vt,
     }
 }
 
+__device__ __forceinline__ void read_frags(Frag<true>& kf, VtFrag<true>& vt, const FragAddr& fa,
+                                           const unsigned char*, int stage) {
+  static_assert(Lay<true>::kStages == 2, "two stages: offsets 0 and kStageBytes");
+  if (stage == 0)
+    read_frags_at<0>(kf, vt, fa);
+  else
+    read_frags_at<Lay<true>::kStageBytes>(kf, vt, fa);
+}
+
 // fp32: plain reads (the compiler may wait for every load in flight first;
 // this instantiation is not tuned).
-__device__ __forceinline__ void read_frags_now(Frag<false>& kf, VtFrag<false>& vt, const unsigned char* stage) {
+__device__ __forceinline__ void read_frags(Frag<false>& kf, VtFrag<false>& vt, const FragAddr&,
+                                           const unsigned char* stage, int) {
   using L = Lay<false>;
   const int lane = lane_id();
   const int row = lane & 31;
@@ -825,10 +846,15 @@ struct BandSrc {
 #pragma unroll
         for (int e = 0; e < 4; ++e) vb |= above_span(qpw - x[e], span) << (8 * g4 + e);
       } else {
+        // the divisor passes through an empty asm so that the division's
+        // setup is redone here instead of being hoisted out of the block loop
+        // and held in a register through every block
+        int d = dil;
+        asm volatile("" : "+s"(d));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int dd = qp - (int)x[e];
-          const bool in_w = (uint32_t)(dd + wd) <= span && dd % dil == 0;
+          const bool in_w = (uint32_t)(dd + wd) <= span && dd % d == 0;
           vb |= in_w ? 0u : (1u << (8 * g4 + e));
         }
       }
@@ -867,6 +893,7 @@ struct HalfLoop {
   int tab_cnt;
   uint32_t full_keys;  // bit k: every key of table block kp + 2k is valid
   int fast_lo, fast_hi;
+  FragAddr fa;  // this lane's fragment read addresses in stage 0 (bf16)
 
   __device__ HalfLoop(const Src& s, const T* k, const T* v, uint32_t rs_, unsigned char* ring_, int n, int kp_,
                       int qh_)
@@ -881,6 +908,7 @@ struct HalfLoop {
     vk0 = 2u * (row_off + 8u * (uint32_t)ck);
     vk1 = 2u * (row_off + 8u * (uint32_t)(ck ^ 4));
     vv = 2u * (row_off + 8u * (uint32_t)cv);
+    if constexpr (B16) fa = frag_addr(ring, lane);
     src.fast_range(fast_lo, fast_hi);
   }
 
@@ -905,7 +933,9 @@ struct HalfLoop {
                                                  0, 0);
       }
     } else {
-      issue_rows<B16>(kb, vb, rs, [&](int r) { return src.kpos(i, r); }, dst, lane, qh * L::kHalfLoads);
+      // lane-derived terms recomputed here (a rare path) rather than hoisted
+      // out of the block loop and held in registers
+      issue_rows<B16>(kb, vb, rs, [&](int r) { return src.kpos(i, r); }, dst, lane_id_here(), qh * L::kHalfLoads);
     }
   }
 
@@ -954,17 +984,18 @@ struct HalfLoop {
     return i >= fast_lo && i < fast_hi && k < 32 && ((full_keys >> k) & 1u);
   }
 
-  // Block i, staged in cst (landed and visible).
-  __device__ __forceinline__ void step(HalfState& st, const Frag<B16>& qf, int i, const unsigned char* cst,
-                                       float c) {
+  // Block i, staged in stage `stage` (landed and visible).
+  __device__ __forceinline__ void step(HalfState& st, const Frag<B16>& qf, int i, int stage, float c) {
+    const unsigned char* cst = ring + stage * L::kStageBytes;
     Frag<B16> kf;
     VtFrag<B16> vt;
     f32x16 s;
     if (is_fast(i)) {
       // every key of the block is scored for every query of the half
-      read_frags_now(kf, vt, cst);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+      read_frags(kf, vt, fa, cst, stage);
+      const f32x16 zero = {};
+      s = zero;
+      qk(s, kf, qf);
     } else {
       uint32_t keymask;
       if (i >= src.nwin) {
@@ -979,7 +1010,7 @@ struct HalfLoop {
       if (keymask == 0u) return;  // no key of the block is in any key set
       const int cls = src.classify(i, keymask);
       if (cls == 0) return;
-      read_frags_now(kf, vt, cst);
+      read_frags(kf, vt, fa, cst, stage);
       const int ln = lane_id_here();
       if (keymask != 0xffffffffu) {
         // rows of keys outside every key set contribute exactly nothing, even
@@ -1003,8 +1034,8 @@ struct HalfLoop {
 #undef LF_BIAS
         st.cnt += __popc(vmk & 0x0f0f0f0fu) - 16;  // softmax_core adds 16
       }
+      qk(s, kf, qf);
     }
-    qk(s, kf, qf);
     PFrag<B16> pf;
     softmax_core<B16>(st, s, pf, c);
     pv(st.o, pf, vt);
@@ -1040,7 +1071,7 @@ struct HalfLoop {
       block_barrier();
       const int nxt = i + 2 * (L::kStages - 1);
       if (nxt < end) issue(nxt, stage == 0 ? L::kStages - 1 : stage - 1);
-      if (active && i < end) step(st, qf, i, ring + stage * L::kStageBytes, c);
+      if (active && i < end) step(st, qf, i, stage, c);
       stage = stage == L::kStages - 1 ? 0 : stage + 1;
     }
   }
