@@ -156,6 +156,10 @@ lf_status lf_attn_forward(const lf_attn_params* p, const void* q, const void* k,
     kp.tile0[h] = pl.tile0[h];
   }
   kp.tile0[p->H] = pl.tile0[p->H];
+  kp.uni_dil = pl.dil[0];
+  for (int h = 1; h < p->H; ++h)
+    if (pl.dil[h] != pl.dil[0]) kp.uni_dil = 0;
+  kp.tiles_per_head = kp.uni_dil > 0 ? pl.tile0[1] - pl.tile0[0] : 0;
   const int e = lf::launch_forward(kp, p->dtype, stream);
   return e == 0 ? LF_OK : LF_ERR_HIP;
 }

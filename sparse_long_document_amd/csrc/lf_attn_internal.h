@@ -38,6 +38,8 @@ struct KernelParams {
   int32_t n_band;      // band workgroups in the launch
   int32_t n_glob;      // global-row workgroups in the launch
   int32_t S;           // splits of a global row
+  int32_t uni_dil;     // the dilation of every head when all heads share one, else 0
+  int32_t tiles_per_head;  // band tiles of each head of a batch row when uni_dil > 0
   int32_t dil[LF_MAX_HEADS];
   int32_t tile0[LF_MAX_HEADS + 1];  // first band tile of each head within a batch row
 };

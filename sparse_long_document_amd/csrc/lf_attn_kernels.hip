@@ -148,6 +148,10 @@ __device__ __forceinline__ void wait_vmem_but() {
 // from moving memory accesses across it.
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Barrier after which this wave's LDS writes are visible to the workgroup
+// (vector-memory loads in flight are not waited for).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ void load_frag(Frag<true>& f, const __bf16* row, int hh) {
   const bf16x8* p = reinterpret_cast<const bf16x8*>(row);
 #pragma unroll
@@ -510,15 +514,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Bit e of the result: byte e of the 16 bytes x is 2.  After x ^ 0x02 the
+// bytes that were 2 are the zero bytes; per byte, ((t & 0x7f) + 0x7f) | t
+// has bit 7 set exactly when the byte is not zero (no carry leaves a byte).
+__device__ __forceinline__ uint32_t twos16(const u32x4& x) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t t = x[j] ^ 0x02020202u;
+    const uint32_t f = ~(((t & 0x7f7f7f7fu) + 0x7f7f7f7fu) | t) & 0x80808080u;
+    // gather bits 7, 15, 23, 31 into bits 4j .. 4j+3
+    bits |= (((f >> 7) & 1u) | ((f >> 14) & 2u) | ((f >> 21) & 4u) | ((f >> 28) & 8u)) << (4 * j);
+  }
+  return bits;
+}
+
 // Bitmask of the bytes equal to 2 among mrow[p0 .. p0+16) (clipped to n).
 __device__ __forceinline__ uint32_t match16(const int8_t* __restrict__ mrow, int p0, int n) {
   uint32_t bits = 0;
   if (p0 + 16 <= n && ((reinterpret_cast<uintptr_t>(mrow + p0) & 15u) == 0)) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(mrow + p0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bits |= (((x[j] >> (8 * e)) & 0xffu) == 2u ? 1u : 0u) << (4 * j + e);
+    bits = twos16(*reinterpret_cast<const u32x4*>(mrow + p0));
   } else {
 #pragma unroll
     for (int e = 0; e < 16; ++e)
@@ -540,21 +555,55 @@ __device__ __forceinline__ int wave_prefix(int cnt) {
   return pre;
 }
 
+// The scan's first round of mask loads (bytes [4096 u + 16 tid, +16) for
+// u < 4), issued before anything else so that they do not queue behind the
+// key and value loads.  Chunks that are out of range or unaligned are left
+// to the scan itself.
+constexpr int kScanStep = kThreads * 16;
+struct ScanPre {
+  u32x4 x[4];
+  uint32_t bits[4];  // twos16 of x, formed by scan_ready
+};
+__device__ __forceinline__ bool scan_chunk_ok(const int8_t* mrow, int p0, int n) {
+  return p0 + 16 <= n && ((reinterpret_cast<uintptr_t>(mrow) & 15u) == 0);
+}
+__device__ __forceinline__ void scan_preload(ScanPre& sp, const int8_t* __restrict__ mrow, int n) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int p0 = u * kScanStep + 16 * tid;
+    sp.x[u] = scan_chunk_ok(mrow, p0, n) ? *reinterpret_cast<const u32x4*>(mrow + p0) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Turns the preloaded chunks into bitmasks in straight-line code, where the
+// compiler's count of loads in flight is exact (at the scan loop's entry it
+// would wait for every load, the key loads included).
+__device__ __forceinline__ void scan_ready(ScanPre& sp) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) sp.bits[u] = twos16(sp.x[u]);
+}
+
 // Ordered list of positions j with mask_row[j] == 2 into G (LDS), at most
 // cap entries; returns the total count.  Every thread of the workgroup
 // calls it and gets the same result.  Each thread looks at 16 bytes of each
-// 4 KB step; four steps are loaded together and ranked with one barrier.
-__device__ int scan_globals(const int8_t* __restrict__ mrow, int n, int* G, int cap, int (*s_tot)[kWaves]) {
-  constexpr int kStep = kThreads * 16;
+// 4 KB step; four steps are loaded together (the first four from sp) and
+// ranked with one barrier.
+__device__ __forceinline__ int scan_globals(const ScanPre& sp, const int8_t* __restrict__ mrow, int n, int* G,
+                                            int cap, int (*s_tot)[kWaves]) {
   int total = 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  for (int base = 0; base < n; base += 4 * kStep) {
+  for (int base = 0; base < n; base += 4 * kScanStep) {
     uint32_t bits[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) bits[u] = match16(mrow, base + u * kStep + 16 * tid, n);
-    if (!__syncthreads_or((bits[0] | bits[1] | bits[2] | bits[3]) != 0)) continue;
+    for (int u = 0; u < 4; ++u) {
+      const int p0 = base + u * kScanStep + 16 * tid;
+      bits[u] = (base == 0 && scan_chunk_ok(mrow, p0, n)) ? sp.bits[u] : match16(mrow, p0, n);
+    }
+    // (barriers without fences: the key loads already in flight are not
+    // waited for here)
     int pre[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -562,7 +611,7 @@ __device__ int scan_globals(const int8_t* __restrict__ mrow, int n, int* G, int 
       pre[u] = wave_prefix(cnt);
       if (lane == 63) s_tot[u][wv] = pre[u] + cnt;
     }
-    __syncthreads();
+    lds_barrier();
     int off = total;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -577,16 +626,15 @@ __device__ int scan_globals(const int8_t* __restrict__ mrow, int n, int* G, int 
       while (bm) {
         const int e = __builtin_ctz(bm);
         bm &= bm - 1;
-        if (slot < cap) G[slot] = base + u * kStep + 16 * tid + e;
+        if (slot < cap) G[slot] = base + u * kScanStep + 16 * tid + e;
         ++slot;
       }
     }
     total = off;
-    __syncthreads();  // s_tot is reused by the next steps
+    lds_barrier();  // G is complete; s_tot is reused by the next steps
   }
   return __builtin_amdgcn_readfirstlane(total);  // the same in every lane
 }
-
 
 // Partial state of one wave parked in LDS for the merge: O^T as
 // [db][g][lane] f32x4, then per query (lane % 32) the reference max, the
@@ -957,6 +1005,7 @@ struct HalfLoop {
     const int row = lane & 31, half = lane >> 5;
 #pragma unroll
     for (int p = 0; p < kTabPairs; ++p) {
+      if (2 * p >= tab_cnt) break;
       const int k = 2 * p + half;
       const int i = kp + 2 * k;
       const bool ok = k < tab_cnt && src.exists(i, row);
@@ -1096,17 +1145,25 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
 
   const int b = L / p.tiles_per_b;
   const int rem = L - b * p.tiles_per_b;
-  // head: tile0 is non-decreasing; count entries <= rem, 8 loads per round
-  int h = 0;
-  for (int k0 = 1; k0 < p.H; k0 += 8) {
-    int cnt = 0;
+  int h, id, dil;
+  if (p.uni_dil > 0 && p.tiles_per_head > 0) {
+    // every head has the same dilation and tile count: no table lookups
+    h = rem / p.tiles_per_head;
+    id = rem - h * p.tiles_per_head;
+    dil = p.uni_dil;
+  } else {
+    // head: tile0 is non-decreasing; count entries <= rem, 8 loads per round
+    h = 0;
+    for (int k0 = 1; k0 < p.H; k0 += 8) {
+      int cnt = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) cnt += (k0 + k < p.H && p.tile0[k0 + k] <= rem) ? 1 : 0;
-    h += cnt;
-    if (cnt < 8) break;
+      for (int k = 0; k < 8; ++k) cnt += (k0 + k < p.H && p.tile0[k0 + k] <= rem) ? 1 : 0;
+      h += cnt;
+      if (cnt < 8) break;
+    }
+    id = rem - p.tile0[h];
+    dil = p.dil[h];
   }
-  const int id = rem - p.tile0[h];
-  const int dil = p.dil[h];
   const int n = p.n;
   const int qn = n / dil, rm = n % dil;
   const int T1 = (qn + 1 + kTileQ - 1) / kTileQ, T0 = (qn + kTileQ - 1) / kTileQ;
@@ -1154,6 +1211,8 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
   src.w_hi = w_hi;
   src.wd = w * dil;
 
+  ScanPre sp;
+  if (p.use_globals) scan_preload(sp, mrow, n);
   // Mask bytes of both halves' query rows (every wave sees the whole tile,
   // so the early-exit test below agrees across the workgroup).
   int qm[2];
@@ -1174,7 +1233,8 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
   loop.tab_commit(sh.ktab[wv]);
 
   if (p.use_globals) {
-    int nG = scan_globals(mrow, n, sh.G, LF_MAX_GLOBAL, sh.wave_tmp);
+    scan_ready(sp);
+    int nG = scan_globals(sp, mrow, n, sh.G, LF_MAX_GLOBAL, sh.wave_tmp);
     if (nG > p.max_global) {
       if (threadIdx.x == 0) atomicOr(p.status, LF_DEV_TOO_MANY_GLOBALS);
       nG = p.max_global;
@@ -1257,11 +1317,14 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
   const int nblk = src.nwin;
   HalfLoop<B16, ChunkSrc> loop(src, reinterpret_cast<const T*>(p.kg) + head,
                                reinterpret_cast<const T*>(p.vg) + head, rs, sh.buf + kp * Ly::kRingBytes, n, kp, qh);
+  ScanPre sp;
+  scan_preload(sp, mrow, n);
   loop.tab_load();
   loop.prime(nblk, [](int) { return true; });  // the split's keys do not depend on the scan
   loop.tab_commit(sh.ktab[wv]);
 
-  int nG = scan_globals(mrow, n, sh.G, LF_MAX_GLOBAL, sh.wave_tmp);
+  scan_ready(sp);
+  int nG = scan_globals(sp, mrow, n, sh.G, LF_MAX_GLOBAL, sh.wave_tmp);
   if (nG > p.max_global) {
     if (threadIdx.x == 0) atomicOr(p.status, LF_DEV_TOO_MANY_GLOBALS);
     nG = p.max_global;

@@ -113,6 +113,29 @@ def test_aliased_global_projections():
     check_full(prob)
 
 
+def test_mask_values_other_than_0_1_2_act_as_0():
+    # bytes such as 3, -1, -126 and 127, some right next to global tokens
+    # (the kernel finds the global tokens 16 mask bytes at a time)
+    prob = workloads.random_problem(13, B=2, n=700, H=2, window=40, global_positions=[0, 5, 130, 131, 600],
+                                    name="oddmask")
+    rng = np.random.default_rng(3)
+    m = prob.mask.clone()
+    for b in range(2):
+        for g in (5, 130, 600):
+            m[b, g - 1] = 3
+            m[b, g + 2] = -126
+        m[b, rng.integers(0, 700, size=40)] = torch.tensor(rng.choice([3, -1, 127, -126], size=40), dtype=torch.int8)
+        m[b, [0, 5, 130, 131, 600]] = 2
+    prob.mask = m
+    # the binding's validation rejects such bytes; the C ABI reads them as 0,
+    # so the reference is the oracle on the mask with those bytes set to 0
+    out, nnz = run_gpu(prob, validate=False, max_global=5)
+    prob.mask = torch.where((m == 1) | (m == 2), m, torch.zeros_like(m))
+    ref, rnnz = run_oracle(prob)
+    np.testing.assert_array_equal(nnz, rnnz)
+    assert np.abs(out - ref).max() <= TOL[prob.q.dtype]
+
+
 def test_scale_argument():
     prob = workloads.random_problem(8, B=1, n=300, H=1, window=30, n_global=2, scale=0.3, name="scale")
     check_full(prob)
