@@ -1374,15 +1374,21 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
   __syncthreads();
   if (!sh.flag) return;
 
+  // Merge: a group of 16 lanes per global token, each lane four head dims;
+  // every split's record of the token is loaded before any is used (the
+  // agent-scope loads go to the coherence point, so the merge is bound by
+  // how many of them are in flight).
   T* out = reinterpret_cast<T*>(p.out) + head;
-  const int d = lane_id_here();
-  for (int gj = wv; gj < nG; gj += kWaves) {
-    // online log-sum-exp merge of the S partials; loads issued 8 at a time
+  const int tid = 64 * wv + lane_id_here();
+  const int q4 = tid & 15;
+  for (int gj = tid >> 4; gj < nG; gj += kThreads / 16) {
+    // online log-sum-exp merge of the S partials, 8 at a time
     const float* recs = part_bh + (size_t)gj * S * kPartialStride;
-    float M = kNegInf, Lsum = 0.f, acc = 0.f;
+    float M = kNegInf, Lsum = 0.f;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
     int cnt = 0;
     for (int s0 = 0; s0 < S; s0 += 8) {
-      float ms[8], ls[8], os[8];
+      float ms[8], ls[8], os[8][4];
       int cs[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -1390,7 +1396,8 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
         ms[j] = ld_agent(rec);
         ls[j] = ld_agent(rec + 1);
         cs[j] = __builtin_bit_cast(int, ld_agent(rec + 2));
-        os[j] = ld_agent(rec + 4 + d);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) os[j][e] = ld_agent(rec + 4 + 4 * q4 + e);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -1400,13 +1407,18 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
         const float fb = (ms[j] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ms[j] - mn);
         M = mn;
         Lsum = Lsum * fa + ls[j] * fb;
-        acc = acc * fa + os[j] * fb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = acc[e] * fa + os[j][e] * fb;
         cnt += cs[j];
       }
     }
     const int pos = sh.G[gj];
-    out[(size_t)pos * rs + d] = (T)(acc / Lsum);
-    if (p.row_nnz && d == 0) p.row_nnz[(size_t)bh * n + pos] = cnt;
+    const float inv = 1.0f / Lsum;
+    float v4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v4[e] = acc[e] * inv;
+    store4<B16>(out + (size_t)pos * rs + 4 * q4, v4);
+    if (p.row_nnz && q4 == 0) p.row_nnz[(size_t)bh * n + pos] = cnt;
   }
   __syncthreads();
   if (wv == 0 && lane_id_here() == 0) __hip_atomic_store(p.tickets + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
