@@ -11,9 +11,12 @@
 
   python -m sparse_long_document_amd.counters traffic --workload W --fetch DIR --write DIR
           --copy-fetch DIR --copy-write DIR --out FILE [--mib N] [--kernel-hash H]
+          [--md FILE --avg-us T --algorithmic-bytes A --commands FILE]
       HBM bytes per launch of the attention kernel from two `--pmc` runs,
       each counter scaled by (known bytes / counted bytes) of the copy
-      kernel; merged into the JSON file FILE under key W.
+      kernel; merged into the JSON file FILE under key W.  With --md, also a
+      markdown summary (T: measured average launch duration in us; A: the
+      algorithmic bytes per launch; the commands listed from FILE).
 """
 from __future__ import annotations
 
@@ -120,6 +123,31 @@ def cmd_traffic(args):
         json.dump(data, fh, indent=1, sort_keys=True)
         fh.write("\n")
     print(json.dumps({args.workload: ent}))
+    if args.md:
+        cmds = open(args.commands).read().strip() if args.commands else ""
+        lines = [f"# HBM traffic of lf_attn_fwd: {args.workload}", "",
+                 "Commands (from the repository root, after `cd /tmp && export TMPDIR=/tmp`), one counter per run:",
+                 "", "```", cmds, "```", "",
+                 f"Calibration: an elementwise copy of {args.mib} MiB ({known_kib:.0f} KiB read and written per "
+                 f"dispatch) counts FETCH_SIZE = {cf:.0f} KiB and WRITE_SIZE = {cw:.0f} KiB per dispatch, so the "
+                 f"factors are {ff:.4f} (fetch) and {fw:.4f} (write).", "",
+                 f"| | counter (KiB / dispatch, median of {nf}) | x factor | bytes per launch |",
+                 "|---|---|---|---|",
+                 f"| fetch | {kf:.1f} | {ff:.4f} | {fetch_b / 1e6:.2f} MB |",
+                 f"| write | {kw:.1f} | {fw:.4f} | {write_b / 1e6:.2f} MB |",
+                 f"| total | | | **{(fetch_b + write_b) / 1e6:.2f} MB** |", ""]
+        if args.algorithmic_bytes:
+            a = float(args.algorithmic_bytes)
+            lines += [f"Algorithmic bytes per launch (q, k, v read and out written per (token, head); k_g, v_g "
+                      f"of the batch row; q_g of the global rows; the mask): {a / 1e6:.2f} MB.  "
+                      f"Counted / algorithmic = {(fetch_b + write_b) / a:.3f}.", ""]
+        if args.avg_us:
+            t = float(args.avg_us) * 1e-6
+            lines += [f"At the measured {args.avg_us} us per launch: {(fetch_b + write_b) / t / 1e9:.0f} GB/s "
+                      f"counted ({(fetch_b + write_b) / t / 8e12 * 100:.1f} % of 8 TB/s).", ""]
+        lines += [f"Kernel source hash {args.kernel_hash}."]
+        with open(args.md, "w") as fh:
+            fh.write("\n".join(lines) + "\n")
 
 
 def main(argv=None):
@@ -143,6 +171,10 @@ def main(argv=None):
     t.add_argument("--kernel-hash", default=None, help="default: the current kernel sources")
     t.add_argument("--mib", type=int, default=512)
     t.add_argument("--out", required=True)
+    t.add_argument("--md", default=None)
+    t.add_argument("--avg-us", default=None)
+    t.add_argument("--algorithmic-bytes", default=None)
+    t.add_argument("--commands", default=None)
     args = ap.parse_args(argv)
     {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic}[args.cmd](args)
 
