@@ -514,32 +514,68 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Bit e of the result: byte e of the 16 bytes x is 2.  After x ^ 0x02 the
+// Bit 7 of byte e of the result: byte e of x is 2.  After x ^ 0x02 the
 // bytes that were 2 are the zero bytes; per byte, ((t & 0x7f) + 0x7f) | t
 // has bit 7 set exactly when the byte is not zero (no carry leaves a byte).
-__device__ __forceinline__ uint32_t twos16(const u32x4& x) {
-  uint32_t bits = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t t = x[j] ^ 0x02020202u;
-    const uint32_t f = ~(((t & 0x7f7f7f7fu) + 0x7f7f7f7fu) | t) & 0x80808080u;
-    // gather bits 7, 15, 23, 31 into bits 4j .. 4j+3
-    bits |= (((f >> 7) & 1u) | ((f >> 14) & 2u) | ((f >> 21) & 4u) | ((f >> 28) & 8u)) << (4 * j);
-  }
-  return bits;
+__device__ __forceinline__ uint32_t twos_flags(uint32_t x) {
+  const uint32_t t = x ^ 0x02020202u;
+  return ~(((t & 0x7f7f7f7fu) + 0x7f7f7f7fu) | t) & 0x80808080u;
 }
 
-// Bitmask of the bytes equal to 2 among mrow[p0 .. p0+16) (clipped to n).
-__device__ __forceinline__ uint32_t match16(const int8_t* __restrict__ mrow, int p0, int n) {
-  uint32_t bits = 0;
-  if (p0 + 16 <= n && ((reinterpret_cast<uintptr_t>(mrow + p0) & 15u) == 0)) {
-    bits = twos16(*reinterpret_cast<const u32x4*>(mrow + p0));
-  } else {
+// Bits 7, 15, 23, 31 of f as bits 0 .. 3.
+__device__ __forceinline__ uint32_t gather_flags(uint32_t f) {
+  return ((f >> 7) & 1u) | ((f >> 14) & 2u) | ((f >> 21) & 4u) | ((f >> 28) & 8u);
+}
+
+// The mask bytes of one batch row, read through a buffer resource over the
+// whole mask: reads past its end return zero, so no load needs a guard and
+// none waits for another.  Rows whose 16-byte chunks are all aligned (n and
+// the mask's address multiples of 16) are read 16 bytes per load, others a
+// byte per load.
+struct MaskRow {
+  __amdgpu_buffer_rsrc_t rm;
+  uint32_t row;  // byte offset of the row
+  bool wide;
+};
+
+__device__ __forceinline__ MaskRow mask_row(const int8_t* mask, int B, int n, int b) {
+  MaskRow m;
+  m.rm = make_rsrc(mask, (uint32_t)B * (uint32_t)n);
+  m.row = (uint32_t)b * (uint32_t)n;
+  m.wide = (n & 15) == 0 && (reinterpret_cast<uintptr_t>(mask) & 15u) == 0;
+  return m;
+}
+
+// Bytes p0 .. p0 + 15 of the row (any beyond the row are masked by the caller).
+__device__ __forceinline__ u32x4 mask_chunk(const MaskRow& m, int p0) {
+  const uint32_t off = m.row + (uint32_t)p0;
+  if (m.wide) return __builtin_amdgcn_raw_buffer_load_b128(m.rm, off, 0, 0);
+  u32x4 x = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (p0 + e < n && mrow[p0 + e] == 2) bits |= 1u << e;
-  }
-  return bits;
+  for (int e = 0; e < 16; ++e)
+    x[e >> 2] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(m.rm, off + (uint32_t)e, 0, 0) << (8 * (e & 3));
+  return x;
+}
+
+// Bits of the chunk at p0 that lie in the row [0, n).
+__device__ __forceinline__ uint32_t chunk_in_row(int p0, int n) {
+  const int k = n - p0;
+  return k >= 16 ? 0xffffu : (k <= 0 ? 0u : (1u << k) - 1u);
+}
+
+// Bit e of the result: byte p0 + e of the row is 2 (p0 + e < n), for the
+// 16 bytes x at p0.  Most chunks hold no global token: the bit gather only
+// runs when some lane of the wave has one.
+__device__ __forceinline__ uint32_t twos16(const u32x4& x, int p0, int n) {
+  uint32_t f[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f[j] = twos_flags(x[j]);
+  const bool any = ((f[0] | f[1] | f[2] | f[3]) != 0u) && p0 < n;
+  if (!__any(any)) return 0u;
+  uint32_t bits = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bits |= gather_flags(f[j]) << (4 * j);
+  return bits & chunk_in_row(p0, n);
 }
 
 // Exclusive prefix sum over the wave of a per-lane count in [0, 31],
@@ -557,31 +593,26 @@ __device__ __forceinline__ int wave_prefix(int cnt) {
 
 // The scan's first round of mask loads (bytes [4096 u + 16 tid, +16) for
 // u < 4), issued before anything else so that they do not queue behind the
-// key and value loads.  Chunks that are out of range or unaligned are left
-// to the scan itself.
+// key and value loads.
 constexpr int kScanStep = kThreads * 16;
 struct ScanPre {
   u32x4 x[4];
-  uint32_t bits[4];  // twos16 of x, formed by scan_ready
+  uint32_t bits[4];  // bytes equal to 2, formed by scan_ready
 };
-__device__ __forceinline__ bool scan_chunk_ok(const int8_t* mrow, int p0, int n) {
-  return p0 + 16 <= n && ((reinterpret_cast<uintptr_t>(mrow) & 15u) == 0);
-}
-__device__ __forceinline__ void scan_preload(ScanPre& sp, const int8_t* __restrict__ mrow, int n) {
+__device__ __forceinline__ void scan_preload(ScanPre& sp, const MaskRow& m, int n) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int p0 = u * kScanStep + 16 * tid;
-    sp.x[u] = scan_chunk_ok(mrow, p0, n) ? *reinterpret_cast<const u32x4*>(mrow + p0) : u32x4{0u, 0u, 0u, 0u};
-  }
+  for (int u = 0; u < 4; ++u)
+    sp.x[u] = u * kScanStep < n ? mask_chunk(m, u * kScanStep + 16 * tid) : u32x4{0u, 0u, 0u, 0u};
 }
 
 // Turns the preloaded chunks into bitmasks in straight-line code, where the
 // compiler's count of loads in flight is exact (at the scan loop's entry it
 // would wait for every load, the key loads included).
-__device__ __forceinline__ void scan_ready(ScanPre& sp) {
+__device__ __forceinline__ void scan_ready(ScanPre& sp, int n) {
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) sp.bits[u] = twos16(sp.x[u]);
+  for (int u = 0; u < 4; ++u) sp.bits[u] = u * kScanStep < n ? twos16(sp.x[u], u * kScanStep + 16 * tid, n) : 0u;
 }
 
 // Ordered list of positions j with mask_row[j] == 2 into G (LDS), at most
@@ -589,18 +620,23 @@ __device__ __forceinline__ void scan_ready(ScanPre& sp) {
 // calls it and gets the same result.  Each thread looks at 16 bytes of each
 // 4 KB step; four steps are loaded together (the first four from sp) and
 // ranked with one barrier.
-__device__ __forceinline__ int scan_globals(const ScanPre& sp, const int8_t* __restrict__ mrow, int n, int* G,
-                                            int cap, int (*s_tot)[kWaves]) {
+__device__ __forceinline__ int scan_globals(const ScanPre& sp, const MaskRow& m, int n, int* G, int cap,
+                                            int (*s_tot)[kWaves]) {
   int total = 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
   for (int base = 0; base < n; base += 4 * kScanStep) {
     uint32_t bits[4];
+    if (base == 0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int p0 = base + u * kScanStep + 16 * tid;
-      bits[u] = (base == 0 && scan_chunk_ok(mrow, p0, n)) ? sp.bits[u] : match16(mrow, p0, n);
+      for (int u = 0; u < 4; ++u) bits[u] = sp.bits[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p0 = base + u * kScanStep + 16 * tid;
+        bits[u] = base + u * kScanStep < n ? twos16(mask_chunk(m, p0), p0, n) : 0u;
+      }
     }
     // (barriers without fences: the key loads already in flight are not
     // waited for here)
@@ -608,7 +644,7 @@ __device__ __forceinline__ int scan_globals(const ScanPre& sp, const int8_t* __r
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int cnt = __popc(bits[u]);
-      pre[u] = wave_prefix(cnt);
+      pre[u] = __any(cnt != 0) ? wave_prefix(cnt) : 0;
       if (lane == 63) s_tot[u][wv] = pre[u] + cnt;
     }
     lds_barrier();
@@ -1212,7 +1248,8 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
   src.wd = w * dil;
 
   ScanPre sp;
-  if (p.use_globals) scan_preload(sp, mrow, n);
+  const MaskRow mr = mask_row(p.mask, p.B, n, b);
+  if (p.use_globals) scan_preload(sp, mr, n);
   // Mask bytes of both halves' query rows (every wave sees the whole tile,
   // so the early-exit test below agrees across the workgroup).
   int qm[2];
@@ -1233,8 +1270,8 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
   loop.tab_commit(sh.ktab[wv]);
 
   if (p.use_globals) {
-    scan_ready(sp);
-    int nG = scan_globals(sp, mrow, n, sh.G, LF_MAX_GLOBAL, sh.wave_tmp);
+    scan_ready(sp, n);
+    int nG = scan_globals(sp, mr, n, sh.G, LF_MAX_GLOBAL, sh.wave_tmp);
     if (nG > p.max_global) {
       if (threadIdx.x == 0) atomicOr(p.status, LF_DEV_TOO_MANY_GLOBALS);
       nG = p.max_global;
@@ -1318,13 +1355,14 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
   HalfLoop<B16, ChunkSrc> loop(src, reinterpret_cast<const T*>(p.kg) + head,
                                reinterpret_cast<const T*>(p.vg) + head, rs, sh.buf + kp * Ly::kRingBytes, n, kp, qh);
   ScanPre sp;
-  scan_preload(sp, mrow, n);
+  const MaskRow mr = mask_row(p.mask, p.B, n, b);
+  scan_preload(sp, mr, n);
   loop.tab_load();
   loop.prime(nblk, [](int) { return true; });  // the split's keys do not depend on the scan
   loop.tab_commit(sh.ktab[wv]);
 
-  scan_ready(sp);
-  int nG = scan_globals(sp, mrow, n, sh.G, LF_MAX_GLOBAL, sh.wave_tmp);
+  scan_ready(sp, n);
+  int nG = scan_globals(sp, mr, n, sh.G, LF_MAX_GLOBAL, sh.wave_tmp);
   if (nG > p.max_global) {
     if (threadIdx.x == 0) atomicOr(p.status, LF_DEV_TOO_MANY_GLOBALS);
     nG = p.max_global;

@@ -96,6 +96,9 @@ SMALL = [
     dict(B=3, n=130, H=2, window=9, n_global=2, zero_frac=0.3),
     dict(B=1, n=700, H=2, window=64, dilation=[5, 7]),
     dict(B=1, n=96, H=1, window=3, global_positions=[0, 1, 2, 95]),
+    # global tokens in the last bytes of the mask, rows not a multiple of 16
+    dict(B=2, n=203, H=1, window=20, global_positions=[0, 190, 201, 202]),
+    dict(B=1, n=4100, H=1, window=32, global_positions=[5, 4096, 4099]),
 ]
 
 
