@@ -1163,6 +1163,89 @@ struct HalfLoop {
 };
 
 // ---------------------------------------------------------------------------
+// Global columns of local rows when a batch row holds at most kVecGlobals
+// global tokens.  Instead of a key block of their own (one more barrier
+// step for every wave of the tile, for a handful of keys), the parity-0
+// wave of each query half scores them after the block loop with dot
+// products on the vector unit.  Their K and V rows are staged in LDS by one
+// direct-to-LDS load during the prologue, in the unused tail of the global
+// list: 1 KB per query half, the K rows then the V rows, 128 B each.
+// ---------------------------------------------------------------------------
+constexpr int kVecGlobals = 4;
+
+__device__ __forceinline__ unsigned char* vec_rows(int* G, int qh) {
+  return reinterpret_cast<unsigned char*>(G + 16) + 1024 * qh;
+}
+
+// Lane l fetches 16-byte chunk l % 8 of the K (l < 32) or V (l >= 32) row of
+// global token (l / 8) % 4 (clamped to the last one); it lands at byte 16 l.
+__device__ __forceinline__ void issue_vec_rows(const __bf16* kb, const __bf16* vb, uint32_t rs, const int* G, int nG,
+                                               unsigned char* dst) {
+  const int l = lane_id_here();
+  const int key = min((l >> 3) & 3, nG - 1);
+  const __bf16* src = ((l >> 5) ? vb : kb) + (size_t)G[key] * rs + 8 * (l & 7);
+  __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)dst, 16, 0, 0);
+}
+
+// Folds the global tokens G[0 .. nG) into the running state of this lane's
+// query as extra keys, skipping those already in its window (they were
+// scored as window keys): the same online softmax as a block step, with the
+// probability rounded to bf16 as in P V.  Lanes l and l ^ 32 hold the two
+// halves of the query's head dims, and each adds its half of the products.
+__device__ void vec_global_columns(HalfState& st, const Frag<true>& qf, const BandSrc& src, const unsigned char* rows,
+                                   float c) {
+  const int lane = lane_id_here();
+  const int hh = lane >> 5;
+  const int tq = src.t0 + 32 * src.qh + (lane & 31);
+  const int qp = src.r + src.dil * (tq < src.n_r ? tq : src.n_r - 1);
+  const uint32_t span = 2u * (uint32_t)src.wd;
+  for (int gi = 0; gi < src.nG; ++gi) {
+    const int g = src.G[gi];
+    const unsigned char* kr = rows + 128 * gi;
+    const unsigned char* vr = rows + 512 + 128 * gi;
+    // q . k over this lane's 32 head dims (16 s + 8 hh + [0, 8))
+    float acc = 0.f;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const bf16x8 kk = *reinterpret_cast<const bf16x8*>(kr + 32 * s4 + 16 * hh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x2 a = {qf.x[s4][2 * j], qf.x[s4][2 * j + 1]};
+        const bf16x2 bb = {kk[2 * j], kk[2 * j + 1]};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(a, bb, acc, false);
+      }
+    }
+    const float sc = (acc + __shfl_xor(acc, 32)) * c;
+    const int d = qp - g;
+    const bool take = !((uint32_t)(d + src.wd) <= span && d % src.dil == 0);
+    if (__any(take && sc > st.m + kRescaleSlack)) {
+      const float mn = fmaxf(st.m, take ? sc : kNegInf);
+      const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
+      st.m = mn;
+      st.l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
+    }
+    const float pr = take ? (float)(__bf16)__builtin_amdgcn_exp2f(sc - st.m) : 0.f;
+    if (hh == 0) {
+      st.l += pr;
+      st.cnt += take ? 1 : 0;
+    }
+    // O^T element r of dim half db: head dim 32 db + 8 (r / 4) + 4 hh + r % 4
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const bf16x4 vv = *reinterpret_cast<const bf16x4*>(vr + 2 * (32 * db + 8 * g4 + 4 * hh));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.o[db][4 * g4 + i] = __builtin_fmaf(pr, (float)vv[i], st.o[db][4 * g4 + i]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Band workgroup: one tile of kTileQ = 64 query rows t0 .. t0 + 63 of the
 // residue sequence r of (b, h).  Its key blocks (window span, then the
 // global columns) alternate between the two key parities; each wave scores
@@ -1278,7 +1361,10 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
     }
     src.nG = __builtin_amdgcn_readfirstlane(nG);  // uniform (the status write above diverges)
   }
-  const int end = src.nwin + (src.nG + kBlockK - 1) / kBlockK;
+  // a few global tokens go to the vector unit after the loop, more of them
+  // into key blocks of their own
+  const bool vec_g = B16 && src.nG > 0 && src.nG <= kVecGlobals;
+  const int end = src.nwin + (vec_g ? 0 : (src.nG + kBlockK - 1) / kBlockK);
   // first blocks that are global-column blocks go after the scan
   loop.prime(end, [&](int i) { return i >= nwin; });
 
@@ -1301,6 +1387,13 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
   }
   const bool my_local = qh ? is_local[1] : is_local[0];
   const bool my_zero = qh ? is_zero[1] : is_zero[0];
+  const bool active = __any(my_local);
+  unsigned char* vrows = vec_rows(sh.G, qh);
+  if constexpr (B16) {
+    if (vec_g && kp == 0 && active)
+      issue_vec_rows(reinterpret_cast<const __bf16*>(p.k) + head, reinterpret_cast<const __bf16*>(p.v) + head, rs,
+                     sh.G, src.nG, vrows);
+  }
   if (!__any(is_local[0] || is_local[1])) {
     wait_vmem_all();  // the primed loads land before the workgroup's LDS is released
     if (my_zero) {
@@ -1313,7 +1406,10 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
 
   HalfState st;
   state_init(st);
-  loop.run(st, qf, end, p.c, __any(my_local));
+  loop.run(st, qf, end, p.c, active);
+  if constexpr (B16) {
+    if (vec_g && kp == 0 && active) vec_global_columns(st, qf, src, vrows, p.c);
+  }
   merge_parities<B16>(st, sh, qh, kp, [&](int db, float, float Lsum, int cnt, const float* o) {
     if (!my_local && !my_zero) return;
     const int qp = src.qpos();

@@ -99,6 +99,8 @@ SMALL = [
     # global tokens in the last bytes of the mask, rows not a multiple of 16
     dict(B=2, n=203, H=1, window=20, global_positions=[0, 190, 201, 202]),
     dict(B=1, n=4100, H=1, window=32, global_positions=[5, 4096, 4099]),
+    # four global tokens (the vector-unit path), some inside rows' windows, dilated heads
+    dict(B=2, n=500, H=2, window=30, dilation=[1, 3], global_positions=[0, 33, 250, 499], pad_tail=20),
 ]
 
 
