@@ -801,7 +801,9 @@ __device__ __forceinline__ void store_quadrant(elem_t<B16>* row, int db, int hh,
 // i < nwin have their key validity in the wave's table, blocks i >= nwin are
 // global-column blocks (band tiles only).  Each provides:
 //   kpos(i, row), exists(i, row)  token position (clamped) / existence of key row `row`
-//   dstep(), affine(i, p0&)       evenly spaced in-range blocks: positions p0 + dstep*row
+//   dstep(), affine_range(lo&, hi&, base&)
+//                                 blocks [lo, hi) are evenly spaced and in range: row r of
+//                                 block i is token base + dstep (32 i + r)
 //   classify(i, keymask)          0 empty, 1 masked per element, 2 full, for the wave's half
 //   valid_bits(i)                 this lane's rows c_r in its query's key set (classify 1)
 //   fast_range(lo&, hi&)          table blocks that are full wherever their keys are valid
@@ -820,9 +822,11 @@ struct ChunkSrc {
   }
   __device__ bool exists(int i, int row) const { return cbeg + kBlockK * i + row < cend; }
   __device__ int dstep() const { return 1; }
-  __device__ bool affine(int i, int& p0) const {
-    p0 = cbeg + kBlockK * i;
-    return p0 + kBlockK - 1 < cend;
+  // blocks [lo, hi) have all 32 rows in the chunk; block i starts at base + 32 i
+  __device__ void affine_range(int& lo, int& hi, int& base) const {
+    lo = 0;
+    hi = (cend - cbeg) / kBlockK;
+    base = cbeg;
   }
   __device__ int classify(int, uint32_t keymask) const { return keymask == 0xffffffffu ? 2 : 1; }
   __device__ uint32_t valid_bits(int) const { return 0xffffffffu; }
@@ -870,11 +874,14 @@ struct BandSrc {
     return kBlockK * (i - nwin) + row < nG;
   }
   __device__ int dstep() const { return dil; }
-  __device__ bool affine(int i, int& p0) const {
-    if (i >= nwin) return false;
-    const int k0 = key(i, 0);
-    p0 = r + dil * k0;
-    return k0 >= 0 && k0 + kBlockK - 1 < n_r;
+  // window blocks [lo, hi) have all 32 keys in [0, n_r); block i starts at
+  // token base + 32 dil i
+  __device__ void affine_range(int& lo, int& hi, int& base) const {
+    const int k0 = kbase + kBlockK * jlo;  // key of row 0 of block 0
+    lo = k0 >= 0 ? 0 : (-k0 + kBlockK - 1) / kBlockK;
+    const int top = n_r - kBlockK - k0;  // block i fits when 32 i <= top
+    hi = top < 0 ? 0 : min(nwin, top / kBlockK + 1);
+    base = r + dil * k0;
   }
   __device__ int classify(int i, uint32_t keymask) const {
     if (i >= nwin) return 1;  // global columns: masked against each row's window
@@ -977,12 +984,16 @@ struct HalfLoop {
   int tab_cnt;
   uint32_t full_keys;  // bit k: every key of table block kp + 2k is valid
   int fast_lo, fast_hi;
+  uint32_t fast_steps;  // bit s: the wave's block of step s is full for its half
+  // evenly spaced blocks [aff_lo, aff_hi): block i's rows start at byte
+  // so_base + i so_blk of each tensor
+  int aff_lo, aff_hi, so_base, so_blk;
   FragAddr fa;  // this lane's fragment read addresses in stage 0 (bf16)
 
   __device__ HalfLoop(const Src& s, const T* k, const T* v, uint32_t rs_, unsigned char* ring_, int n, int kp_,
                       int qh_)
       : src(s), kb(k), vb(v), rs(rs_), ring(ring_), lane(lane_id()), kp(kp_), qh(qh_), ktab(nullptr), tab_cnt(0),
-        full_keys(0), fast_lo(0), fast_hi(0) {
+        full_keys(0), fast_lo(0), fast_hi(0), fast_steps(0) {
     const uint32_t bytes = (uint32_t)(((size_t)(n - 1) * rs + kHeadDim) * sizeof(T));
     rk = make_rsrc(k, bytes);
     rv = make_rsrc(v, bytes);
@@ -994,6 +1005,10 @@ struct HalfLoop {
     vv = 2u * (row_off + 8u * (uint32_t)cv);
     if constexpr (B16) fa = frag_addr(ring, lane);
     src.fast_range(fast_lo, fast_hi);
+    int base;
+    src.affine_range(aff_lo, aff_hi, base);
+    so_base = base * (int)(2u * rs);
+    so_blk = kBlockK * src.dstep() * (int)(2u * rs);
   }
 
   // This wave's loads of block i into stage st (exactly kIssueLoads
@@ -1001,11 +1016,10 @@ struct HalfLoop {
   // waits count them).
   __device__ void issue(int i, int st) {
     unsigned char* dst = ring + st * L::kStageBytes;
-    int p0;
-    if (B16 && src.affine(i, p0)) {
+    if (B16 && i >= aff_lo && i < aff_hi) {
       // scalar offsets: wave-uniform by construction; readfirstlane keeps
       // them in SGPRs even where register pressure moved a term to a VGPR
-      const uint32_t so = (uint32_t)p0 * rs * 2u;
+      const uint32_t so = (uint32_t)(so_base + i * so_blk);
       const uint32_t step = (uint32_t)src.dstep() * (uint32_t)L::kRowsPerLoad * rs * 2u;
 #pragma unroll
       for (int u = 0; u < L::kHalfLoads; ++u) {
@@ -1062,20 +1076,21 @@ struct HalfLoop {
       full_keys |= ((uint32_t)(bits >> 32) == 0xffffffffu ? 1u : 0u) << (2 * p + 1);
     }
     ktab = tab;
-  }
-
-  __device__ bool is_fast(int i) const {
-    const int k = (i - kp) >> 1;
-    return i >= fast_lo && i < fast_hi && k < 32 && ((full_keys >> k) & 1u);
+    // steps k whose block kp + 2k lies in [fast_lo, fast_hi)
+    const int k_lo = max(fast_lo - kp + 1, 0) >> 1;
+    const int k_hi = max(fast_hi - kp + 1, 0) >> 1;
+    const uint32_t below_hi = k_hi >= 32 ? 0xffffffffu : ((1u << k_hi) - 1u);
+    const uint32_t below_lo = k_lo >= 32 ? 0xffffffffu : ((1u << k_lo) - 1u);
+    fast_steps = full_keys & below_hi & ~below_lo;
   }
 
   // Block i, staged in stage `stage` (landed and visible).
-  __device__ __forceinline__ void step(HalfState& st, const Frag<B16>& qf, int i, int stage, float c) {
+  __device__ __forceinline__ void step(HalfState& st, const Frag<B16>& qf, int i, int stage, float c, bool fast) {
     const unsigned char* cst = ring + stage * L::kStageBytes;
     Frag<B16> kf;
     VtFrag<B16> vt;
     f32x16 s;
-    if (is_fast(i)) {
+    if (fast) {
       // every key of the block is scored for every query of the half
       read_frags(kf, vt, fa, cst, stage);
       const f32x16 zero = {};
@@ -1156,7 +1171,7 @@ struct HalfLoop {
       block_barrier();
       const int nxt = i + 2 * (L::kStages - 1);
       if (nxt < end) issue(nxt, stage == 0 ? L::kStages - 1 : stage - 1);
-      if (active && i < end) step(st, qf, i, stage, c);
+      if (active && i < end) step(st, qf, i, stage, c, s < 32 && ((fast_steps >> s) & 1u));
       stage = stage == L::kStages - 1 ? 0 : stage + 1;
     }
   }
