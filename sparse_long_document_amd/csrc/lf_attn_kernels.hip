@@ -1421,7 +1421,9 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
 
   HalfState st;
   state_init(st);
+  __builtin_amdgcn_s_setprio(0);
   loop.run(st, qf, end, p.c, active);
+  __builtin_amdgcn_s_setprio(2);
   if constexpr (B16) {
     if (vec_g && kp == 0 && active) vec_global_columns(st, qf, src, vrows, p.c);
   }
@@ -1493,7 +1495,9 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
     load_frag(qf, qg + (size_t)sh.G[gi < nG ? gi : nG - 1] * rs, hh);
     HalfState st;
     state_init(st);
+    __builtin_amdgcn_s_setprio(0);
     loop.run(st, qf, nblk, c, g0 + 32 * qh < nG);
+    __builtin_amdgcn_s_setprio(2);
     merge_parities<B16>(st, sh, qh, kp, [&](int db, float M, float Lsum, int cnt, const float* o) {
       if (gi >= nG) return;
       float* rec = part_bh + ((size_t)gi * S + cidx) * kPartialStride;
@@ -1577,6 +1581,11 @@ template <bool B16>
 __device__ __forceinline__ void fwd_body(const KernelParams& p) {
   __shared__ Shared<B16> sh;
   const int bid = blockIdx.x;
+  // Prologues and epilogues are chains of dependent loads, scans and
+  // barriers; they run at a raised wave priority so that a workgroup that
+  // starts next to others already in their block loops gets through them
+  // quickly.  The block loops run at normal priority.
+  __builtin_amdgcn_s_setprio(2);
   if (bid < p.n_glob) {
     global_split<B16>(p, bid, sh);  // first: their merge waits for the last split
     return;
