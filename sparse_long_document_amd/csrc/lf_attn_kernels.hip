@@ -1365,23 +1365,6 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
   loop.tab_load();
   const int nwin = src.nwin;
   loop.prime(nwin, [](int) { return true; });
-  loop.tab_commit(sh.ktab[wv]);
-
-  if (p.use_globals) {
-    scan_ready(sp, n);
-    int nG = scan_globals(sp, mr, n, sh.G, LF_MAX_GLOBAL, sh.wave_tmp);
-    if (nG > p.max_global) {
-      if (threadIdx.x == 0) atomicOr(p.status, LF_DEV_TOO_MANY_GLOBALS);
-      nG = p.max_global;
-    }
-    src.nG = __builtin_amdgcn_readfirstlane(nG);  // uniform (the status write above diverges)
-  }
-  // a few global tokens go to the vector unit after the loop, more of them
-  // into key blocks of their own
-  const bool vec_g = B16 && src.nG > 0 && src.nG <= kVecGlobals;
-  const int end = src.nwin + (vec_g ? 0 : (src.nG + kBlockK - 1) / kBlockK);
-  // first blocks that are global-column blocks go after the scan
-  loop.prime(end, [&](int i) { return i >= nwin; });
 
   bool is_local[2], is_zero[2];
 #pragma unroll
@@ -1402,13 +1385,8 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
   }
   const bool my_local = qh ? is_local[1] : is_local[0];
   const bool my_zero = qh ? is_zero[1] : is_zero[0];
-  const bool active = __any(my_local);
-  unsigned char* vrows = vec_rows(sh.G, qh);
-  if constexpr (B16) {
-    if (vec_g && kp == 0 && active)
-      issue_vec_rows(reinterpret_cast<const __bf16*>(p.k) + head, reinterpret_cast<const __bf16*>(p.v) + head, rs,
-                     sh.G, src.nG, vrows);
-  }
+  // a tile with no local row (padding, or only global rows) writes its
+  // zero rows and stops here, before the table and the global scan
   if (!__any(is_local[0] || is_local[1])) {
     wait_vmem_all();  // the primed loads land before the workgroup's LDS is released
     if (my_zero) {
@@ -1417,6 +1395,32 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
       if (p.row_nnz && kp == 0 && hh == 0) p.row_nnz[((size_t)b * p.H + h) * n + qp] = 0;
     }
     return;
+  }
+
+  loop.tab_commit(sh.ktab[wv]);
+
+  if (p.use_globals) {
+    scan_ready(sp, n);
+    int nG = scan_globals(sp, mr, n, sh.G, LF_MAX_GLOBAL, sh.wave_tmp);
+    if (nG > p.max_global) {
+      if (threadIdx.x == 0) atomicOr(p.status, LF_DEV_TOO_MANY_GLOBALS);
+      nG = p.max_global;
+    }
+    src.nG = __builtin_amdgcn_readfirstlane(nG);  // uniform (the status write above diverges)
+  }
+  // a few global tokens go to the vector unit after the loop, more of them
+  // into key blocks of their own
+  const bool vec_g = B16 && src.nG > 0 && src.nG <= kVecGlobals;
+  const int end = src.nwin + (vec_g ? 0 : (src.nG + kBlockK - 1) / kBlockK);
+  // first blocks that are global-column blocks go after the scan
+  loop.prime(end, [&](int i) { return i >= nwin; });
+
+  const bool active = __any(my_local);
+  unsigned char* vrows = vec_rows(sh.G, qh);
+  if constexpr (B16) {
+    if (vec_g && kp == 0 && active)
+      issue_vec_rows(reinterpret_cast<const __bf16*>(p.k) + head, reinterpret_cast<const __bf16*>(p.v) + head, rs,
+                     sh.G, src.nG, vrows);
   }
 
   HalfState st;
