@@ -672,10 +672,10 @@ __device__ __forceinline__ int scan_globals(const ScanPre& sp, const MaskRow& m,
   return __builtin_amdgcn_readfirstlane(total);  // the same in every lane
 }
 
-// Partial state of one wave parked in LDS for the merge: O^T as
-// [db][g][lane] f32x4, then per query (lane % 32) the reference max, the
-// row sum and the key count.
-constexpr int kParkOBytes = 2 * 4 * 64 * 16;
+// Partial state of one wave parked in LDS for the merge: the head-dim half
+// of O^T that the partner wave emits, as [g][lane] f32x4, then per query
+// (lane % 32) the reference max, the row sum and the key count.
+constexpr int kParkOBytes = 4 * 64 * 16;
 constexpr int kParkBytes = kParkOBytes + 3 * 32 * 4;
 
 template <bool B16>
@@ -690,26 +690,25 @@ struct Shared {
 };
 
 // The two waves of query half qh (key parities 0 and 1) hold partial
-// results for the same 32 queries over disjoint key subsets.  Every wave
-// parks its state (after a barrier: the rings it overwrites are no longer
-// read), and after a second barrier wave (qh, kp) merges head-dim half
-// db = kp of both partials and passes, per lane, the merged max M (log2
-// domain), row sum L, key count and the 16 unnormalised outputs of head
-// dims 32db + 8g + 4(lane/32) + i (in o[4g + i]) to emit(db, M, L, cnt, o).
+// results for the same 32 queries over disjoint key subsets; wave (qh, kp)
+// emits head-dim half db = kp.  Every wave parks the half its partner
+// emits with its (m, l, count) (after a barrier: the rings it overwrites
+// are no longer read), and after a second barrier combines its own half
+// with the partner's parked one.  It passes, per lane, the merged max M
+// (log2 domain), row sum L, key count and the 16 unnormalised outputs of
+// head dims 32db + 8g + 4(lane/32) + i (in o[4g + i]) to
+// emit(db, M, L, cnt, o).  Both waves of a row form M, L and the outputs
+// with parity 0's terms first, so the row's two halves share one L.
 template <bool B16, class Emit>
 __device__ void merge_parities(const HalfState& st, Shared<B16>& sh, int qh, int kp, Emit emit) {
   const int lane = lane_id();
   const int hh = lane >> 5;
-  const int wv = 2 * kp + qh;
   __syncthreads();
-  unsigned char* mine = sh.buf + wv * kParkBytes;
+  unsigned char* mine = sh.buf + (2 * kp + qh) * kParkBytes;
   f32x4* po = reinterpret_cast<f32x4*>(mine);
+  const f32x16& give = kp ? st.o[0] : st.o[1];
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      po[(db * 4 + g) * 64 + lane] =
-          f32x4{st.o[db][4 * g], st.o[db][4 * g + 1], st.o[db][4 * g + 2], st.o[db][4 * g + 3]};
+  for (int g = 0; g < 4; ++g) po[g * 64 + lane] = f32x4{give[4 * g], give[4 * g + 1], give[4 * g + 2], give[4 * g + 3]};
   const float l = st.l + __shfl_xor(st.l, 32);
   const int cnt = st.cnt + __shfl_xor(st.cnt, 32);
   float* pm = reinterpret_cast<float*>(mine + kParkOBytes);
@@ -719,28 +718,32 @@ __device__ void merge_parities(const HalfState& st, Shared<B16>& sh, int qh, int
     reinterpret_cast<int*>(pm + 64)[lane] = cnt;
   }
   __syncthreads();
-  const int db = kp;
   const int q = lane & 31;
-  const unsigned char* pa = sh.buf + qh * kParkBytes;
-  const unsigned char* pb = sh.buf + (2 + qh) * kParkBytes;
-  const float* ma = reinterpret_cast<const float*>(pa + kParkOBytes);
-  const float* mb = reinterpret_cast<const float*>(pb + kParkOBytes);
-  const float M = fmaxf(ma[q], mb[q]);
-  const float fa = __builtin_amdgcn_exp2f(ma[q] - M);
-  const float fb = __builtin_amdgcn_exp2f(mb[q] - M);
-  const float Lsum = ma[32 + q] * fa + mb[32 + q] * fb;
-  const int c = reinterpret_cast<const int*>(ma + 64)[q] + reinterpret_cast<const int*>(mb + 64)[q];
+  const unsigned char* pp = sh.buf + (2 * (1 - kp) + qh) * kParkBytes;
+  const float* mp = reinterpret_cast<const float*>(pp + kParkOBytes);
+  const float m_p = mp[q], l_p = mp[32 + q];
+  const int c = cnt + reinterpret_cast<const int*>(mp + 64)[q];
+  // parity 0's terms are "a", parity 1's "b"
+  const float ma = kp ? m_p : st.m, mb = kp ? st.m : m_p;
+  const float la = kp ? l_p : l, lb = kp ? l : l_p;
+  const float M = fmaxf(ma, mb);
+  const float fa = __builtin_amdgcn_exp2f(ma - M);
+  const float fb = __builtin_amdgcn_exp2f(mb - M);
+  const float Lsum = la * fa + lb * fb;
+  const float f_own = kp ? fb : fa, f_p = kp ? fa : fb;
+  const f32x16& own = kp ? st.o[1] : st.o[0];
+  const f32x4* op = reinterpret_cast<const f32x4*>(pp);
   float o[16];
-  const f32x4* oa = reinterpret_cast<const f32x4*>(pa);
-  const f32x4* ob = reinterpret_cast<const f32x4*>(pb);
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const f32x4 x = oa[(db * 4 + g) * 64 + lane];
-    const f32x4 y = ob[(db * 4 + g) * 64 + lane];
+    const f32x4 y = op[g * 64 + lane];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[4 * g + i] = __builtin_fmaf(x[i], fa, y[i] * fb);
+    for (int i = 0; i < 4; ++i) {
+      const float xo = own[4 * g + i];
+      o[4 * g + i] = kp ? __builtin_fmaf(y[i], f_p, xo * f_own) : __builtin_fmaf(xo, f_own, y[i] * f_p);
+    }
   }
-  emit(db, M, Lsum, c, o);
+  emit(kp, M, Lsum, c, o);
 }
 
 template <bool B16>
@@ -1153,27 +1156,44 @@ struct HalfLoop {
     }
   }
 
+  // Step s over block i = 2 s + kp (skipped when i >= end), in `stage`.
+  __device__ __forceinline__ void one_step(HalfState& st, const Frag<B16>& qf, int s, int& stage, int end, float c,
+                                           bool active) {
+    const int i = 2 * s + kp;
+    // this wave's share of block i has landed (the next block's may still fly)
+    if (L::kStages > 2 && i + 2 < end)
+      wait_vmem_but<kIssueLoads>();
+    else
+      wait_vmem_all();
+    // ... and the other wave's share too; both waves are done reading the
+    // stage of step s - 1, which the next issue refills
+    block_barrier();
+    const int nxt = i + 2 * (L::kStages - 1);
+    if (nxt < end) issue(nxt, stage == 0 ? L::kStages - 1 : stage - 1);
+    if (active && i < end) step(st, qf, i, stage, c, s < 32 && ((fast_steps >> s) & 1u));
+    stage = stage == L::kStages - 1 ? 0 : stage + 1;
+  }
+
   // Steps over blocks 2 s + kp < end; the blocks of steps 0 .. kStages - 2
   // are already issued.  `active`: the wave has rows to score (otherwise it
   // only keeps its share of the loads and the barriers going).
   __device__ void run(HalfState& st, const Frag<B16>& qf, int end, float c, bool active) {
     const int nsteps = (end + 1) >> 1;
     int stage = 0;
-    for (int s = 0; s < nsteps; ++s) {
-      const int i = 2 * s + kp;
-      // this wave's share of block i has landed (the next block's may still fly)
-      if (L::kStages > 2 && i + 2 < end)
-        wait_vmem_but<kIssueLoads>();
-      else
-        wait_vmem_all();
-      // ... and the other wave's share too; both waves are done reading the
-      // stage of step s - 1, which the next issue refills
-      block_barrier();
-      const int nxt = i + 2 * (L::kStages - 1);
-      if (nxt < end) issue(nxt, stage == 0 ? L::kStages - 1 : stage - 1);
-      if (active && i < end) step(st, qf, i, stage, c, s < 32 && ((fast_steps >> s) & 1u));
-      stage = stage == L::kStages - 1 ? 0 : stage + 1;
-    }
+    for (int s = 0; s < nsteps; ++s) one_step(st, qf, s, stage, end, c, active);
+  }
+
+  // The same with after_first run in every wave once the first step is done
+  // (outside the loop, so that what it uses is not held through it); it may
+  // raise end, and the blocks it adds must have indices of at least
+  // kp + 2 kStages, so that later steps issue them.
+  template <class Hook>
+  __device__ void run(HalfState& st, const Frag<B16>& qf, int end, float c, bool active, Hook after_first) {
+    int stage = 0;
+    one_step(st, qf, 0, stage, end, c, active);
+    after_first(end);
+    const int nsteps = (end + 1) >> 1;
+    for (int s = 1; s < nsteps; ++s) one_step(st, qf, s, stage, end, c, active);
   }
 };
 
@@ -1399,34 +1419,52 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
 
   loop.tab_commit(sh.ktab[wv]);
 
-  if (p.use_globals) {
-    scan_ready(sp, n);
+  const bool active = __any(my_local);
+  unsigned char* vrows = vec_rows(sh.G, qh);
+  bool vec_g = false;
+  // The global list: the scan, then the global-column work it implies.  A
+  // few global tokens go to the vector unit after the loop (their K and V
+  // rows are staged now), more of them into key blocks of their own after
+  // the window blocks.  Returns the block count.
+  auto globals = [&]() -> int {
     int nG = scan_globals(sp, mr, n, sh.G, LF_MAX_GLOBAL, sh.wave_tmp);
     if (nG > p.max_global) {
       if (threadIdx.x == 0) atomicOr(p.status, LF_DEV_TOO_MANY_GLOBALS);
       nG = p.max_global;
     }
     src.nG = __builtin_amdgcn_readfirstlane(nG);  // uniform (the status write above diverges)
-  }
-  // a few global tokens go to the vector unit after the loop, more of them
-  // into key blocks of their own
-  const bool vec_g = B16 && src.nG > 0 && src.nG <= kVecGlobals;
-  const int end = src.nwin + (vec_g ? 0 : (src.nG + kBlockK - 1) / kBlockK);
-  // first blocks that are global-column blocks go after the scan
-  loop.prime(end, [&](int i) { return i >= nwin; });
-
-  const bool active = __any(my_local);
-  unsigned char* vrows = vec_rows(sh.G, qh);
-  if constexpr (B16) {
-    if (vec_g && kp == 0 && active)
-      issue_vec_rows(reinterpret_cast<const __bf16*>(p.k) + head, reinterpret_cast<const __bf16*>(p.v) + head, rs,
-                     sh.G, src.nG, vrows);
+    vec_g = B16 && src.nG > 0 && src.nG <= kVecGlobals;
+    if constexpr (B16) {
+      if (vec_g && kp == 0 && active)
+        issue_vec_rows(reinterpret_cast<const __bf16*>(p.k) + head, reinterpret_cast<const __bf16*>(p.v) + head, rs,
+                       sh.G, src.nG, vrows);
+    }
+    return nwin + (vec_g ? 0 : (src.nG + kBlockK - 1) / kBlockK);
+  };
+  // With enough window blocks the scan runs after the first block step (its
+  // mask bytes have landed by then, and the next blocks' loads fly during
+  // it): no global-column block is due before the third step.
+  const bool late_scan = p.use_globals && nwin >= 2 * Ly::kStages;
+  if (p.use_globals) scan_ready(sp, n);
+  int end = nwin;
+  if (p.use_globals && !late_scan) {
+    end = globals();
+    // first blocks that are global-column blocks go after the scan
+    loop.prime(end, [&](int i) { return i >= nwin; });
   }
 
   HalfState st;
   state_init(st);
   __builtin_amdgcn_s_setprio(0);
-  loop.run(st, qf, end, p.c, active);
+  if (late_scan) {
+    loop.run(st, qf, end, p.c, active, [&](int& e) {
+      __builtin_amdgcn_s_setprio(2);
+      e = globals();
+      __builtin_amdgcn_s_setprio(0);
+    });
+  } else {
+    loop.run(st, qf, end, p.c, active);
+  }
   __builtin_amdgcn_s_setprio(2);
   if constexpr (B16) {
     if (vec_g && kp == 0 && active) vec_global_columns(st, qf, src, vrows, p.c);
