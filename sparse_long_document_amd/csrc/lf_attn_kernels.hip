@@ -195,13 +195,13 @@ __host__ __device__ constexpr int acc_c(int r) { return 8 * (r >> 2) + (r & 3); 
 // always a valid position (rows outside the key set are clamped here and
 // masked later).  Lane l of load t fetches chunk (l % kChunks) ^ swz(row)
 // of row kRowsPerLoad*t + l / kChunks; it lands at byte 1024t + 16l.
-template <bool B16, class KPos>
+template <bool B16, int kN, class KPos>
 __device__ __forceinline__ void issue_rows(const elem_t<B16>* kb, const elem_t<B16>* vb, uint32_t rs, KPos kpos,
                                            unsigned char* stage, int lane, int t0) {
   using L = Lay<B16>;
   constexpr int kEltPerChunk = 16 / L::kElt;
 #pragma unroll
-  for (int u = 0; u < L::kHalfLoads; ++u) {
+  for (int u = 0; u < kN; ++u) {
     const int t = t0 + u;
     const int row = L::kRowsPerLoad * t + lane / L::kChunks;
     const int c = lane % L::kChunks;
@@ -384,7 +384,8 @@ __device__ __forceinline__ int bit_as_mask(uint32_t x) {
 // 1 where u > span, else 0: med3(u, span, span + 1) - span (span < 2^32 - 1).
 __device__ __forceinline__ uint32_t above_span(uint32_t u, uint32_t span) {
   uint32_t m;
-  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(m) : "v"(u), "s"(span), "v"(span + 1u));  // one scalar operand per VALU op
+  const uint32_t sspan = __builtin_amdgcn_readfirstlane(span);  // uniform: the asm takes it from an SGPR
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(m) : "v"(u), "s"(sspan), "v"(span + 1u));  // one scalar operand per VALU op
   return m - span;
 }
 
@@ -943,7 +944,7 @@ struct BandSrc {
         // the divisor passes through an empty asm so that the division's
         // setup is redone here instead of being hoisted out of the block loop
         // and held in a register through every block
-        int d = dil;
+        int d = __builtin_amdgcn_readfirstlane(dil);
         asm volatile("" : "+s"(d));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -962,12 +963,17 @@ struct BandSrc {
 // step s handling block 2 s + kp from stage s % kStages of the parity's
 // ring.  Every wave of the workgroup runs the same number of steps (one
 // barrier each), whether or not it has a block or rows to score.
+//
+// Solo (a run-time choice, uniform): the wave owns its blocks i = kp,
+// kp + 4, ... (kp is then the wave index) and one stage of its own, loads
+// each block whole and needs no barrier (run_solo).
 // ---------------------------------------------------------------------------
 template <bool B16, class Src>
 struct HalfLoop {
   using T = elem_t<B16>;
   using L = Lay<B16>;
-  // vector-memory instructions one issue() emits (K and V rows)
+  // vector-memory instructions one issue() emits (K and V rows), shared
+  // with the other wave of the parity
   static constexpr int kIssueLoads = 2 * L::kHalfLoads;
   static constexpr int kTabPairs = 12;
   const Src& src;
@@ -976,6 +982,8 @@ struct HalfLoop {
   uint32_t rs;
   unsigned char* ring;
   int lane, kp, qh;
+  bool solo;
+  int lg;  // log2 of the block index step between this wave's blocks (1, or 2 solo)
   // buffer resources and per-lane offsets of the evenly spaced (affine) path
   __amdgpu_buffer_rsrc_t rk, rv;
   uint32_t vk0, vk1, vv;
@@ -994,9 +1002,9 @@ struct HalfLoop {
   FragAddr fa;  // this lane's fragment read addresses in stage 0 (bf16)
 
   __device__ HalfLoop(const Src& s, const T* k, const T* v, uint32_t rs_, unsigned char* ring_, int n, int kp_,
-                      int qh_)
-      : src(s), kb(k), vb(v), rs(rs_), ring(ring_), lane(lane_id()), kp(kp_), qh(qh_), ktab(nullptr), tab_cnt(0),
-        full_keys(0), fast_lo(0), fast_hi(0), fast_steps(0) {
+                      int qh_, bool solo_ = false)
+      : src(s), kb(k), vb(v), rs(rs_), ring(ring_), lane(lane_id()), kp(kp_), qh(qh_), solo(solo_), lg(solo_ ? 2 : 1),
+        ktab(nullptr), tab_cnt(0), full_keys(0), fast_lo(0), fast_hi(0), fast_steps(0) {
     const uint32_t bytes = (uint32_t)(((size_t)(n - 1) * rs + kHeadDim) * sizeof(T));
     rk = make_rsrc(k, bytes);
     rv = make_rsrc(v, bytes);
@@ -1025,10 +1033,11 @@ struct HalfLoop {
       const uint32_t so = (uint32_t)(so_base + i * so_blk);
       const uint32_t step = (uint32_t)src.dstep() * (uint32_t)L::kRowsPerLoad * rs * 2u;
 #pragma unroll
-      for (int u = 0; u < L::kHalfLoads; ++u) {
-        const int t = qh * L::kHalfLoads + u;
+      for (int u = 0; u < 2 * L::kHalfLoads; ++u) {
+        if (u >= L::kHalfLoads && !solo) break;
+        const int t = (solo ? 0 : qh * L::kHalfLoads) + u;
         const uint32_t sot = __builtin_amdgcn_readfirstlane(so + t * step);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)(dst + 1024 * t), 16, (u & 1) ? vk1 : vk0, sot,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)(dst + 1024 * t), 16, (t & 1) ? vk1 : vk0, sot,
                                                  0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS_AS void*)(dst + L::kBlockBytes + 1024 * t), 16, vv, sot,
                                                  0, 0);
@@ -1036,7 +1045,11 @@ struct HalfLoop {
     } else {
       // lane-derived terms recomputed here (a rare path) rather than hoisted
       // out of the block loop and held in registers
-      issue_rows<B16>(kb, vb, rs, [&](int r) { return src.kpos(i, r); }, dst, lane_id_here(), qh * L::kHalfLoads);
+      if (solo)
+        issue_rows<B16, 2 * L::kHalfLoads>(kb, vb, rs, [&](int r) { return src.kpos(i, r); }, dst, lane_id_here(), 0);
+      else
+        issue_rows<B16, L::kHalfLoads>(kb, vb, rs, [&](int r) { return src.kpos(i, r); }, dst, lane_id_here(),
+                                       qh * L::kHalfLoads);
     }
   }
 
@@ -1053,14 +1066,14 @@ struct HalfLoop {
   // issued its first K/V loads, turns them into bits.  Sources with more
   // than 2 kTabPairs table blocks per wave go without the table.
   __device__ void tab_load() {
-    tab_cnt = kp < src.nwin ? (src.nwin - kp + 1) >> 1 : 0;
+    tab_cnt = kp < src.nwin ? (src.nwin - kp + (1 << lg) - 1) >> lg : 0;
     if (tab_cnt > 2 * kTabPairs) return;
     const int row = lane & 31, half = lane >> 5;
 #pragma unroll
     for (int p = 0; p < kTabPairs; ++p) {
       if (2 * p >= tab_cnt) break;
       const int k = 2 * p + half;
-      const int i = kp + 2 * k;
+      const int i = kp + (k << lg);
       const bool ok = k < tab_cnt && src.exists(i, row);
       tabv[p] = ok ? (int)src.mrow[src.kpos(i, row)] : 0;
     }
@@ -1079,9 +1092,9 @@ struct HalfLoop {
       full_keys |= ((uint32_t)(bits >> 32) == 0xffffffffu ? 1u : 0u) << (2 * p + 1);
     }
     ktab = tab;
-    // steps k whose block kp + 2k lies in [fast_lo, fast_hi)
-    const int k_lo = max(fast_lo - kp + 1, 0) >> 1;
-    const int k_hi = max(fast_hi - kp + 1, 0) >> 1;
+    // steps k whose block kp + (k << lg) lies in [fast_lo, fast_hi)
+    const int k_lo = max(fast_lo - kp + (1 << lg) - 1, 0) >> lg;
+    const int k_hi = max(fast_hi - kp + (1 << lg) - 1, 0) >> lg;
     const uint32_t below_hi = k_hi >= 32 ? 0xffffffffu : ((1u << k_hi) - 1u);
     const uint32_t below_lo = k_lo >= 32 ? 0xffffffffu : ((1u << k_lo) - 1u);
     fast_steps = full_keys & below_hi & ~below_lo;
@@ -1106,7 +1119,7 @@ struct HalfLoop {
         const int left = src.nG - kBlockK * (i - src.nwin);
         keymask = left >= kBlockK ? 0xffffffffu : ((1u << left) - 1u);
       } else if (ktab) {
-        keymask = ktab[(i - kp) >> 1];
+        keymask = ktab[(i - kp) >> lg];
       } else {
         keymask = table_keymask(i);  // waits for every outstanding load: wide windows only
       }
@@ -1151,7 +1164,7 @@ struct HalfLoop {
   __device__ void prime(int end, Pred pred) {
 #pragma unroll
     for (int s = 0; s < L::kStages - 1; ++s) {
-      const int i = 2 * s + kp;
+      const int i = (s << lg) + kp;
       if (i < end && pred(i)) issue(i, s);
     }
   }
@@ -1194,6 +1207,19 @@ struct HalfLoop {
     after_first(end);
     const int nsteps = (end + 1) >> 1;
     for (int s = 1; s < nsteps; ++s) one_step(st, qf, s, stage, end, c, active);
+  }
+
+  // Solo: this wave's blocks kp, kp + 4, ... < end through its one stage;
+  // its first block is already issued.  A block's fragments are read (and
+  // the reads waited for) inside step(), so the next block can be issued
+  // into the same stage right after it.
+  __device__ void run_solo(HalfState& st, const Frag<B16>& qf, int end, float c, bool active) {
+    for (int s = 0; kp + 4 * s < end; ++s) {
+      const int i = kp + 4 * s;
+      wait_vmem_all();
+      if (active) step(st, qf, i, 0, c, s < 32 && ((fast_steps >> s) & 1u));
+      if (i + 4 < end) issue(i + 4, 0);
+    }
   }
 };
 
@@ -1477,9 +1503,72 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
   });
 }
 
+// Partial record of one (global token, split): merged max, row sum, key
+// count, then the unnormalised outputs; this lane writes head dims
+// 32 db + 8 g + 4 hh + e from o[4 g + e].
+__device__ __forceinline__ void write_record(float* rec, int db, int hh, float M, float Lsum, int cnt,
+                                             const float* o) {
+  if (db == 0 && hh == 0) {
+    st_agent(rec, M);
+    st_agent(rec + 1, Lsum);
+    st_agent(rec + 2, __builtin_bit_cast(float, cnt));
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st_agent(rec + 4 + 32 * db + 8 * g + 4 * hh + e, o[4 * g + e]);
+}
+
+// Second merge round of a solo split (below): waves (0, kp) and (1, kp)
+// hold merged results of head-dim half kp for the same query slots over
+// disjoint key sets.  Wave (1, kp) parks its (M, L, count, outputs) past
+// the first round's parked states; after a barrier wave (0, kp) combines,
+// its own terms first, and passes the result to emit(M, L, cnt, o).
+constexpr int kRound2Off = kWaves * kParkBytes;
+
+template <bool B16, class Emit>
+__device__ void merge_halves(Shared<B16>& sh, int qh, int kp, float M, float L, int cnt, const float* o, Emit emit) {
+  static_assert(kRound2Off + 2 * kParkBytes <= Shared<B16>::kBufBytes, "second-round park fits the buffer");
+  const int lane = lane_id();
+  const int q = lane & 31;
+  unsigned char* r2 = sh.buf + kRound2Off + kp * kParkBytes;
+  f32x4* po = reinterpret_cast<f32x4*>(r2);
+  float* pm = reinterpret_cast<float*>(r2 + kParkOBytes);
+  if (qh == 1) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) po[g * 64 + lane] = f32x4{o[4 * g], o[4 * g + 1], o[4 * g + 2], o[4 * g + 3]};
+    if ((lane >> 5) == 0) {
+      pm[lane] = M;
+      pm[32 + lane] = L;
+      reinterpret_cast<int*>(pm + 64)[lane] = cnt;
+    }
+  }
+  __syncthreads();
+  if (qh == 1) return;
+  const float mb = pm[q], lb = pm[32 + q];
+  const int c = cnt + reinterpret_cast<const int*>(pm + 64)[q];
+  const float Mm = fmaxf(M, mb);
+  const float fa = __builtin_amdgcn_exp2f(M - Mm);
+  const float fb = __builtin_amdgcn_exp2f(mb - Mm);
+  const float Lm = L * fa + lb * fb;
+  float om[16];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 y = po[g * 64 + lane];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) om[4 * g + e] = __builtin_fmaf(o[4 * g + e], fa, y[e] * fb);
+  }
+  emit(Mm, Lm, c, om);
+}
+
 // ---------------------------------------------------------------------------
 // Global-row workgroup: split c of (b, h); all global tokens of b, 64 at a
-// time (two query halves).
+// time (two query halves).  When a batch row holds at most 32 global tokens
+// (one query half) the split runs solo: all four waves score the same 32
+// query slots, each over its own quarter of the split's blocks (blocks w,
+// w + 4, ...) in an 8 KB stage of its own.  The split's work then spreads
+// over the four SIMDs instead of two, and its loop needs no barrier; the
+// four partials are merged in two rounds (key parities, then the halves).
 // ---------------------------------------------------------------------------
 template <bool B16>
 __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
@@ -1507,10 +1596,16 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
   src.nwin = (src.cend - src.cbeg + kBlockK - 1) / kBlockK;
   src.nG = 0;
   const int nblk = src.nwin;
-  HalfLoop<B16, ChunkSrc> loop(src, reinterpret_cast<const T*>(p.kg) + head,
-                               reinterpret_cast<const T*>(p.vg) + head, rs, sh.buf + kp * Ly::kRingBytes, n, kp, qh);
+  const float c = p.c;
+  float* part_bh = p.partials + (size_t)bh * p.max_global * S * kPartialStride;
   ScanPre sp;
   const MaskRow mr = mask_row(p.mask, p.B, n, b);
+  // solo split: one query half of slots, four owners of blocks
+  const bool solo = B16 && p.max_global <= 32;
+  HalfLoop<B16, ChunkSrc> loop(src, reinterpret_cast<const T*>(p.kg) + head,
+                               reinterpret_cast<const T*>(p.vg) + head, rs,
+                               solo ? sh.buf + wv * Ly::kStageBytes : sh.buf + kp * Ly::kRingBytes, n, solo ? wv : kp,
+                               qh, solo);
   scan_preload(sp, mr, n);
   loop.tab_load();
   loop.prime(nblk, [](int) { return true; });  // the split's keys do not depend on the scan
@@ -1527,33 +1622,44 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
     wait_vmem_all();
     return;
   }
-  const float c = p.c;
-  float* part_bh = p.partials + (size_t)bh * p.max_global * S * kPartialStride;
 
-  for (int g0 = 0; g0 < nG; g0 += kTileQ) {
-    if (g0 > 0) loop.prime(nblk, [](int) { return true; });  // after the previous group's last barrier
-    const int gi = g0 + 32 * qh + (lane & 31);
+  if (solo) {
+    const int gi = lane & 31;
     Frag<B16> qf;
     load_frag(qf, qg + (size_t)sh.G[gi < nG ? gi : nG - 1] * rs, hh);
     HalfState st;
     state_init(st);
     __builtin_amdgcn_s_setprio(0);
-    loop.run(st, qf, nblk, c, g0 + 32 * qh < nG);
+    loop.run_solo(st, qf, nblk, c, true);
     __builtin_amdgcn_s_setprio(2);
-    merge_parities<B16>(st, sh, qh, kp, [&](int db, float M, float Lsum, int cnt, const float* o) {
-      if (gi >= nG) return;
-      float* rec = part_bh + ((size_t)gi * S + cidx) * kPartialStride;
-      if (db == 0 && hh == 0) {
-        st_agent(rec, M);
-        st_agent(rec + 1, Lsum);
-        st_agent(rec + 2, __builtin_bit_cast(float, cnt));
-      }
+    float M1 = 0.f, L1 = 0.f, o1[16];
+    int c1 = 0;
+    merge_parities<B16>(st, sh, qh, kp, [&](int, float M, float Lsum, int cnt, const float* o) {
+      M1 = M;
+      L1 = Lsum;
+      c1 = cnt;
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st_agent(rec + 4 + 32 * db + 8 * g + 4 * hh + e, o[4 * g + e]);
+      for (int r = 0; r < 16; ++r) o1[r] = o[r];
     });
-    __syncthreads();  // the parked states are read before the rings are refilled
+    merge_halves<B16>(sh, qh, kp, M1, L1, c1, o1, [&](float M, float Lsum, int cnt, const float* o) {
+      if (gi < nG) write_record(part_bh + ((size_t)gi * S + cidx) * kPartialStride, kp, hh, M, Lsum, cnt, o);
+    });
+  } else {
+    for (int g0 = 0; g0 < nG; g0 += kTileQ) {
+      if (g0 > 0) loop.prime(nblk, [](int) { return true; });  // after the previous group's last barrier
+      const int gi = g0 + 32 * qh + (lane & 31);
+      Frag<B16> qf;
+      load_frag(qf, qg + (size_t)sh.G[gi < nG ? gi : nG - 1] * rs, hh);
+      HalfState st;
+      state_init(st);
+      __builtin_amdgcn_s_setprio(0);
+      loop.run(st, qf, nblk, c, g0 + 32 * qh < nG);
+      __builtin_amdgcn_s_setprio(2);
+      merge_parities<B16>(st, sh, qh, kp, [&](int db, float M, float Lsum, int cnt, const float* o) {
+        if (gi < nG) write_record(part_bh + ((size_t)gi * S + cidx) * kPartialStride, db, hh, M, Lsum, cnt, o);
+      });
+      __syncthreads();  // the parked states are read before the rings are refilled
+    }
   }
 
   // Arrival: the last split of (b, h) merges all partials.  Every thread's
