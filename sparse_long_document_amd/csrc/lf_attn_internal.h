@@ -15,7 +15,7 @@ constexpr int kTileQ = 64;         // query rows of one band workgroup (two halv
 constexpr int kBlockK = 32;        // keys per inner block (M of the 32x32 MFMA)
 constexpr int kWaves = 4;          // waves per workgroup: query half x key parity
 constexpr int kThreads = 64 * kWaves;
-constexpr int kGlobalChunk = 512;  // keys per split of a global row
+constexpr int kGlobalChunk = 1024;  // keys per split of a global row
 constexpr int kPartialStride = 68; // floats per partial record: m, l, count, pad, O[64]
 
 // Everything one launch needs, passed by value as the kernel argument.
