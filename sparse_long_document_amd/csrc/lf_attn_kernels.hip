@@ -3,12 +3,13 @@
 // One launch computes every output row with two kinds of workgroups:
 //   * global-row splits (dispatched first): split c of one (batch row b,
 //     head h) scores every global token of b against keys
-//     [512c, 512c + 512) with the global projections (each global token
+//     [1024c, 1024c + 1024) with the global projections (each global token
 //     attends to every token: segmentfault Longformer summary, "Global
 //     attention" and "Linear projections for global attention").  Each
 //     split leaves a partial (max, sum, unnormalised output) record in the
 //     workspace; the last split of (b, h) to arrive merges them and writes
-//     the global rows;
+//     the global rows.  With at most 32 global tokens per batch row the four
+//     waves of a split share the keys instead of the queries ("solo");
 //   * band tiles: 64 consecutive query rows of one (b, h, residue class r
 //     of the head's dilation d).  A dilated window over positions
 //     {r, r+d, r+2d, ...} is a plain window over that subsequence, so each

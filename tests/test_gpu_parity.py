@@ -101,8 +101,12 @@ SMALL = [
     dict(B=1, n=4100, H=1, window=32, global_positions=[5, 4096, 4099]),
     # four global tokens (the vector-unit path), some inside rows' windows, dilated heads
     dict(B=2, n=500, H=2, window=30, dilation=[1, 3], global_positions=[0, 33, 250, 499], pad_tail=20),
-    # one dilation for every head, n not a multiple of it (tile decode by multiply-high)
+    # one dilation for every head, n not a multiple of it (the arithmetic tile decode)
     dict(B=3, n=1001, H=3, window=40, dilation=[3, 3, 3], n_global=2),
+    # 32 global tokens, the most the four-wave split takes, over two key chunks
+    dict(B=1, n=1500, H=1, window=40, n_global=32),
+    # 33 global tokens (the two-parity split), three key chunks, the last ragged
+    dict(B=1, n=2100, H=2, window=48, n_global=33, pad_tail=50),
 ]
 
 
