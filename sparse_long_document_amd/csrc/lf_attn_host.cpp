@@ -65,7 +65,8 @@ lf_status make_plan(const lf_attn_params* p, Plan& pl) {
   if (tiles * p->B > (int64_t)1 << 30) return LF_ERR_UNSUPPORTED;
 
   pl.use_globals = (p->causal == 0 && p->max_global > 0) ? 1 : 0;
-  pl.S = (p->n + lf::kGlobalChunk - 1) / lf::kGlobalChunk;
+  // records are laid out for the split count of the short chunk, the most
+  pl.S = (p->n + lf::kGlobalChunkShort - 1) / lf::kGlobalChunkShort;
   const size_t bh = (size_t)p->B * p->H;
   pl.ws_tickets_off = kAlign;
   pl.ws_partials_off = pl.ws_tickets_off + align_up(bh * sizeof(int32_t), kAlign);
@@ -149,8 +150,17 @@ lf_status lf_attn_forward(const lf_attn_params* p, const void* q, const void* k,
   kp.c = (float)(scale * 1.4426950408889634);  // log2(e)
   kp.tiles_per_b = (int32_t)pl.tiles_per_b;
   kp.n_band = (int32_t)(pl.tiles_per_b * p->B);
-  kp.n_glob = pl.use_globals ? p->B * p->H * pl.S : 0;
-  kp.S = pl.S;
+  // Global-row splits: short chunks when band tiles and short splits are all
+  // resident at once, long ones otherwise (both fit the workspace).
+  int chunk = lf::kGlobalChunkLong;
+  if (pl.use_globals) {
+    const int64_t resident = lf::resident_workgroups(p->dtype);
+    const int64_t short_splits = (int64_t)p->B * p->H * pl.S;
+    if (resident > 0 && (int64_t)kp.n_band + short_splits <= resident) chunk = lf::kGlobalChunkShort;
+  }
+  kp.chunk = chunk;
+  kp.S = (p->n + chunk - 1) / chunk;
+  kp.n_glob = pl.use_globals ? p->B * p->H * kp.S : 0;
   for (int h = 0; h < p->H; ++h) {
     kp.dil[h] = pl.dil[h];
     kp.tile0[h] = pl.tile0[h];

@@ -15,7 +15,11 @@ constexpr int kTileQ = 64;         // query rows of one band workgroup (two halv
 constexpr int kBlockK = 32;        // keys per inner block (M of the 32x32 MFMA)
 constexpr int kWaves = 4;          // waves per workgroup: query half x key parity
 constexpr int kThreads = 64 * kWaves;
-constexpr int kGlobalChunk = 1024;  // keys per split of a global row
+// Keys per split of a global row: the short chunk when the whole launch is
+// resident at once (splits then end sooner), else the long one (fewer splits,
+// fewer records to merge).  The workspace is sized for the short one.
+constexpr int kGlobalChunkShort = 512;
+constexpr int kGlobalChunkLong = 1024;
 constexpr int kPartialStride = 68; // floats per partial record: m, l, count, pad, O[64]
 
 // Everything one launch needs, passed by value as the kernel argument.
@@ -38,6 +42,7 @@ struct KernelParams {
   int32_t n_band;      // band workgroups in the launch
   int32_t n_glob;      // global-row workgroups in the launch
   int32_t S;           // splits of a global row
+  int32_t chunk;       // keys per split
   int32_t uni_dil;     // the dilation of every head when all heads share one, else 0
   int32_t tiles_per_head;  // band tiles of each head of a batch row when uni_dil > 0
   int32_t dil[LF_MAX_HEADS];
@@ -46,5 +51,9 @@ struct KernelParams {
 
 // Launches the forward kernel.  Returns the hipError_t value as int.
 int launch_forward(const KernelParams& kp, int dtype, void* stream);
+
+// Workgroups of the forward kernel that the current device holds at once
+// (compute units times workgroups per unit), or 0 if the runtime cannot say.
+int64_t resident_workgroups(int dtype);
 
 }  // namespace lf

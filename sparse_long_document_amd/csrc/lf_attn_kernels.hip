@@ -1592,8 +1592,8 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
   const T* qg = reinterpret_cast<const T*>(p.qg) + head;
   ChunkSrc src;
   src.mrow = mrow;
-  src.cbeg = cidx * kGlobalChunk;
-  src.cend = min(n, src.cbeg + kGlobalChunk);
+  src.cbeg = cidx * p.chunk;
+  src.cend = min(n, src.cbeg + p.chunk);
   src.nwin = (src.cend - src.cbeg + kBlockK - 1) / kBlockK;
   src.nG = 0;
   const int nblk = src.nwin;
@@ -1752,6 +1752,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 __global__ __launch_bounds__(kThreads) void lf_attn_fwd_f32(const KernelParams p) { fwd_body<false>(p); }
 
 }  // namespace
+
+int64_t resident_workgroups(int dtype) {
+  // per device, computed once (concurrent first calls compute the same value)
+  static int64_t cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  const int slot = (dev < 32 ? dev : 31) * 2 + (dtype == LF_BF16 ? 0 : 1);
+  if (cache[slot] > 0) return cache[slot];
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  const hipError_t e =
+      dtype == LF_BF16
+          ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void*>(lf_attn_fwd_bf16), kThreads, 0)
+          : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void*>(lf_attn_fwd_f32), kThreads, 0);
+  if (e != hipSuccess) return 0;
+  cache[slot] = (int64_t)cus * per;
+  return cache[slot];
+}
 
 int launch_forward(const KernelParams& kp, int dtype, void* stream) {
   const int grid = kp.n_band + kp.n_glob;

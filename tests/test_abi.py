@@ -69,10 +69,11 @@ def _forward(p, ptrs=None, ws_bytes=1 << 30, row_nnz=None):
 
 def test_workspace_bytes_layout():
     # 256-byte status block, B*H counters padded to 256, then the partial
-    # records of the global rows: B*H*max_global*ceil(n/1024) records of 68 floats
+    # records of the global rows: B*H*max_global*ceil(n/512) records of 68
+    # floats (the split count of the shorter key chunk)
     p, _k = _params(B=2, n=4096, H=12, max_global=64)
     got = lf.library().lf_attn_workspace_bytes(ctypes.byref(p))
-    rec = 2 * 12 * 64 * 4 * 68 * 4
+    rec = 2 * 12 * 64 * 8 * 68 * 4
     assert got == 256 + 256 + rec
     p, _k = _params(causal=True, max_global=0)
     assert lf.library().lf_attn_workspace_bytes(ctypes.byref(p)) == 512
