@@ -103,7 +103,9 @@ lf_status lf_attn_workspace_init(void* workspace, size_t workspace_bytes, void* 
  * by lf_attn_workspace_init; two calls in flight at once must not share a
  * workspace.  LF_OK means the arguments were valid and the launch was
  * accepted; faults during execution surface at the caller's next
- * synchronisation. */
+ * synchronisation.  The first call on a device also asks the runtime for
+ * that device's compute-unit count and the kernel's occupancy (no
+ * allocation, no synchronisation); they set how the global rows are split. */
 lf_status lf_attn_forward(const lf_attn_params* p,
                           const void* q, const void* k, const void* v,
                           const void* q_g, const void* k_g, const void* v_g,
