@@ -107,6 +107,10 @@ SMALL = [
     dict(B=1, n=1500, H=1, window=40, n_global=32),
     # 33 global tokens (the two-parity split), three key chunks, the last ragged
     dict(B=1, n=2100, H=2, window=48, n_global=33, pad_tail=50),
+    # the most heads the library takes
+    dict(B=1, n=300, H=64, window=20, n_global=2),
+    # the most global tokens a batch row may hold (LF_MAX_GLOBAL)
+    dict(B=1, n=1100, H=1, window=16, n_global=1024),
 ]
 
 
