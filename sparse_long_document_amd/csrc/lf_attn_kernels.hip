@@ -973,8 +973,8 @@ template <bool B16, class Src>
 struct HalfLoop {
   using T = elem_t<B16>;
   using L = Lay<B16>;
-  // vector-memory instructions one issue() emits (K and V rows), shared
-  // with the other wave of the parity
+  // vector-memory instructions one issue() emits (K and V rows) when the
+  // wave shares the block with the other wave of its parity (twice that solo)
   static constexpr int kIssueLoads = 2 * L::kHalfLoads;
   static constexpr int kTabPairs = 12;
   const Src& src;
@@ -988,13 +988,13 @@ struct HalfLoop {
   // buffer resources and per-lane offsets of the evenly spaced (affine) path
   __amdgpu_buffer_rsrc_t rk, rv;
   uint32_t vk0, vk1, vv;
-  // key-validity bits of this wave's table blocks (entry k: block kp + 2k),
-  // filled in the prologue; null when the source has more table blocks than
-  // the table holds
+  // key-validity bits of this wave's table blocks (entry k: block
+  // kp + (k << lg)), filled in the prologue; null when the source has more
+  // table blocks than the table holds
   const uint32_t* ktab;
   int tabv[kTabPairs];
   int tab_cnt;
-  uint32_t full_keys;  // bit k: every key of table block kp + 2k is valid
+  uint32_t full_keys;  // bit k: every key of table entry k's block is valid
   int fast_lo, fast_hi;
   uint32_t fast_steps;  // bit s: the wave's block of step s is full for its half
   // evenly spaced blocks [aff_lo, aff_hi): block i's rows start at byte
@@ -1230,8 +1230,9 @@ struct HalfLoop {
 // step for every wave of the tile, for a handful of keys), the parity-0
 // wave of each query half scores them after the block loop with dot
 // products on the vector unit.  Their K and V rows are staged in LDS by one
-// direct-to-LDS load during the prologue, in the unused tail of the global
-// list: 1 KB per query half, the K rows then the V rows, 128 B each.
+// direct-to-LDS load as soon as the global list is known (after the scan),
+// in the unused tail of the list: 1 KB per query half, the K rows then the
+// V rows, 128 B each.
 // ---------------------------------------------------------------------------
 constexpr int kVecGlobals = 4;
 
