@@ -62,7 +62,10 @@ typedef enum {
   LF_ERR_HIP = 4          /* the HIP runtime refused the launch */
 } lf_status;
 
-typedef enum { LF_F32 = 0, LF_BF16 = 1 } lf_dtype;
+/* Element type of q, k, v, q_g, k_g, v_g and out.  Scores, softmax state
+ * and P V accumulate in fp32 in every case; the probabilities enter P V in
+ * the element type (fp32, bf16 or f16). */
+typedef enum { LF_F32 = 0, LF_BF16 = 1, LF_F16 = 2 } lf_dtype;
 
 /* Limits of this build. */
 #define LF_HEAD_DIM 64

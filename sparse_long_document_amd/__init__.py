@@ -30,7 +30,7 @@ __all__ = [
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblf_attn.so")
-KERNEL_SOURCES = ("csrc/lf_attn_kernels.hip", "csrc/lf_attn_internal.h")
+KERNEL_SOURCES = ("csrc/lf_attn_kernels.hip", "csrc/lf_attn_kernels_f16.hip", "csrc/lf_attn_internal.h")
 
 
 def kernel_source_hash() -> str:
@@ -46,7 +46,8 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 LF_OK, LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED, LF_ERR_WORKSPACE, LF_ERR_HIP = range(5)
-LF_F32, LF_BF16 = 0, 1
+LF_F32, LF_BF16, LF_F16 = 0, 1, 2
+_DTYPES = {torch.float32: LF_F32, torch.bfloat16: LF_BF16, torch.float16: LF_F16}
 LF_HEAD_DIM = 64
 LF_MAX_HEADS = 64
 LF_MAX_GLOBAL = 1024
@@ -120,7 +121,7 @@ def make_params(B: int, n: int, H: int, D: int, window: int,
         dilation=ctypes.cast(dil, ctypes.POINTER(ctypes.c_int32)) if dil is not None else None,
         causal=int(bool(causal)), scale=0.0 if scale is None else float(scale),
         max_global=int(max_global),
-        dtype=LF_BF16 if dtype == torch.bfloat16 else (LF_F32 if dtype == torch.float32 else 99),
+        dtype=_DTYPES.get(dtype, 99),
     )
     return p, dil
 
@@ -180,7 +181,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             row_nnz: Optional[torch.Tensor] = None):
     """Longformer attention forward (``lf_attn_forward``).
 
-    q, k, v, q_g, k_g, v_g: [B, n, H, 64] bf16 or fp32 GPU tensors, contiguous
+    q, k, v, q_g, k_g, v_g: [B, n, H, 64] bf16, f16 or fp32 GPU tensors, contiguous
     (q_g/k_g/v_g default to q/k/v).  mask: [B, n] int8 (other integer dtypes
     are converted) with 0 = no attention, 1 = local, 2 = global; None means
     all local.  window: one-sided w.  dilation: per-head stride.  Returns

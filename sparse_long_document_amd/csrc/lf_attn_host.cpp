@@ -37,12 +37,12 @@ lf_status make_plan(const lf_attn_params* p, Plan& pl) {
   if (!std::isfinite(p->scale) || p->scale < 0.f) return LF_ERR_INVALID_ARG;
   if (p->max_global < 0) return LF_ERR_INVALID_ARG;
   if (p->D != LF_HEAD_DIM) return LF_ERR_UNSUPPORTED;
-  if (p->dtype != LF_F32 && p->dtype != LF_BF16) return LF_ERR_UNSUPPORTED;
+  if (p->dtype != LF_F32 && p->dtype != LF_BF16 && p->dtype != LF_F16) return LF_ERR_UNSUPPORTED;
   if (p->H > LF_MAX_HEADS || p->max_global > LF_MAX_GLOBAL || p->n > LF_MAX_SEQ) return LF_ERR_UNSUPPORTED;
   const int64_t tokens = (int64_t)p->B * p->n;
   if (tokens > INT32_MAX) return LF_ERR_UNSUPPORTED;
 
-  pl.elem = p->dtype == LF_BF16 ? 2 : 4;
+  pl.elem = p->dtype == LF_F32 ? 4 : 2;
   pl.tensor_bytes = (size_t)tokens * p->H * p->D * pl.elem;
   // The kernels address one batch row of a tensor with 32-bit byte offsets.
   if ((int64_t)p->n * p->H * p->D * pl.elem > (int64_t)LF_MAX_ROW_BYTES) return LF_ERR_UNSUPPORTED;

@@ -56,4 +56,9 @@ int launch_forward(const KernelParams& kp, int dtype, void* stream);
 // (compute units times workgroups per unit), or 0 if the runtime cannot say.
 int64_t resident_workgroups(int dtype);
 
+// The same two for the f16 kernel, which the kernel source yields when it is
+// compiled a second time with LF_HALF_F16 (lf_attn_kernels_f16.hip).
+int launch_forward_f16(const KernelParams& kp, void* stream);
+int64_t resident_workgroups_f16();
+
 }  // namespace lf

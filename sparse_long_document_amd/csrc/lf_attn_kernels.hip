@@ -54,9 +54,33 @@
 namespace lf {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// The 16-bit element type of this translation unit: bf16, or f16 when the
+// source is compiled with LF_HALF_F16 (which then yields the f16 kernel).
+#if LF_HALF_F16
+typedef _Float16 h16;
+#else
+typedef __bf16 h16;
+#endif
+typedef h16 h16x8 __attribute__((ext_vector_type(8)));
+typedef h16 h16x4 __attribute__((ext_vector_type(4)));
+typedef h16 h16x2 __attribute__((ext_vector_type(2)));
+
+// 32x32x16 MFMA and two-term dot product on 16-bit operands with fp32
+// accumulation, for the element type above.
+__device__ __forceinline__ auto mfma16(h16x8 a, h16x8 b, __attribute__((ext_vector_type(16))) float c) {
+#if LF_HALF_F16
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+#else
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+#endif
+}
+__device__ __forceinline__ float dot2h(h16x2 a, h16x2 b, float c) {
+#if LF_HALF_F16
+  return __builtin_amdgcn_fdot2(a, b, c, false);
+#else
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+#endif
+}
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -104,7 +128,7 @@ __device__ __forceinline__ int vswz(int row) {
 }
 
 template <bool B16>
-using elem_t = typename std::conditional<B16, __bf16, float>::type;
+using elem_t = typename std::conditional<B16, h16, float>::type;
 
 // Per-lane operand fragment of 64 head dims of one row (query or key) for
 // the QK^T contraction; the head dims a lane holds depend on lane / 32.
@@ -112,7 +136,7 @@ template <bool B16>
 struct Frag;
 template <>
 struct Frag<true> {
-  bf16x8 x[4];  // dims 16s + 8*(lane/32) + [0, 8)
+  h16x8 x[4];  // dims 16s + 8*(lane/32) + [0, 8)
 };
 template <>
 struct Frag<false> {
@@ -153,8 +177,8 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 // (vector-memory loads in flight are not waited for).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__device__ __forceinline__ void load_frag(Frag<true>& f, const __bf16* row, int hh) {
-  const bf16x8* p = reinterpret_cast<const bf16x8*>(row);
+__device__ __forceinline__ void load_frag(Frag<true>& f, const h16* row, int hh) {
+  const h16x8* p = reinterpret_cast<const h16x8*>(row);
 #pragma unroll
   for (int s = 0; s < 4; ++s) f.x[s] = p[2 * s + hh];
 }
@@ -174,7 +198,7 @@ __device__ __forceinline__ void load_frag(Frag<false>& f, const float* row, int 
 // acc (32 keys x 32 queries) += K Q^T over the 64 head dims.
 __device__ __forceinline__ void qk(f32x16& acc, const Frag<true>& kf, const Frag<true>& qf) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.x[s], qf.x[s], acc, 0, 0, 0);
+  for (int s = 0; s < 4; ++s) acc = mfma16(kf.x[s], qf.x[s], acc);
 }
 
 __device__ __forceinline__ void qk(f32x16& acc, const Frag<false>& kf, const Frag<false>& qf) {
@@ -223,7 +247,7 @@ template <bool B16>
 struct VtFrag;
 template <>
 struct VtFrag<true> {
-  bf16x8 a[2][2];
+  h16x8 a[2][2];
 };
 template <>
 struct VtFrag<false> {
@@ -299,13 +323,13 @@ __device__ __forceinline__ void read_frags_at(Frag<true>& kf, VtFrag<true>& vt, 
         "i"(kOff + 1024), "i"(kOff + 2048), "i"(kOff + 3072)
       : "memory");
 #pragma unroll
-  for (int s = 0; s < 4; ++s) kf.x[s] = __builtin_bit_cast(bf16x8, k[s]);
+  for (int s = 0; s < 4; ++s) kf.x[s] = __builtin_bit_cast(h16x8, k[s]);
 #pragma unroll
   for (int db = 0; db < 2; ++db)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const u32x2 lo = r[4 * db + 2 * ks], hi = r[4 * db + 2 * ks + 1];
-      vt.a[db][ks] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      vt.a[db][ks] = __builtin_bit_cast(h16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
     }
 }
 
@@ -359,7 +383,7 @@ __device__ __forceinline__ void zero_dead_keys(VtFrag<true>& vt, uint32_t keymas
     }
 #pragma unroll
     for (int db = 0; db < 2; ++db)
-      vt.a[db][ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, vt.a[db][ks]) & keep);
+      vt.a[db][ks] = __builtin_bit_cast(h16x8, __builtin_bit_cast(u32x4, vt.a[db][ks]) & keep);
   }
 }
 
@@ -395,7 +419,7 @@ __device__ __forceinline__ uint32_t above_span(uint32_t u, uint32_t span) {
 __device__ __forceinline__ void zero_dead_krow(Frag<true>& kf, uint32_t keymask, int lane) {
   if (!((keymask >> (lane & 31)) & 1u)) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kf.x[s] = bf16x8{};
+    for (int s = 0; s < 4; ++s) kf.x[s] = h16x8{};
   }
 }
 
@@ -411,7 +435,7 @@ template <bool B16>
 struct PFrag;
 template <>
 struct PFrag<true> {
-  bf16x8 x[2];  // PV k-step ks holds accumulator elements 8ks .. 8ks+7
+  h16x8 x[2];  // PV k-step ks holds accumulator elements 8ks .. 8ks+7
 };
 template <>
 struct PFrag<false> {
@@ -442,7 +466,7 @@ __device__ __forceinline__ void pv(f32x16 (&o)[2], const PFrag<true>& pf, const 
   for (int db = 0; db < 2; ++db)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt.a[db][ks], pf.x[ks], o[db], 0, 0, 0);
+      o[db] = mfma16(vt.a[db][ks], pf.x[ks], o[db]);
 }
 
 __device__ __forceinline__ void pv(f32x16 (&o)[2], const PFrag<false>& pf, const VtFrag<false>& vt) {
@@ -487,17 +511,17 @@ __device__ __forceinline__ void softmax_core(HalfState& st, f32x16& s, PFrag<B16
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf.x[ks][e] = (__bf16)s[8 * ks + e];
+      for (int e = 0; e < 8; ++e) pf.x[ks][e] = (h16)s[8 * ks + e];
     // row sum of the rounded probabilities that enter P V (two bf16 at a
     // time with fp32 accumulation), in two chains
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    const h16x2 one = {(h16)1.0f, (h16)1.0f};
     float la = 0.f, lb = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bf16x2 p0 = {pf.x[0][2 * j], pf.x[0][2 * j + 1]};
-      const bf16x2 p1 = {pf.x[1][2 * j], pf.x[1][2 * j + 1]};
-      la = __builtin_amdgcn_fdot2_f32_bf16(p0, one, la, false);
-      lb = __builtin_amdgcn_fdot2_f32_bf16(p1, one, lb, false);
+      const h16x2 p0 = {pf.x[0][2 * j], pf.x[0][2 * j + 1]};
+      const h16x2 p1 = {pf.x[1][2 * j], pf.x[1][2 * j + 1]};
+      la = dot2h(p0, one, la);
+      lb = dot2h(p1, one, lb);
     }
     st.l += la + lb;
   } else {
@@ -752,13 +776,13 @@ template <bool B16>
 __device__ __forceinline__ void store4(elem_t<B16>* dst, const float* v);
 
 template <>
-__device__ __forceinline__ void store4<true>(__bf16* dst, const float* v) {
-  bf16x4 t;
-  t[0] = (__bf16)v[0];
-  t[1] = (__bf16)v[1];
-  t[2] = (__bf16)v[2];
-  t[3] = (__bf16)v[3];
-  *reinterpret_cast<bf16x4*>(dst) = t;
+__device__ __forceinline__ void store4<true>(h16* dst, const float* v) {
+  h16x4 t;
+  t[0] = (h16)v[0];
+  t[1] = (h16)v[1];
+  t[2] = (h16)v[2];
+  t[3] = (h16)v[3];
+  *reinterpret_cast<h16x4*>(dst) = t;
 }
 
 template <>
@@ -1242,11 +1266,11 @@ __device__ __forceinline__ unsigned char* vec_rows(int* G, int qh) {
 
 // Lane l fetches 16-byte chunk l % 8 of the K (l < 32) or V (l >= 32) row of
 // global token (l / 8) % 4 (clamped to the last one); it lands at byte 16 l.
-__device__ __forceinline__ void issue_vec_rows(const __bf16* kb, const __bf16* vb, uint32_t rs, const int* G, int nG,
+__device__ __forceinline__ void issue_vec_rows(const h16* kb, const h16* vb, uint32_t rs, const int* G, int nG,
                                                unsigned char* dst) {
   const int l = lane_id_here();
   const int key = min((l >> 3) & 3, nG - 1);
-  const __bf16* src = ((l >> 5) ? vb : kb) + (size_t)G[key] * rs + 8 * (l & 7);
+  const h16* src = ((l >> 5) ? vb : kb) + (size_t)G[key] * rs + 8 * (l & 7);
   __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)dst, 16, 0, 0);
 }
 
@@ -1270,12 +1294,12 @@ __device__ void vec_global_columns(HalfState& st, const Frag<true>& qf, const Ba
     float acc = 0.f;
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      const bf16x8 kk = *reinterpret_cast<const bf16x8*>(kr + 32 * s4 + 16 * hh);
+      const h16x8 kk = *reinterpret_cast<const h16x8*>(kr + 32 * s4 + 16 * hh);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x2 a = {qf.x[s4][2 * j], qf.x[s4][2 * j + 1]};
-        const bf16x2 bb = {kk[2 * j], kk[2 * j + 1]};
-        acc = __builtin_amdgcn_fdot2_f32_bf16(a, bb, acc, false);
+        const h16x2 a = {qf.x[s4][2 * j], qf.x[s4][2 * j + 1]};
+        const h16x2 bb = {kk[2 * j], kk[2 * j + 1]};
+        acc = dot2h(a, bb, acc);
       }
     }
     const float sc = (acc + __shfl_xor(acc, 32)) * c;
@@ -1291,7 +1315,7 @@ __device__ void vec_global_columns(HalfState& st, const Frag<true>& qf, const Ba
 #pragma unroll
         for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
     }
-    const float pr = take ? (float)(__bf16)__builtin_amdgcn_exp2f(sc - st.m) : 0.f;
+    const float pr = take ? (float)(h16)__builtin_amdgcn_exp2f(sc - st.m) : 0.f;
     if (hh == 0) {
       st.l += pr;
       st.cnt += take ? 1 : 0;
@@ -1301,7 +1325,7 @@ __device__ void vec_global_columns(HalfState& st, const Frag<true>& qf, const Ba
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const bf16x4 vv = *reinterpret_cast<const bf16x4*>(vr + 2 * (32 * db + 8 * g4 + 4 * hh));
+        const h16x4 vv = *reinterpret_cast<const h16x4*>(vr + 2 * (32 * db + 8 * g4 + 4 * hh));
 #pragma unroll
         for (int i = 0; i < 4; ++i) st.o[db][4 * g4 + i] = __builtin_fmaf(pr, (float)vv[i], st.o[db][4 * g4 + i]);
       }
@@ -1464,7 +1488,7 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
     vec_g = B16 && src.nG > 0 && src.nG <= kVecGlobals;
     if constexpr (B16) {
       if (vec_g && kp == 0 && active)
-        issue_vec_rows(reinterpret_cast<const __bf16*>(p.k) + head, reinterpret_cast<const __bf16*>(p.v) + head, rs,
+        issue_vec_rows(reinterpret_cast<const h16*>(p.k) + head, reinterpret_cast<const h16*>(p.v) + head, rs,
                        sh.G, src.nG, vrows);
     }
     return nwin + (vec_g ? 0 : (src.nG + kBlockK - 1) / kBlockK);
@@ -1743,6 +1767,13 @@ __device__ __forceinline__ void fwd_body(const KernelParams& p) {
   band_tile<B16>(p, xcd_remap(bid - p.n_glob, p.n_band), sh);
 }
 
+#if LF_HALF_F16
+// f16: the 16-bit kernel built for f16 elements.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void lf_attn_fwd_f16(
+    const KernelParams p) {
+  fwd_body<true>(p);
+}
+#else
 // bf16: four workgroups (16 waves) per CU: at most 128 VGPRs, under 40 KB of LDS.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void lf_attn_fwd_bf16(
     const KernelParams p) {
@@ -1751,28 +1782,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 
 // fp32: larger operand fragments and stages.
 __global__ __launch_bounds__(kThreads) void lf_attn_fwd_f32(const KernelParams p) { fwd_body<false>(p); }
+#endif
 
 }  // namespace
 
-int64_t resident_workgroups(int dtype) {
-  // per device, computed once (concurrent first calls compute the same value)
-  static int64_t cache[64];
+// Workgroups of one kernel that the current device holds at once (cached
+// per device), or 0.
+static int64_t resident_of(const void* kernel, int64_t* cache) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  const int slot = (dev < 32 ? dev : 31) * 2 + (dtype == LF_BF16 ? 0 : 1);
+  const int slot = dev < 32 ? dev : 31;
   if (cache[slot] > 0) return cache[slot];
   int cus = 0, per = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  const hipError_t e =
-      dtype == LF_BF16
-          ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void*>(lf_attn_fwd_bf16), kThreads, 0)
-          : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void*>(lf_attn_fwd_f32), kThreads, 0);
-  if (e != hipSuccess) return 0;
-  cache[slot] = (int64_t)cus * per;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kThreads, 0) != hipSuccess) return 0;
+  cache[slot] = (int64_t)cus * per;  // concurrent first calls store the same value
   return cache[slot];
 }
 
+#if LF_HALF_F16
+int64_t resident_workgroups_f16() {
+  static int64_t cache[32];
+  return resident_of(reinterpret_cast<const void*>(lf_attn_fwd_f16), cache);
+}
+
+int launch_forward_f16(const KernelParams& kp, void* stream) {
+  hipLaunchKernelGGL(lf_attn_fwd_f16, dim3(kp.n_band + kp.n_glob), dim3(kThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), kp);
+  return (int)hipGetLastError();
+}
+#else
+
+int64_t resident_workgroups(int dtype) {
+  static int64_t cache_bf16[32], cache_f32[32];
+  if (dtype == LF_F16) return resident_workgroups_f16();
+  return dtype == LF_BF16 ? resident_of(reinterpret_cast<const void*>(lf_attn_fwd_bf16), cache_bf16)
+                          : resident_of(reinterpret_cast<const void*>(lf_attn_fwd_f32), cache_f32);
+}
+
 int launch_forward(const KernelParams& kp, int dtype, void* stream) {
+  if (dtype == LF_F16) return launch_forward_f16(kp, stream);
   const int grid = kp.n_band + kp.n_glob;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == LF_BF16)
@@ -1781,5 +1830,6 @@ int launch_forward(const KernelParams& kp, int dtype, void* stream) {
     hipLaunchKernelGGL(lf_attn_fwd_f32, dim3(grid), dim3(kThreads), 0, s, kp);
   return (int)hipGetLastError();
 }
+#endif
 
 }  // namespace lf

@@ -91,7 +91,7 @@ def test_workspace_bytes_layout():
     (dict(max_global=-1), lf.LF_ERR_INVALID_ARG),
     (dict(D=32), lf.LF_ERR_UNSUPPORTED),
     (dict(D=128), lf.LF_ERR_UNSUPPORTED),
-    (dict(dtype=torch.float16), lf.LF_ERR_UNSUPPORTED),
+    (dict(dtype=torch.float64), lf.LF_ERR_UNSUPPORTED),
     (dict(H=65, dilation=None), lf.LF_ERR_UNSUPPORTED),
     (dict(max_global=2000), lf.LF_ERR_UNSUPPORTED),
     (dict(n=(1 << 24) + 1), lf.LF_ERR_UNSUPPORTED),

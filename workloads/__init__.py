@@ -216,10 +216,21 @@ def led_large_n16384() -> Problem:
     return Problem("led_large_n16384", *t, mask, 512, None, False, None)
 
 
+def longformer_base_n4096_f16() -> Problem:
+    """The longformer_base_n4096 problem with its six tensors in f16 (the
+    bf16 values of that workload are exact in f16)."""
+    p = longformer_base_n4096()
+    for name in ("q", "k", "v", "q_g", "k_g", "v_g"):
+        setattr(p, name, getattr(p, name).to(torch.float16))
+    p.name = "longformer_base_n4096_f16"
+    return p
+
+
 def by_name(name: str) -> Problem:
     return {
         "single_head_fp32_n512": single_head_fp32_n512,
         "longformer_base_n4096": longformer_base_n4096,
+        "longformer_base_n4096_f16": longformer_base_n4096_f16,
         "qa_padded_b2_n4096": qa_padded_b2_n4096,
         "charlm_causal_dilated_n23040": charlm_causal_dilated_n23040,
         "led_large_n16384": led_large_n16384,
@@ -227,5 +238,5 @@ def by_name(name: str) -> Problem:
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
-    """Exact widening of a bf16/fp32 CPU tensor to a float64 array."""
+    """Exact widening of a bf16/f16/fp32 CPU tensor to a float64 array."""
     return t.detach().to("cpu").to(torch.float64).numpy()
