@@ -216,7 +216,8 @@ def _sample_rows(n, w, mask_b, rng, extra=()):
 
 
 @pytest.mark.parametrize("name", ["longformer_base_n4096", "qa_padded_b2_n4096",
-                                  "charlm_causal_dilated_n23040", "led_large_n16384"])
+                                  "charlm_causal_dilated_n23040", "led_large_n16384",
+                                  "charlm_causal_dilated_n32256"])
 def test_workload_sampled_parity(name):
     prob = workloads.by_name(name)
     B, n, H, D = prob.shape
@@ -241,6 +242,9 @@ def test_workload_sampled_parity(name):
         assert nnz.sum() == 2043134 * 12
     if name == "charlm_causal_dilated_n23040":
         assert nnz.sum() == 93242880
+    if name == "charlm_causal_dilated_n32256":
+        # sum over heads and residues r of sum_t (min(t, w) + 1), t < |{r, r+d, ...}|
+        assert nnz.sum() == 131065344
     assert (out[np.broadcast_to((mask == 0)[:, :, None, None], out.shape)] == 0).all()
     _say(f"      {name}: worst sampled abs err {worst:.3e}")
 

@@ -203,6 +203,17 @@ def charlm_causal_dilated_n23040() -> Problem:
                    [1, 1, 1, 1, 1, 1, 2, 2], True, None)
 
 
+def charlm_causal_dilated_n32256() -> Problem:
+    """The char-LM layer at its evaluation length: B1 n32256 H8 D64, causal
+    w=512, dilation 1 on heads 0-5 and 2 on heads 6-7, bf16, no globals."""
+    rng = np.random.Generator(np.random.PCG64(6))
+    shape = (1, 32256, 8, D_HEAD)
+    t = [_draw(rng, shape, torch.bfloat16) for _ in range(6)]
+    mask = torch.ones((1, 32256), dtype=torch.int8)
+    return Problem("charlm_causal_dilated_n32256", *t, mask, 512,
+                   [1, 1, 1, 1, 1, 1, 2, 2], True, None)
+
+
 def led_large_n16384() -> Problem:
     """B1 n16384 H16 D64, w=512, bf16; global at 0 plus 16 distinct random
     positions in 1..n-1."""
@@ -233,6 +244,7 @@ def by_name(name: str) -> Problem:
         "longformer_base_n4096_f16": longformer_base_n4096_f16,
         "qa_padded_b2_n4096": qa_padded_b2_n4096,
         "charlm_causal_dilated_n23040": charlm_causal_dilated_n23040,
+        "charlm_causal_dilated_n32256": charlm_causal_dilated_n32256,
         "led_large_n16384": led_large_n16384,
     }[name]()
 
