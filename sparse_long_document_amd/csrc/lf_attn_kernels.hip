@@ -47,6 +47,7 @@
 #include <stdint.h>
 
 
+#include <atomic>
 #include <type_traits>
 
 #include "lf_attn_internal.h"
@@ -1787,22 +1788,25 @@ __global__ __launch_bounds__(kThreads) void lf_attn_fwd_f32(const KernelParams p
 }  // namespace
 
 // Workgroups of one kernel that the current device holds at once (cached
-// per device), or 0.
-static int64_t resident_of(const void* kernel, int64_t* cache) {
+// per device; devices past the 32nd are asked every time), or 0.
+static int64_t resident_of(const void* kernel, std::atomic<int64_t>* cache) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  const int slot = dev < 32 ? dev : 31;
-  if (cache[slot] > 0) return cache[slot];
+  if (dev < 32) {
+    const int64_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0, per = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kThreads, 0) != hipSuccess) return 0;
-  cache[slot] = (int64_t)cus * per;  // concurrent first calls store the same value
-  return cache[slot];
+  const int64_t r = (int64_t)cus * per;
+  if (dev < 32) cache[dev].store(r, std::memory_order_relaxed);  // concurrent first calls store the same value
+  return r;
 }
 
 #if LF_HALF_F16
 int64_t resident_workgroups_f16() {
-  static int64_t cache[32];
+  static std::atomic<int64_t> cache[32];
   return resident_of(reinterpret_cast<const void*>(lf_attn_fwd_f16), cache);
 }
 
@@ -1814,7 +1818,7 @@ int launch_forward_f16(const KernelParams& kp, void* stream) {
 #else
 
 int64_t resident_workgroups(int dtype) {
-  static int64_t cache_bf16[32], cache_f32[32];
+  static std::atomic<int64_t> cache_bf16[32], cache_f32[32];
   if (dtype == LF_F16) return resident_workgroups_f16();
   return dtype == LF_BF16 ? resident_of(reinterpret_cast<const void*>(lf_attn_fwd_bf16), cache_bf16)
                           : resident_of(reinterpret_cast<const void*>(lf_attn_fwd_f32), cache_f32);
