@@ -1,5 +1,5 @@
 """Oracle package: plain fp64 CPU implementation of the Longformer combined
-attention forward.
+attention forward and of its gradients.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by
 the benchmark's CPU-baseline leg, never by the product library.  It shares
@@ -13,3 +13,4 @@ from .longformer_attention import (  # noqa: F401
     pair_count,
     pattern,
 )
+from .longformer_backward import backward, row_lse  # noqa: F401,E402
