@@ -115,6 +115,51 @@ lf_status lf_attn_forward(const lf_attn_params* p,
                           const int8_t* mask, void* out, int32_t* row_nnz,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* lf_attn_forward that also writes lse[b,h,i] (fp32 [B, H, n], caller-owned,
+ * must not overlap any other buffer): the natural log of the row's softmax
+ * denominator, log sum_{j in S(i)} exp(s <q, k_j>) with the projections of
+ * the row's kind, and -inf for mask-0 rows.  It is the row statistic
+ * lf_attn_backward takes.  lse must not be NULL. */
+lf_status lf_attn_forward_lse(const lf_attn_params* p,
+                              const void* q, const void* k, const void* v,
+                              const void* q_g, const void* k_g, const void* v_g,
+                              const int8_t* mask, void* out, int32_t* row_nnz, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace lf_attn_backward needs (status word, the global
+ * token list of each batch row, one fp32 per row for <dout, out>).  Returns
+ * 0 if the parameters are invalid. */
+size_t lf_attn_backward_workspace_bytes(const lf_attn_params* p);
+
+/* Enqueue the backward on `stream` and return: the gradients of the forward
+ * above with respect to q, k, v, q_g, k_g, v_g for the upstream gradient
+ * dout of out.  The pages train the layer (segmentfault Longformer summary,
+ * "Training" and "Pre-training"; gittoolsai page, the gradient-checkpointing
+ * note) but print no formula for its gradient; what is computed is
+ * the chain rule through each row's softmax over S(i):
+ *   P_ij = exp(s <q_i, k_j> - lse_i) for j in S(i), D_i = <dout_i, out_i>,
+ *   dS_ij = P_ij (<dout_i, v_j> - D_i),
+ *   dq_i = s sum_j dS_ij k_j,  dk_j = s sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i,
+ * with (q, k, v) for local rows and (q_g, k_g, v_g) for global rows.
+ *   - dtype must be LF_BF16 or LF_F16 (LF_ERR_UNSUPPORTED otherwise); q..v_g,
+ *     out and dout are [B, n, H, D] of that type; out and lse are what
+ *     lf_attn_forward_lse wrote for the same inputs and parameters.
+ *   - dq, dk, dv, dq_g, dk_g, dv_g are fp32 [B, n, H, D], caller-owned, each
+ *     fully overwritten, none overlapping another buffer.  Rows that take no
+ *     part get zeros (mask-0 rows and keys; dq of global rows; dq_g of local
+ *     rows).  When q_g, k_g, v_g are NULL (aliasing q, k, v), the gradient of
+ *     a shared tensor is the sum of its two results.
+ *   - workspace holds lf_attn_backward_workspace_bytes(p) bytes; its first
+ *     256 bytes are the device status word (lf_attn_workspace_init clears
+ *     it, lf_attn_device_status reads it); the rest needs no initialisation.
+ *   - Asynchronous like lf_attn_forward; the same argument errors. */
+lf_status lf_attn_backward(const lf_attn_params* p,
+                           const void* q, const void* k, const void* v,
+                           const void* q_g, const void* k_g, const void* v_g,
+                           const int8_t* mask, const void* out, const void* dout, const float* lse,
+                           float* dq, float* dk, float* dv, float* dq_g, float* dk_g, float* dv_g,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Debug helper: synchronise `stream`, then read the device status word of
  * `workspace` into *status (LF_DEV_* bits; 0 = no condition seen). */
 lf_status lf_attn_device_status(const void* workspace, void* stream, int32_t* status);

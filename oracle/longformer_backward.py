@@ -9,8 +9,8 @@ What is computed: the exact gradient of the forward defined in
 semantics; see that module's header for the readings of the pages) with
 respect to all six inputs q, k, v, q_g, k_g, v_g, for an upstream gradient
 ``dout`` of the output.  The pages motivate the layer for fine-tuning and
-pre-training (allenai README "Usage" and news on training; segmentfault
-Longformer summary, "Training"), which needs this pass, but print no
+pre-training (segmentfault Longformer summary, "Training" and
+"Pre-training"; gittoolsai page, the gradient-checkpointing note), which needs this pass, but print no
 formula for it; the gradient of softmax attention restricted to a key set
 is the chain rule written out.  For one row i with key set S(i), scores
 e_j = s <q_i, k_j>, probabilities p = softmax(e) over S(i) and output

@@ -25,7 +25,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "forward", "workspace_bytes", "device_status", "pad_to_window_size",
+    "forward", "backward", "workspace_bytes", "device_status", "pad_to_window_size",
     "merge_masks", "library", "LfError", "LF_MAX_GLOBAL", "LF_MAX_HEADS",
 ]
 
@@ -54,6 +54,7 @@ LF_MAX_GLOBAL = 1024
 LF_DEV_TOO_MANY_GLOBALS = 1
 
 SYMBOLS = ("lf_attn_workspace_bytes", "lf_attn_workspace_init", "lf_attn_forward",
+           "lf_attn_forward_lse", "lf_attn_backward_workspace_bytes", "lf_attn_backward",
            "lf_attn_device_status", "lf_status_str")
 
 
@@ -97,6 +98,13 @@ def library() -> ctypes.CDLL:
             lib.lf_attn_forward.argtypes = [ctypes.POINTER(Params), vp, vp, vp, vp, vp, vp,
                                             vp, vp, vp, vp, sz, vp]
             lib.lf_attn_forward.restype = ctypes.c_int
+            lib.lf_attn_forward_lse.argtypes = [ctypes.POINTER(Params), vp, vp, vp, vp, vp, vp,
+                                                vp, vp, vp, vp, vp, sz, vp]
+            lib.lf_attn_forward_lse.restype = ctypes.c_int
+            lib.lf_attn_backward_workspace_bytes.argtypes = [ctypes.POINTER(Params)]
+            lib.lf_attn_backward_workspace_bytes.restype = sz
+            lib.lf_attn_backward.argtypes = [ctypes.POINTER(Params)] + [vp] * 16 + [vp, sz, vp]
+            lib.lf_attn_backward.restype = ctypes.c_int
             lib.lf_attn_device_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
             lib.lf_attn_device_status.restype = ctypes.c_int
             lib.lf_status_str.argtypes = [ctypes.c_int32]
@@ -178,14 +186,17 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             causal: bool = False, scale: Optional[float] = None,
             max_global: Optional[int] = None, return_row_nnz: bool = False,
             validate: bool = True, out: Optional[torch.Tensor] = None,
-            row_nnz: Optional[torch.Tensor] = None):
+            row_nnz: Optional[torch.Tensor] = None, return_lse: bool = False,
+            lse: Optional[torch.Tensor] = None):
     """Longformer attention forward (``lf_attn_forward``).
 
     q, k, v, q_g, k_g, v_g: [B, n, H, 64] bf16, f16 or fp32 GPU tensors, contiguous
     (q_g/k_g/v_g default to q/k/v).  mask: [B, n] int8 (other integer dtypes
     are converted) with 0 = no attention, 1 = local, 2 = global; None means
     all local.  window: one-sided w.  dilation: per-head stride.  Returns
-    out (and row_nnz int32 [B, H, n] if asked).
+    out, then row_nnz int32 [B, H, n] and lse fp32 [B, H, n] if asked
+    (``lf_attn_forward_lse``: each row's natural log-sum-exp, what
+    ``backward`` takes).
 
     validate=True checks mask contents on the host (one device sync) and
     derives max_global from the mask; validate=False trusts the caller
@@ -203,6 +214,47 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     v_g = v if v_g is None else v_g
     for name, t in (("q", q), ("k", k), ("v", v), ("q_g", q_g), ("k_g", k_g), ("v_g", v_g)):
         _check_tensor(name, t, (B, n, H, D), dtype, device)
+    mask, max_global = _prep_mask(mask, B, n, device, causal, max_global, validate)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, (B, n, H, D), dtype, device)
+    if return_row_nnz and row_nnz is None:
+        row_nnz = torch.empty((B, H, n), dtype=torch.int32, device=device)
+    if row_nnz is not None:
+        _check_tensor("row_nnz", row_nnz, (B, H, n), torch.int32, device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, n), dtype=torch.float32, device=device)
+    if lse is not None:
+        _check_tensor("lse", lse, (B, H, n), torch.float32, device)
+
+    p, _keep = make_params(B, n, H, D, window, dilation, causal, scale, max_global, dtype)
+    lib = library()
+    need = int(lib.lf_attn_workspace_bytes(ctypes.byref(p)))
+    if need == 0:
+        raise LfError(LF_ERR_INVALID_ARG, "lf_attn_workspace_bytes")
+    stream = torch.cuda.current_stream(device).cuda_stream
+    ws = _workspace(need, device, stream, (B, H))
+    vp = ctypes.c_void_p
+    args = [ctypes.byref(p), vp(q.data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()),
+            vp(q_g.data_ptr()), vp(k_g.data_ptr()), vp(v_g.data_ptr()), vp(mask.data_ptr()),
+            vp(out.data_ptr()), vp(row_nnz.data_ptr() if row_nnz is not None else None)]
+    tail = [vp(ws.data_ptr()), ctypes.c_size_t(ws.numel()), vp(stream)]
+    if lse is not None:
+        st = lib.lf_attn_forward_lse(*args, vp(lse.data_ptr()), *tail)
+        if st != LF_OK:
+            raise LfError(st, "lf_attn_forward_lse")
+    else:
+        st = lib.lf_attn_forward(*args, *tail)
+        if st != LF_OK:
+            raise LfError(st, "lf_attn_forward")
+    res = (out,) + ((row_nnz,) if return_row_nnz else ()) + ((lse,) if return_lse else ())
+    return res if len(res) > 1 else out
+
+
+def _prep_mask(mask, B, n, device, causal, max_global, validate):
+    """Mask as contiguous int8 [B, n] on the device, and the max_global bound
+    (derived from the mask when validating)."""
     if mask is None:
         mask = torch.ones((B, n), dtype=torch.int8, device=device)
     elif mask.dtype != torch.int8:
@@ -224,33 +276,66 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             raise ValueError(f"at most {LF_MAX_GLOBAL} global tokens per row are supported")
     if max_global is None:
         max_global = 0 if causal else min(n, LF_MAX_GLOBAL)
-    if out is None:
-        out = torch.empty_like(q)
-    else:
-        _check_tensor("out", out, (B, n, H, D), dtype, device)
-    if return_row_nnz and row_nnz is None:
-        row_nnz = torch.empty((B, H, n), dtype=torch.int32, device=device)
-    if row_nnz is not None:
-        _check_tensor("row_nnz", row_nnz, (B, H, n), torch.int32, device)
+    return mask, max_global
 
+
+_bwd_ws = {}
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+             q_g: Optional[torch.Tensor], k_g: Optional[torch.Tensor], v_g: Optional[torch.Tensor],
+             mask: Optional[torch.Tensor], out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
+             window: int = 256, dilation: Optional[Sequence[int]] = None, causal: bool = False,
+             scale: Optional[float] = None, max_global: Optional[int] = None,
+             validate: bool = True, grads: Optional[Sequence[torch.Tensor]] = None):
+    """Gradients of the forward (``lf_attn_backward``): returns fp32
+    (dq, dk, dv, dq_g, dk_g, dv_g), each [B, n, H, 64].  q..v_g, out and dout
+    are bf16 or f16; out and lse are what ``forward(..., return_lse=True)``
+    returned for the same inputs.  When q_g/k_g/v_g are None (aliasing
+    q/k/v) the gradient of a shared tensor is the sum of its two results.
+    ``grads`` may supply the six output tensors."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, n, H, D]")
+    B, n, H, D = q.shape
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("q must be a GPU tensor (this library has no CPU path)")
+    dtype = q.dtype
+    q_g = q if q_g is None else q_g
+    k_g = k if k_g is None else k_g
+    v_g = v if v_g is None else v_g
+    for name, t in (("q", q), ("k", k), ("v", v), ("q_g", q_g), ("k_g", k_g), ("v_g", v_g),
+                    ("out", out), ("dout", dout)):
+        _check_tensor(name, t, (B, n, H, D), dtype, device)
+    _check_tensor("lse", lse, (B, H, n), torch.float32, device)
+    mask, max_global = _prep_mask(mask, B, n, device, causal, max_global, validate)
+    if grads is None:
+        grads = [torch.empty((B, n, H, D), dtype=torch.float32, device=device) for _ in range(6)]
+    for name, t in zip(("dq", "dk", "dv", "dq_g", "dk_g", "dv_g"), grads):
+        _check_tensor(name, t, (B, n, H, D), torch.float32, device)
     p, _keep = make_params(B, n, H, D, window, dilation, causal, scale, max_global, dtype)
     lib = library()
-    need = int(lib.lf_attn_workspace_bytes(ctypes.byref(p)))
+    need = int(lib.lf_attn_backward_workspace_bytes(ctypes.byref(p)))
     if need == 0:
-        raise LfError(LF_ERR_INVALID_ARG, "lf_attn_workspace_bytes")
+        raise LfError(LF_ERR_INVALID_ARG, "lf_attn_backward_workspace_bytes")
     stream = torch.cuda.current_stream(device).cuda_stream
-    ws = _workspace(need, device, stream, (B, H))
+    key = (device.index, stream)
+    with _ws_lock:
+        ws = _bwd_ws.get(key)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+            st = lib.lf_attn_workspace_init(ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+                                            ctypes.c_void_p(stream))
+            if st != LF_OK:
+                raise LfError(st, "lf_attn_workspace_init")
+            _bwd_ws[key] = ws
     vp = ctypes.c_void_p
-    st = lib.lf_attn_forward(
-        ctypes.byref(p), vp(q.data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()),
-        vp(q_g.data_ptr()), vp(k_g.data_ptr()), vp(v_g.data_ptr()), vp(mask.data_ptr()),
-        vp(out.data_ptr()), vp(row_nnz.data_ptr() if row_nnz is not None else None),
-        vp(ws.data_ptr()), ctypes.c_size_t(ws.numel()), vp(stream))
+    st = lib.lf_attn_backward(
+        ctypes.byref(p), *[vp(t.data_ptr()) for t in (q, k, v, q_g, k_g, v_g, mask, out, dout, lse)],
+        *[vp(t.data_ptr()) for t in grads], vp(ws.data_ptr()), ctypes.c_size_t(ws.numel()), vp(stream))
     if st != LF_OK:
-        raise LfError(st, "lf_attn_forward")
-    if return_row_nnz:
-        return out, row_nnz
-    return out
+        raise LfError(st, "lf_attn_backward")
+    return tuple(grads)
 
 
 def device_status(device: Optional[torch.device] = None) -> int:

@@ -99,9 +99,13 @@ lf_status lf_attn_workspace_init(void* workspace, size_t workspace_bytes, void* 
   return e == hipSuccess ? LF_OK : LF_ERR_HIP;
 }
 
-lf_status lf_attn_forward(const lf_attn_params* p, const void* q, const void* k, const void* v,
-                          const void* q_g, const void* k_g, const void* v_g, const int8_t* mask, void* out,
-                          int32_t* row_nnz, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+lf_status forward_impl(const lf_attn_params* p, const void* q, const void* k, const void* v, const void* q_g,
+                       const void* k_g, const void* v_g, const int8_t* mask, void* out, int32_t* row_nnz,
+                       float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   Plan pl;
   const lf_status st = make_plan(p, pl);
   if (st != LF_OK) return st;
@@ -121,8 +125,17 @@ lf_status lf_attn_forward(const lf_attn_params* p, const void* q, const void* k,
       if (overlaps(row_nnz, nb, in, tb)) return LF_ERR_INVALID_ARG;
     if (overlaps(row_nnz, nb, out, tb) || overlaps(row_nnz, nb, mask, mb)) return LF_ERR_INVALID_ARG;
   }
+  if (lse) {
+    const size_t lb = (size_t)p->B * p->H * p->n * sizeof(float);
+    for (const void* in : ins)
+      if (overlaps(lse, lb, in, tb)) return LF_ERR_INVALID_ARG;
+    if (overlaps(lse, lb, out, tb) || overlaps(lse, lb, mask, mb)) return LF_ERR_INVALID_ARG;
+    if (row_nnz && overlaps(lse, lb, row_nnz, nb)) return LF_ERR_INVALID_ARG;
+  }
   if (!workspace || workspace_bytes < pl.ws_bytes) return LF_ERR_WORKSPACE;
   if (overlaps(workspace, pl.ws_bytes, out, tb)) return LF_ERR_INVALID_ARG;
+  if (lse && overlaps(workspace, pl.ws_bytes, lse, (size_t)p->B * p->H * p->n * sizeof(float)))
+    return LF_ERR_INVALID_ARG;
 
   lf::KernelParams kp;
   std::memset(&kp, 0, sizeof(kp));
@@ -135,6 +148,7 @@ lf_status lf_attn_forward(const lf_attn_params* p, const void* q, const void* k,
   kp.mask = mask;
   kp.out = out;
   kp.row_nnz = row_nnz;
+  kp.lse = lse;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   kp.status = reinterpret_cast<int32_t*>(ws);
   kp.tickets = reinterpret_cast<int32_t*>(ws + pl.ws_tickets_off);
@@ -171,6 +185,152 @@ lf_status lf_attn_forward(const lf_attn_params* p, const void* q, const void* k,
     if (pl.dil[h] != pl.dil[0]) kp.uni_dil = 0;
   kp.tiles_per_head = kp.uni_dil > 0 ? pl.tile0[1] - pl.tile0[0] : 0;
   const int e = lf::launch_forward(kp, p->dtype, stream);
+  return e == 0 ? LF_OK : LF_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+lf_status lf_attn_forward(const lf_attn_params* p, const void* q, const void* k, const void* v,
+                          const void* q_g, const void* k_g, const void* v_g, const int8_t* mask, void* out,
+                          int32_t* row_nnz, void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(p, q, k, v, q_g, k_g, v_g, mask, out, row_nnz, nullptr, workspace, workspace_bytes, stream);
+}
+
+lf_status lf_attn_forward_lse(const lf_attn_params* p, const void* q, const void* k, const void* v,
+                              const void* q_g, const void* k_g, const void* v_g, const int8_t* mask, void* out,
+                              int32_t* row_nnz, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (!lse) return LF_ERR_INVALID_ARG;
+  return forward_impl(p, q, k, v, q_g, k_g, v_g, mask, out, row_nnz, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+struct BwdLayout {
+  size_t gcount_off = 0, glist_off = 0, dsum_off = 0, bytes = 0;
+  int gstride = 1;
+};
+
+BwdLayout bwd_layout(const lf_attn_params* p) {
+  BwdLayout L;
+  L.gstride = p->max_global > 0 ? p->max_global : 1;
+  L.gcount_off = kAlign;
+  L.glist_off = L.gcount_off + align_up((size_t)p->B * sizeof(int32_t), kAlign);
+  L.dsum_off = L.glist_off + align_up((size_t)p->B * L.gstride * sizeof(int32_t), kAlign);
+  L.bytes = L.dsum_off + align_up((size_t)p->B * p->H * p->n * sizeof(float), kAlign);
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lf_attn_backward_workspace_bytes(const lf_attn_params* p) {
+  Plan pl;
+  if (make_plan(p, pl) != LF_OK) return 0;
+  return bwd_layout(p).bytes;
+}
+
+lf_status lf_attn_backward(const lf_attn_params* p, const void* q, const void* k, const void* v,
+                           const void* q_g, const void* k_g, const void* v_g, const int8_t* mask,
+                           const void* out, const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                           float* dq_g, float* dk_g, float* dv_g, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  Plan pl;
+  const lf_status st = make_plan(p, pl);
+  if (st != LF_OK) return st;
+  if (p->dtype != LF_BF16 && p->dtype != LF_F16) return LF_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !mask || !out || !dout || !lse) return LF_ERR_INVALID_ARG;
+  if (!dq || !dk || !dv || !dq_g || !dk_g || !dv_g) return LF_ERR_INVALID_ARG;
+  if (!q_g) q_g = q;
+  if (!k_g) k_g = k;
+  if (!v_g) v_g = v;
+  const size_t tb = pl.tensor_bytes;
+  const size_t gb = tb / pl.elem * sizeof(float);
+  const size_t mb = (size_t)p->B * p->n;
+  const size_t lb = (size_t)p->B * p->H * p->n * sizeof(float);
+  const BwdLayout L = bwd_layout(p);
+  // per-head residue tiles of 32 rows
+  int64_t tiles = 0;
+  lf::BwdParams bp;
+  std::memset(&bp, 0, sizeof(bp));
+  for (int h = 0; h < p->H; ++h) {
+    const int d = pl.dil[h];
+    const int64_t per_class = ((p->n + d - 1) / d + 31) / 32;
+    bp.dil[h] = d;
+    bp.rtiles[h] = (int32_t)per_class;
+    bp.tile0[h] = (int32_t)tiles;
+    tiles += per_class * d;
+  }
+  bp.tile0[p->H] = (int32_t)tiles;
+  const int64_t gslots = (p->max_global + 31) / 32;
+  const int64_t chunks = (p->n + lf::kBwdChunk - 1) / lf::kBwdChunk;
+  const int64_t bhn = (int64_t)p->B * p->H;
+  const int64_t n_gkv = pl.use_globals ? bhn * ((p->n + 31) / 32) : 0;
+  const int64_t n_gq = pl.use_globals ? bhn * gslots * chunks : 0;
+  const int64_t grid = 2 * (int64_t)p->B * tiles + n_gkv + 2 * n_gq;
+  if (grid > INT32_MAX) return LF_ERR_UNSUPPORTED;
+
+  const void* ins[10] = {q, k, v, q_g, k_g, v_g, out, dout, mask, lse};
+  const size_t in_bytes[10] = {tb, tb, tb, tb, tb, tb, tb, tb, mb, lb};
+  float* outs[6] = {dq, dk, dv, dq_g, dk_g, dv_g};
+  for (int i = 0; i < 6; ++i) {
+    for (int j = 0; j < 10; ++j)
+      if (overlaps(outs[i], gb, ins[j], in_bytes[j])) return LF_ERR_INVALID_ARG;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], gb, outs[j], gb)) return LF_ERR_INVALID_ARG;
+  }
+  if (!workspace || workspace_bytes < L.bytes) return LF_ERR_WORKSPACE;
+  for (int i = 0; i < 6; ++i)
+    if (overlaps(workspace, L.bytes, outs[i], gb)) return LF_ERR_INVALID_ARG;
+  for (int j = 0; j < 10; ++j)
+    if (overlaps(workspace, L.bytes, ins[j], in_bytes[j])) return LF_ERR_INVALID_ARG;
+
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.qg = q_g;
+  bp.kg = k_g;
+  bp.vg = v_g;
+  bp.mask = mask;
+  bp.out = out;
+  bp.dout = dout;
+  bp.lse = lse;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.dqg = dq_g;
+  bp.dkg = dk_g;
+  bp.dvg = dv_g;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  bp.status = reinterpret_cast<int32_t*>(ws);
+  bp.gcount = reinterpret_cast<int32_t*>(ws + L.gcount_off);
+  bp.glist = reinterpret_cast<int32_t*>(ws + L.glist_off);
+  bp.Dsum = reinterpret_cast<float*>(ws + L.dsum_off);
+  bp.B = p->B;
+  bp.n = p->n;
+  bp.H = p->H;
+  bp.w = p->window;
+  bp.causal = p->causal;
+  bp.max_global = p->max_global;
+  bp.use_globals = pl.use_globals;
+  bp.dtype = p->dtype;
+  const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / std::sqrt((double)p->D);
+  bp.scale = (float)scale;
+  bp.c = (float)(scale * 1.4426950408889634);
+  bp.tiles_per_b = (int32_t)tiles;
+  bp.n_res = (int32_t)(p->B * tiles);
+  bp.n_gkv = (int32_t)n_gkv;
+  bp.n_gq = (int32_t)n_gq;
+  bp.n_gk = (int32_t)n_gq;
+  bp.gslots = (int32_t)gslots;
+  bp.chunks = (int32_t)chunks;
+  bp.gstride = L.gstride;
+  const int e = lf::launch_backward(bp, stream);
   return e == 0 ? LF_OK : LF_ERR_HIP;
 }
 

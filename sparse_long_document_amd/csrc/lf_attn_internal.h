@@ -33,6 +33,7 @@ struct KernelParams {
   const int8_t* mask;
   void* out;
   int32_t* row_nnz;    // may be null
+  float* lse;          // may be null: natural log-sum-exp of each row's scores [B][H][n]
   int32_t* status;     // device status word
   int32_t* tickets;    // [B*H] arrival counters of the global-row splits
   float* partials;     // [B][H][max_global][S][kPartialStride]
@@ -48,6 +49,52 @@ struct KernelParams {
   int32_t dil[LF_MAX_HEADS];
   int32_t tile0[LF_MAX_HEADS + 1];  // first band tile of each head within a batch row
 };
+
+// Backward: keys or rows per global-work unit.
+constexpr int kBwdChunk = 512;
+
+// Everything the backward launches need.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* qg;
+  const void* kg;
+  const void* vg;
+  const int8_t* mask;
+  const void* out;
+  const void* dout;
+  const float* lse;    // [B][H][n] natural log-sum-exp saved by the forward
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dqg;
+  float* dkg;
+  float* dvg;
+  float* Dsum;         // [B][H][n] workspace: <dout, out> per row
+  int32_t* glist;      // [B][gstride] workspace: global positions, ascending
+  int32_t* gcount;     // [B] workspace: entries of glist in use
+  int32_t* status;     // device status word
+  int32_t B, n, H, w, causal, max_global, use_globals, dtype;
+  float c;             // score scale * log2(e)
+  float scale;
+  int32_t tiles_per_b; // 32-row residue tiles per batch row, all heads
+  int32_t n_res;       // B * tiles_per_b
+  int32_t n_gkv;       // units of the global rows' key work: B * H * ceil(n / 32)
+  int32_t n_gq;        // units of the global rows' query work
+  int32_t n_gk;        // units of the global keys' work of local rows
+  int32_t gslots;      // ceil(max_global / 32)
+  int32_t chunks;      // ceil(n / kBwdChunk)
+  int32_t gstride;     // max(max_global, 1)
+  int32_t dil[LF_MAX_HEADS];
+  int32_t tile0[LF_MAX_HEADS + 1];  // first residue tile of each head within a batch row
+  int32_t rtiles[LF_MAX_HEADS];     // tiles per residue class of each head: ceil(ceil(n / d) / 32)
+};
+
+// Launches the backward (global list, preparation, main kernel) for bf16 or
+// f16 elements.  Returns the hipError_t value as int.
+int launch_backward(const BwdParams& bp, void* stream);
+int launch_backward_f16(const BwdParams& bp, void* stream);
 
 // Launches the forward kernel.  Returns the hipError_t value as int.
 int launch_forward(const KernelParams& kp, int dtype, void* stream);

@@ -97,6 +97,12 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kMInit = -1.0e30f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
 
+// Natural log-sum-exp of a row's scaled scores from its log2-domain
+// reference max M and the row sum L = sum_j 2^(c s_j - M).
+__device__ __forceinline__ float row_lse(float M, float L) {
+  return (M + __builtin_amdgcn_logf(L)) * 0.69314718055994531f;
+}
+
 // LDS staging of key blocks.  A stage holds one block's K rows then its V
 // rows (32 rows of 64 head dims each); each key parity owns a ring of
 // kStages stages, filled by direct-to-LDS loads while older stages are
@@ -1466,6 +1472,7 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
       const int qp = src.qpos();
       store_quadrant<B16>(out + (size_t)qp * rs, kp, hh, nullptr, 0.f, true);
       if (p.row_nnz && kp == 0 && hh == 0) p.row_nnz[((size_t)b * p.H + h) * n + qp] = 0;
+      if (p.lse && kp == 0 && hh == 0) p.lse[((size_t)b * p.H + h) * n + qp] = kNegInf;
     }
     return;
   }
@@ -1522,11 +1529,13 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
   if constexpr (B16) {
     if (vec_g && kp == 0 && active) vec_global_columns(st, qf, src, vrows, p.c);
   }
-  merge_parities<B16>(st, sh, qh, kp, [&](int db, float, float Lsum, int cnt, const float* o) {
+  merge_parities<B16>(st, sh, qh, kp, [&](int db, float M, float Lsum, int cnt, const float* o) {
     if (!my_local && !my_zero) return;
     const int qp = src.qpos();
     store_quadrant<B16>(out + (size_t)qp * rs, db, hh, o, my_local ? 1.0f / Lsum : 0.f, !my_local);
     if (p.row_nnz && db == 0 && hh == 0) p.row_nnz[((size_t)b * p.H + h) * n + qp] = my_local ? cnt : 0;
+    if (p.lse && db == 0 && hh == 0)
+      p.lse[((size_t)b * p.H + h) * n + qp] = my_local ? row_lse(M, Lsum) : kNegInf;
   });
 }
 
@@ -1747,6 +1756,7 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
     for (int e = 0; e < 4; ++e) v4[e] = acc[e] * inv;
     store4<B16>(out + (size_t)pos * rs + 4 * q4, v4);
     if (p.row_nnz && q4 == 0) p.row_nnz[(size_t)bh * n + pos] = cnt;
+    if (p.lse && q4 == 0) p.lse[(size_t)bh * n + pos] = row_lse(M, Lsum);
   }
   __syncthreads();
   if (wv == 0 && lane_id_here() == 0) __hip_atomic_store(p.tickets + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -1,0 +1,129 @@
+"""Parity of the HIP backward (through the C ABI) with the fp64 gradient
+oracle, and of the forward's saved log-sum-exp with the oracle's.
+
+Tolerances.  lse: |lse - oracle| <= 5e-3 (the row sum adds probabilities
+rounded to the element type, relative error at most 2^-9, so the log is off
+by at most about 2e-3).  Gradients: for each of the six fp32 results,
+max |g - oracle| <= tol * max |oracle| with tol 2e-2 for bf16 and 5e-3 for
+f16: the GPU rounds P and dS to the element type before the gradient
+products (relative 2^-9 in bf16, 2^-12 in f16 per term) and takes D from the
+forward's rounded output, so errors stay a few 2^-9 of the largest entry;
+a gradient that is exactly zero keeps fp32 rounding residue below 1e-5.
+Small problems are compared with the full oracle; the benchmark workload at
+full size on two heads, with closed-form column sums on every head.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_long_document_amd as lf
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: 2e-2, torch.float16: 5e-3}
+NAMES = ("dq", "dk", "dv", "dq_g", "dk_g", "dv_g")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lf.library()
+
+
+def run_gpu(prob, dout):
+    _say(f"[gpu bwd] {prob.name} shape={prob.shape} w={prob.window} dil={prob.dilation} "
+         f"causal={prob.causal} dtype={prob.q.dtype}")
+    d = torch.device("cuda")
+    t = [x.to(d) for x in (prob.q, prob.k, prob.v, prob.q_g, prob.k_g, prob.v_g)]
+    mask = prob.mask.to(d)
+    out, lse = lf.forward(*t, mask=mask, window=prob.window, dilation=prob.dilation,
+                          causal=prob.causal, scale=prob.scale, return_lse=True)
+    grads = lf.backward(*t, mask, out, dout.to(d), lse, window=prob.window, dilation=prob.dilation,
+                        causal=prob.causal, scale=prob.scale)
+    torch.cuda.synchronize()
+    assert lf.device_status() == 0
+    return lse.cpu().numpy().astype(np.float64), [g.cpu().numpy().astype(np.float64) for g in grads]
+
+
+def _np(prob):
+    return [x.float().numpy() for x in (prob.q, prob.k, prob.v, prob.q_g, prob.k_g, prob.v_g)]
+
+
+def check(prob, dout, heads=None):
+    lse, grads = run_gpu(prob, dout)
+    t = _np(prob)
+    m = prob.mask.numpy()
+    ref_lse = oracle.row_lse(t[0], t[1], t[3], t[4], m, prob.window, dilation=prob.dilation,
+                             causal=prob.causal, scale=prob.scale)
+    hs = list(range(prob.shape[2])) if heads is None else list(heads)
+    fin = np.isfinite(ref_lse[:, hs])
+    assert (np.isneginf(lse[:, hs]) == ~fin).all()
+    lerr = np.abs(lse[:, hs][fin] - ref_lse[:, hs][fin]).max() if fin.any() else 0.0
+    _say(f"      lse max abs err {lerr:.3e}")
+    assert lerr <= 5e-3
+    ref = oracle.backward(*t, m, dout.float().numpy(), prob.window, dilation=prob.dilation,
+                          causal=prob.causal, scale=prob.scale, heads=heads)
+    tol = TOL[prob.q.dtype]
+    for name, g, r in zip(NAMES, grads, ref):
+        g, r = g[:, :, hs], r[:, :, hs]
+        big = np.abs(r).max()
+        err = np.abs(g - r).max()
+        _say(f"      {name}: max abs err {err:.3e} of max {big:.3e}")
+        # a gradient that is zero in exact arithmetic (w = 0: out = v, so
+        # dp - D vanishes) keeps fp32 rounding residue
+        assert err <= max(tol * big, 1e-5), (name, err, big)
+    return grads
+
+
+SMALL = [
+    dict(B=1, n=300, H=2, window=40, dilation=[1, 2], global_positions=[0, 137], pad_tail=23),
+    dict(B=2, n=517, H=3, window=64, dilation=[1, 2, 3], causal=True, zero_frac=0.02),
+    dict(B=1, n=1100, H=1, window=16, n_global=40),
+    dict(B=1, n=70, H=1, window=0),
+    dict(B=1, n=45, H=2, window=100, n_global=3),
+    dict(B=2, n=640, H=2, window=33, n_global=5, pad_tail=100, aliased_global=True),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_backward_small(case, dtype):
+    kw = dict(SMALL[case])
+    prob = workloads.random_problem(300 + case, dtype=dtype, name=f"bwd_small{case}", **kw)
+    dout = workloads.upstream_grad(300 + case, prob.shape, dtype)
+    check(prob, dout)
+
+
+def test_backward_longformer_base_two_heads():
+    """The benchmark workload (B1 n4096 H12 w256, token 0 global) at full size:
+    heads 0 and 11 against the oracle; every head by closed-form sums."""
+    prob = workloads.by_name("longformer_base_n4096")
+    dout = workloads.upstream_grad(2, prob.shape, prob.q.dtype)
+    grads = check(prob, dout, heads=[0, 11])
+    dq, dk, dv, dqg, dkg, dvg = grads
+    m = prob.mask.numpy()[0]
+    do = dout.float().numpy()[0]
+    for h in range(prob.shape[2]):
+        sv = dv[0, :, h].sum(0)
+        np.testing.assert_allclose(sv, do[m == 1, h].sum(0), atol=2e-2 * np.abs(sv).max() + 1e-3)
+        np.testing.assert_allclose(dvg[0, :, h].sum(0), do[m == 2, h].sum(0), atol=2e-2)
+        assert np.abs(dk[0, :, h].sum(0)).max() <= 2e-2 * np.abs(dk[0, :, h]).sum(0).max()
+
+
+def test_backward_rejects_fp32():
+    prob = workloads.random_problem(9, 1, 64, 1, 8, dtype=torch.float32)
+    d = torch.device("cuda")
+    t = [x.to(d) for x in (prob.q, prob.k, prob.v)]
+    out, lse = lf.forward(*t, window=8, return_lse=True)
+    with pytest.raises(lf.LfError):
+        lf.backward(*t, None, None, None, None, out, out, lse, window=8)

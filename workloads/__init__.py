@@ -85,6 +85,12 @@ def _draw(rng: np.random.Generator, shape, dtype: torch.dtype) -> torch.Tensor:
     return torch.from_numpy(a).to(dtype)
 
 
+def upstream_grad(seed: int, shape, dtype: torch.dtype) -> torch.Tensor:
+    """A seeded upstream gradient of the output, standard normal in ``dtype``
+    (its own stream: seed + 1000)."""
+    return _draw(np.random.Generator(np.random.PCG64(seed + 1000)), shape, dtype)
+
+
 def random_problem(
     seed: int,
     B: int,
