@@ -8,7 +8,11 @@ Default workload: the longformer-base layer shape, B=1, n=4096, H=12, D=64,
 one-sided window 256, bf16, token 0 global.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu-baseline] [--no-check] [--eager]
+                  [--no-cpu-baseline] [--no-check] [--eager] [--pass backward]
+
+With --pass backward a step is one lf_attn_backward (preparation with the
+global lists, then the gradient kernel) on the same workload, from the output and
+row log-sum-exp of one lf_attn_forward_lse and a seeded upstream gradient.
 """
 from __future__ import annotations
 
@@ -89,6 +93,103 @@ class Runner:
             raise RuntimeError(f"lf_attn_forward failed with status {st}")
 
 
+def backward_flops(prob) -> float:
+    """Useful band FLOPs of one backward: per scored window pair, the score
+    recomputed once and the four gradient products dP, dV, dQ, dK, each
+    2*D: 2.5 times the forward's count."""
+    return 2.5 * band_flops(prob)
+
+
+class BwdRunner:
+    """Prepared arguments for repeated lf_attn_backward calls: out and lse
+    from one lf_attn_forward_lse, a seeded upstream gradient."""
+
+    def __init__(self, prob, device):
+        import torch
+
+        import sparse_long_document_amd as lf
+        import workloads
+
+        self.prob = prob
+        self.t = [x.to(device).contiguous() for x in (prob.q, prob.k, prob.v, prob.q_g, prob.k_g, prob.v_g)]
+        self.mask = prob.mask.to(device).contiguous()
+        self.dout = workloads.upstream_grad(2, prob.shape, prob.q.dtype).to(device)
+        self.max_global = 0 if prob.causal else prob.max_global()
+        self.out, self.lse = lf.forward(*self.t, mask=self.mask, window=prob.window, dilation=prob.dilation,
+                                        causal=prob.causal, scale=prob.scale, return_lse=True,
+                                        max_global=self.max_global, validate=False)
+        B, n, H, D = prob.shape
+        self.grads = [torch.empty((B, n, H, D), dtype=torch.float32, device=device) for _ in range(6)]
+        self.params, self._keep = lf.make_params(B, n, H, D, prob.window, prob.dilation, prob.causal,
+                                                 prob.scale, self.max_global, prob.q.dtype)
+        lib = lf.library()
+        need = lib.lf_attn_backward_workspace_bytes(ctypes.byref(self.params))
+        self.stream = torch.cuda.current_stream(device).cuda_stream
+        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        st = lib.lf_attn_workspace_init(ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(),
+                                        ctypes.c_void_p(self.stream))
+        assert st == 0, st
+        vp = ctypes.c_void_p
+        self.args = (ctypes.byref(self.params), *[vp(x.data_ptr()) for x in self.t], vp(self.mask.data_ptr()),
+                     vp(self.out.data_ptr()), vp(self.dout.data_ptr()), vp(self.lse.data_ptr()),
+                     *[vp(g.data_ptr()) for g in self.grads], vp(self.ws.data_ptr()),
+                     ctypes.c_size_t(self.ws.numel()), vp(self.stream))
+        self.fn = lib.lf_attn_backward
+        self.out_t = self.grads[0]  # dq: written without atomics, compared across graph replays
+
+    def launch(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"lf_attn_backward failed with status {st}")
+
+
+def check_backward(prob, run):
+    """Closed forms that hold at any size, on every head: summed over
+    tokens, dv equals the upstream gradient summed over local rows (dv_g:
+    over global rows), and dk sums to zero (relative to its column mass)."""
+    import numpy as np
+
+    dq, dk, dv, dqg, dkg, dvg = [g.double().cpu().numpy() for g in run.grads]
+    m = prob.mask.numpy()
+    do = run.dout.double().cpu().numpy()
+    worst = 0.0
+    B, n, H, D = prob.shape
+    for b in range(B):
+        for h in range(H):
+            ref = do[b, m[b] == 1, h].sum(0)
+            worst = max(worst, np.abs(dv[b, :, h].sum(0) - ref).max() / max(np.abs(ref).max(), 1e-3))
+            refg = do[b, m[b] == 2, h].sum(0)
+            if (m[b] == 2).any():
+                worst = max(worst, np.abs(dvg[b, :, h].sum(0) - refg).max() / max(np.abs(refg).max(), 1e-3))
+            mass = np.abs(dk[b, :, h]).sum(0).max()
+            worst = max(worst, np.abs(dk[b, :, h].sum(0)).max() / max(mass, 1e-30))
+    return {"kind": "closed-form column sums, every (b, h)", "max_rel_err": float(worst),
+            "tol": 2e-2, "ok": bool(worst <= 2e-2)}
+
+
+def cpu_baseline_backward(prob):
+    """The fp64 gradient oracle on one host thread, on one (b, h) of the
+    workload at full length, scaled to tokens/s of the whole job."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    torch.set_num_threads(1)
+    t = [x.float().numpy() for x in (prob.q, prob.k, prob.v, prob.q_g, prob.k_g, prob.v_g)]
+    dout = workloads.upstream_grad(2, prob.shape, prob.q.dtype).float().numpy()
+    B, n, H, D = prob.shape
+    t0 = time.perf_counter()
+    hs = list(range(min(H, 2)))
+    oracle.backward(*[x[:1] for x in t], prob.mask.numpy()[:1], dout[:1], prob.window,
+                    dilation=prob.dilation, causal=prob.causal, scale=prob.scale, heads=hs)
+    dt = time.perf_counter() - t0
+    return {"value": B * n * len(hs) / (dt * H * B), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"batch row 0, heads 0..{len(hs) - 1} of {H}, all {n} tokens ({dt:.1f} s), "
+                      "scaled to B*H"}
+
+
 def check_parity(prob, out, row_nnz, max_rows=48):
     """Sampled rows of the timed output against the fp64 oracle."""
     import numpy as np
@@ -164,6 +265,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time direct launches instead of a graph replay")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU layout of this "
@@ -178,7 +280,8 @@ def main():
     prob = workloads.by_name(args.workload)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    run = Runner(prob, dev)
+    bwd = args.which == "backward"
+    run = BwdRunner(prob, dev) if bwd else Runner(prob, dev)
     for _ in range(max(1, args.warmup)):
         run.launch()
     torch.cuda.synchronize()
@@ -188,7 +291,7 @@ def main():
     graph = None
     if not args.eager:
         try:
-            ref = run.out.clone()
+            ref = (run.out_t if bwd else run.out).clone()
             per = max(d for d in range(1, min(K, 50) + 1) if K % d == 0)
             s = torch.cuda.Stream()
             s.wait_stream(torch.cuda.current_stream())
@@ -204,7 +307,7 @@ def main():
             torch.cuda.synchronize()
             graph.replay()
             torch.cuda.synchronize()
-            if not torch.equal(ref, run.out):
+            if not torch.equal(ref, run.out_t if bwd else run.out):
                 raise RuntimeError("graph replay output differs from the eager launch")
             mode = f"graph({per} launches per replay)"
         except Exception as e:  # fall back to eager timing
@@ -232,6 +335,8 @@ def main():
     ms = start.elapsed_time(end) / K
 
     B, n, H, D = prob.shape
+    if bwd:
+        return report_backward(args, prob, run, ms, mode, t_wall)
     flops = band_flops(prob)
     achieved = flops / (ms * 1e-3) / 1e12
     # dense MFMA peak of the element type (f16 and bf16 share one)
@@ -279,6 +384,43 @@ def main():
         result["parity"] = check_parity(prob, run.out, run.row_nnz)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(prob)
+    print(json.dumps(result), flush=True)
+
+
+def report_backward(args, prob, run, ms, mode, t_wall):
+    import torch
+
+    B, n, H, D = prob.shape
+    flops = backward_flops(prob)
+    achieved = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS
+    dname = {torch.bfloat16: "bf16", torch.float16: "f16"}[prob.q.dtype]
+    result = {
+        "metric": "sliding-window attn bwd tokens/s (all six input gradients), bf16; MFMA util %",
+        "value": B * n / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dname,
+        "data": "synthetic (seeded N(0,1) inputs and upstream gradient, mask per workload recipe)",
+        "config": {"workload": args.workload, "pass": "backward", "B": B, "n": n, "H": H, "D": D,
+                   "w": prob.window, "causal": prob.causal, "dilation": prob.dilation,
+                   "globals_per_row": [int(x) for x in (prob.mask == 2).sum(dim=1).tolist()],
+                   "timing": mode, "wall_s": round(t_wall, 3)},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None,
+                     "kernel": f"lf_attn_bwd<{dname}> (whole backward: 2 launches)",
+                     "flops_per_launch": flops},
+    }
+    if not args.no_check:
+        result["parity"] = check_backward(prob, run)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_backward(prob)
     print(json.dumps(result), flush=True)
 
 

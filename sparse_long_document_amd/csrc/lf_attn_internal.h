@@ -91,8 +91,8 @@ struct BwdParams {
   int32_t rtiles[LF_MAX_HEADS];     // tiles per residue class of each head: ceil(ceil(n / d) / 32)
 };
 
-// Launches the backward (global list, preparation, main kernel) for bf16 or
-// f16 elements.  Returns the hipError_t value as int.
+// Launches the backward (preparation with the global lists, then the
+// gradient kernel) for bf16 or f16 elements.  Returns the hipError_t value as int.
 int launch_backward(const BwdParams& bp, void* stream);
 int launch_backward_f16(const BwdParams& bp, void* stream);
 
