@@ -163,3 +163,54 @@ def test_merge_masks():
     g = torch.tensor([[1, 0, 0, 1]])
     assert lf.merge_masks(a, g).tolist() == [[2, 1, 1, 0]]
     assert lf.merge_masks(a, g).dtype == torch.int8
+
+
+# ---------------------------------------------------------------------------
+# lf_attn_forward_lse and lf_attn_backward: argument checks (no HIP call)
+# ---------------------------------------------------------------------------
+
+def _backward(p, ptrs=None, ws_bytes=1 << 30):
+    lib = lf.library()
+    vp = ctypes.c_void_p
+    names = ("q", "k", "v", "qg", "kg", "vg", "mask", "out", "dout", "lse",
+             "dq", "dk", "dv", "dqg", "dkg", "dvg", "ws")
+    base = {nm: FAKE + (i << 32) for i, nm in enumerate(names)}
+    base.update(qg=None, kg=None, vg=None)
+    base.update(ptrs or {})
+    return lib.lf_attn_backward(ctypes.byref(p), *[vp(base[nm]) for nm in names],
+                                ctypes.c_size_t(ws_bytes), vp(None))
+
+
+def test_backward_workspace_bytes_layout():
+    # status block, B counts, B lists of max_global entries, one fp32 per row
+    p, _k = _params(B=2, n=4096, H=12, max_global=64)
+    got = lf.library().lf_attn_backward_workspace_bytes(ctypes.byref(p))
+    assert got == 256 + 256 + 512 + 2 * 12 * 4096 * 4
+    p, _k = _params(B=0)
+    assert lf.library().lf_attn_backward_workspace_bytes(ctypes.byref(p)) == 0
+
+
+def test_backward_argument_errors():
+    p, _k = _params()
+    for name in ("q", "k", "v", "mask", "out", "dout", "lse", "dq", "dk", "dv", "dqg", "dkg", "dvg"):
+        assert _backward(p, {name: None}) == lf.LF_ERR_INVALID_ARG, name
+    assert _backward(p, {"dk": FAKE + (10 << 32)}) == lf.LF_ERR_INVALID_ARG  # dk == dq
+    assert _backward(p, {"dq": FAKE + 64}) == lf.LF_ERR_INVALID_ARG  # dq overlaps q
+    assert _backward(p, {"ws": None}) == lf.LF_ERR_WORKSPACE
+    need = lf.library().lf_attn_backward_workspace_bytes(ctypes.byref(p))
+    assert _backward(p, ws_bytes=need - 1) == lf.LF_ERR_WORKSPACE
+    p32, _k = _params(dtype=torch.float32)
+    assert _backward(p32) == lf.LF_ERR_UNSUPPORTED
+
+
+def test_forward_lse_requires_lse():
+    p, _k = _params()
+    lib = lf.library()
+    vp = ctypes.c_void_p
+    args = [vp(FAKE), vp(FAKE + (1 << 32)), vp(FAKE + (2 << 32)), vp(None), vp(None), vp(None),
+            vp(FAKE + (3 << 32)), vp(FAKE + (4 << 32)), vp(None)]
+    ws = [vp(FAKE + (5 << 32)), ctypes.c_size_t(1 << 30), vp(None)]
+    assert lib.lf_attn_forward_lse(ctypes.byref(p), *args, vp(None), *ws) == lf.LF_ERR_INVALID_ARG
+    # lse overlapping the output
+    assert lib.lf_attn_forward_lse(ctypes.byref(p), *args, vp(FAKE + (4 << 32) + 256), *ws) \
+        == lf.LF_ERR_INVALID_ARG

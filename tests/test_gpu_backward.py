@@ -92,6 +92,8 @@ SMALL = [
     dict(B=1, n=70, H=1, window=0),
     dict(B=1, n=45, H=2, window=100, n_global=3),
     dict(B=2, n=640, H=2, window=33, n_global=5, pad_tail=100, aliased_global=True),
+    dict(B=2, n=900, H=2, window=48, dilation=[1, 3], n_global=2, zero_frac=0.05),
+    dict(B=1, n=2100, H=1, window=300, n_global=70, pad_tail=31),
 ]
 
 
