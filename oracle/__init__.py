@@ -1,5 +1,5 @@
 """Oracle package: plain fp64 CPU implementation of the Longformer combined
-attention forward and of its gradients.
+attention forward, of its gradients and of its input projections.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by
 the benchmark's CPU-baseline leg, never by the product library.  It shares
@@ -14,3 +14,4 @@ from .longformer_attention import (  # noqa: F401
     pattern,
 )
 from .longformer_backward import backward, row_lse  # noqa: F401,E402
+from .projections import project  # noqa: F401,E402
