@@ -10,6 +10,10 @@ one-sided window 256, bf16, token 0 global.  Prints one JSON line.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline] [--no-check] [--eager] [--pass backward]
 
+With --pass projections a step is one lf_attn_project: the six input
+projections (Q_s, K_s, V_s, Q_g, K_g, V_g) of the workload's B*n tokens
+from C = H*64 hidden features.
+
 With --pass backward a step is one lf_attn_backward (preparation with the
 global lists, then the gradient kernel) on the same workload, from the output and
 row log-sum-exp of one lf_attn_forward_lse and a seeded upstream gradient.
@@ -143,6 +147,82 @@ class BwdRunner:
             raise RuntimeError(f"lf_attn_backward failed with status {st}")
 
 
+class ProjRunner:
+    """Prepared arguments for repeated lf_attn_project calls: the six
+    projections of the workload's tokens."""
+
+    def __init__(self, prob, device):
+        import torch
+
+        import sparse_long_document_amd as lf
+        import workloads
+
+        B, n, H, D = prob.shape
+        self.M, self.C, self.P = B * n, H * D, 6
+        x, w, b = workloads.projection_problem(3, self.M, self.C, self.P, prob.q.dtype)
+        self.x_cpu, self.w_cpu, self.b_cpu = x, w, b
+        self.x, self.w, self.b = x.to(device), w.to(device), b.to(device)
+        self.out = torch.empty((self.P, self.M, self.C), dtype=prob.q.dtype, device=device)
+        self.out_t = self.out
+        self.stream = torch.cuda.current_stream(device).cuda_stream
+        vp = ctypes.c_void_p
+        self.lib = lf.library()
+        self.dt = lf._DTYPES[prob.q.dtype]
+        self.args = (self.M, self.C, self.P, self.dt, vp(self.x.data_ptr()), vp(self.w.data_ptr()),
+                     vp(self.b.data_ptr()), vp(self.out.data_ptr()), vp(self.stream))
+        self.fn = self.lib.lf_attn_project
+
+    def launch(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"lf_attn_project failed with status {st}")
+
+
+def report_projections(args, prob, run, ms, mode, t_wall):
+    import numpy as np
+    import torch
+
+    import oracle
+
+    flops = 2.0 * run.M * run.C * run.P * run.C
+    achieved = flops / (ms * 1e-3) / 1e12
+    dname = {torch.bfloat16: "bf16", torch.float16: "f16"}[prob.q.dtype]
+    B, n, H, D = prob.shape
+    result = {
+        "metric": "Longformer input projections tokens/s (six C x C maps, C = H*64), bf16; MFMA util %",
+        "value": run.M / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dname,
+        "data": "synthetic (seeded N(0,1) hidden states, N(0,1/C) weights, N(0,0.01) bias)",
+        "config": {"workload": args.workload, "pass": "projections", "M": run.M, "C": run.C, "P": run.P,
+                   "timing": mode, "wall_s": round(t_wall, 3)},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": f"lf_proj_{dname}", "flops_per_launch": flops},
+    }
+    if not args.no_check:
+        rows = np.linspace(0, run.M - 1, 64).astype(np.int64)
+        ref = oracle.project(run.x_cpu.float().numpy()[rows], run.w_cpu.float().numpy(), run.b_cpu.numpy())
+        got = run.out[:, torch.from_numpy(rows).to(run.out.device)].float().cpu().numpy()
+        excess = float((np.abs(got - ref) - (2.0 ** -8 * np.abs(ref) + 1e-3)).max())
+        result["parity"] = {"kind": "64 sampled rows of all six projections vs the fp64 oracle",
+                            "max_abs_err": float(np.abs(got - ref).max()), "ok": excess <= 0}
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        xs, ws, bs = run.x_cpu.float().numpy(), run.w_cpu.float().numpy(), run.b_cpu.numpy()
+        reps, t0 = 0, time.perf_counter()
+        while reps < 3 or time.perf_counter() - t0 < 2.0:
+            oracle.project(xs, ws, bs)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        threads = max([int(t.get("num_threads", 1)) for t in threadpool_info()] or [1])
+        result["cpu_baseline"] = {"value": run.M / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                                  "sample": f"the whole job ({run.M} tokens, six projections), fp64 NumPy "
+                                            f"matmul on {threads} BLAS threads, mean of {reps} runs"}
+    print(json.dumps(result), flush=True)
+
+
 def check_backward(prob, run):
     """Closed forms that hold at any size, on every head: summed over
     tokens, dv equals the upstream gradient summed over local rows (dv_g:
@@ -265,7 +345,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time direct launches instead of a graph replay")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "projections"], default="forward")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU layout of this "
@@ -280,8 +360,8 @@ def main():
     prob = workloads.by_name(args.workload)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    bwd = args.which == "backward"
-    run = BwdRunner(prob, dev) if bwd else Runner(prob, dev)
+    bwd = args.which != "forward"  # a runner with out_t, compared across graph replays
+    run = {"forward": Runner, "backward": BwdRunner, "projections": ProjRunner}[args.which](prob, dev)
     for _ in range(max(1, args.warmup)):
         run.launch()
     torch.cuda.synchronize()
@@ -335,8 +415,10 @@ def main():
     ms = start.elapsed_time(end) / K
 
     B, n, H, D = prob.shape
-    if bwd:
+    if args.which == "backward":
         return report_backward(args, prob, run, ms, mode, t_wall)
+    if args.which == "projections":
+        return report_projections(args, prob, run, ms, mode, t_wall)
     flops = band_flops(prob)
     achieved = flops / (ms * 1e-3) / 1e12
     # dense MFMA peak of the element type (f16 and bf16 share one)

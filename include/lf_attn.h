@@ -160,6 +160,27 @@ lf_status lf_attn_backward(const lf_attn_params* p,
                            float* dq, float* dk, float* dv, float* dq_g, float* dk_g, float* dv_g,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Most projections lf_attn_project computes in one launch. */
+#define LF_MAX_PROJ 6
+
+/* Enqueue the layer's input projections on `stream` and return: P stacked
+ * linear maps of the hidden states x [M, C] (M = B*n tokens, C = H*D
+ * features, token-major, dtype LF_BF16 or LF_F16),
+ *   out[p][m][c] = sum_k x[m][k] w[p*C + c][k] + bias[p*C + c],
+ * with w [P*C, C] in the [out features, in features] layout and bias fp32
+ * [P*C] or NULL.  out is [P, M, C] of the same dtype; each out[p], viewed as
+ * [B, n, H, D], is one input of lf_attn_forward.  With P = 6 and the
+ * weights stacked as Q_s, K_s, V_s, Q_g, K_g, V_g these are the layer's
+ * sliding-window and separate global projections (segmentfault Longformer
+ * summary, "Linear projections for global attention"; the global weights
+ * start as copies of the local ones).  fp32 accumulation, the bias added in
+ * fp32, the result rounded to nearest even.  Errors: LF_ERR_INVALID_ARG for
+ * M, C or P < 1, a NULL x, w or out, or out overlapping an input;
+ * LF_ERR_UNSUPPORTED for another dtype, C not a multiple of 64, P > 6.
+ * Allocates nothing, needs no workspace. */
+lf_status lf_attn_project(int32_t M, int32_t C, int32_t P, int32_t dtype,
+                          const void* x, const void* w, const float* bias, void* out, void* stream);
+
 /* Debug helper: synchronise `stream`, then read the device status word of
  * `workspace` into *status (LF_DEV_* bits; 0 = no condition seen). */
 lf_status lf_attn_device_status(const void* workspace, void* stream, int32_t* status);

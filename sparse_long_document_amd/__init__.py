@@ -25,7 +25,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "forward", "backward", "workspace_bytes", "device_status", "pad_to_window_size",
+    "forward", "backward", "project", "workspace_bytes", "device_status", "pad_to_window_size",
     "merge_masks", "library", "LfError", "LF_MAX_GLOBAL", "LF_MAX_HEADS",
 ]
 
@@ -52,9 +52,11 @@ LF_HEAD_DIM = 64
 LF_MAX_HEADS = 64
 LF_MAX_GLOBAL = 1024
 LF_DEV_TOO_MANY_GLOBALS = 1
+LF_MAX_PROJ = 6
 
 SYMBOLS = ("lf_attn_workspace_bytes", "lf_attn_workspace_init", "lf_attn_forward",
            "lf_attn_forward_lse", "lf_attn_backward_workspace_bytes", "lf_attn_backward",
+           "lf_attn_project",
            "lf_attn_device_status", "lf_status_str")
 
 
@@ -105,6 +107,9 @@ def library() -> ctypes.CDLL:
             lib.lf_attn_backward_workspace_bytes.restype = sz
             lib.lf_attn_backward.argtypes = [ctypes.POINTER(Params)] + [vp] * 16 + [vp, sz, vp]
             lib.lf_attn_backward.restype = ctypes.c_int
+            i32 = ctypes.c_int32
+            lib.lf_attn_project.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
+            lib.lf_attn_project.restype = ctypes.c_int
             lib.lf_attn_device_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
             lib.lf_attn_device_status.restype = ctypes.c_int
             lib.lf_status_str.argtypes = [ctypes.c_int32]
@@ -250,6 +255,40 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             raise LfError(st, "lf_attn_forward")
     res = (out,) + ((row_nnz,) if return_row_nnz else ()) + ((lse,) if return_lse else ())
     return res if len(res) > 1 else out
+
+
+def project(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The layer's input projections (``lf_attn_project``): x [M, C] (or
+    [B, n, C]) bf16/f16, w [P*C, C] stacked weights in the [out, in] layout,
+    bias fp32 [P*C] or None.  Returns out [P, M, C] (or [P, B, n, C]);
+    out[p].view(B, n, H, 64) is one attention input."""
+    shape = x.shape
+    if x.dim() == 3:
+        x = x.reshape(-1, shape[-1])
+    if x.dim() != 2:
+        raise ValueError("x must be [M, C] or [B, n, C]")
+    M, C = x.shape
+    if x.device.type != "cuda":
+        raise ValueError("x must be a GPU tensor (this library has no CPU path)")
+    if w.dim() != 2 or w.shape[1] != C or w.shape[0] % C != 0:
+        raise ValueError("w must be [P*C, C]")
+    P = w.shape[0] // C
+    _check_tensor("x", x, (M, C), x.dtype, x.device)
+    _check_tensor("w", w, (P * C, C), x.dtype, x.device)
+    if bias is not None:
+        _check_tensor("bias", bias, (P * C,), torch.float32, x.device)
+    if out is None:
+        out = torch.empty((P, M, C), dtype=x.dtype, device=x.device)
+    _check_tensor("out", out, (P, M, C), x.dtype, x.device)
+    vp = ctypes.c_void_p
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = library().lf_attn_project(M, C, P, _DTYPES.get(x.dtype, 99), vp(x.data_ptr()), vp(w.data_ptr()),
+                                   vp(bias.data_ptr() if bias is not None else None), vp(out.data_ptr()),
+                                   vp(stream))
+    if st != LF_OK:
+        raise LfError(st, "lf_attn_project")
+    return out.view((P,) + tuple(shape[:-1]) + (C,))
 
 
 def _prep_mask(mask, B, n, device, causal, max_global, validate):

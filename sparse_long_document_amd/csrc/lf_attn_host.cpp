@@ -335,6 +335,30 @@ lf_status lf_attn_backward(const lf_attn_params* p, const void* q, const void* k
   return e == 0 ? LF_OK : LF_ERR_HIP;
 }
 
+lf_status lf_attn_project(int32_t M, int32_t C, int32_t P, int32_t dtype, const void* x, const void* w,
+                          const float* bias, void* out, void* stream) {
+  if (M <= 0 || C <= 0 || P <= 0) return LF_ERR_INVALID_ARG;
+  if (!x || !w || !out) return LF_ERR_INVALID_ARG;
+  if (dtype != LF_BF16 && dtype != LF_F16) return LF_ERR_UNSUPPORTED;
+  if (C % 64 != 0 || P > LF_MAX_PROJ) return LF_ERR_UNSUPPORTED;
+  const int64_t N = (int64_t)P * C;
+  if (N > INT32_MAX || (N + 127) / 128 > 65535) return LF_ERR_UNSUPPORTED;
+  const size_t xb = (size_t)M * C * 2, wb = (size_t)N * C * 2, ob = (size_t)P * xb, bb = (size_t)N * 4;
+  if (overlaps(out, ob, x, xb) || overlaps(out, ob, w, wb) || (bias && overlaps(out, ob, bias, bb)))
+    return LF_ERR_INVALID_ARG;
+  lf::ProjParams pp;
+  pp.x = x;
+  pp.w = w;
+  pp.bias = bias;
+  pp.out = out;
+  pp.M = M;
+  pp.C = C;
+  pp.N = (int32_t)N;
+  pp.dtype = dtype;
+  const int e = lf::launch_project(pp, stream);
+  return e == 0 ? LF_OK : LF_ERR_HIP;
+}
+
 lf_status lf_attn_device_status(const void* workspace, void* stream, int32_t* status) {
   if (!workspace || !status) return LF_ERR_INVALID_ARG;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

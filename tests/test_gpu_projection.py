@@ -1,0 +1,86 @@
+"""Parity of the HIP input projections (through the C ABI) with the fp64
+projection oracle, and of projections followed by the attention forward with
+the two oracles chained.
+
+Tolerance: |y - oracle| <= 2^-8 |oracle| + 1e-3 for bf16 (the kernel
+accumulates in fp32 and rounds once to nearest even: half a bf16 ulp is at
+most 2^-9 relative, fp32 accumulation over C <= 1024 terms adds well under
+1e-3) and 2^-10 |oracle| + 1e-3 for f16.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_long_document_amd as lf
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+REL = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -10}
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lf.library()
+
+
+def check(seed, M, C, P, dtype, with_bias=True):
+    _say(f"[gpu proj] M={M} C={C} P={P} dtype={dtype} bias={with_bias}")
+    x, w, b = workloads.projection_problem(seed, M, C, P, dtype)
+    d = torch.device("cuda")
+    y = lf.project(x.to(d), w.to(d), b.to(d) if with_bias else None)
+    torch.cuda.synchronize()
+    ref = oracle.project(x.float().numpy(), w.float().numpy(), b.numpy() if with_bias else None)
+    got = y.float().cpu().numpy()
+    excess = np.abs(got - ref) - (REL[dtype] * np.abs(ref) + 1e-3)
+    _say(f"      max abs err {np.abs(got - ref).max():.3e}, worst excess {excess.max():.3e}")
+    assert excess.max() <= 0
+    return y
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("M,C,P", [(300, 128, 3), (1, 64, 1), (257, 192, 6), (1000, 64, 2)])
+def test_projection_small(M, C, P, dtype):
+    check(7 + M, M, C, P, dtype)
+
+
+def test_projection_without_bias():
+    check(11, 130, 128, 2, torch.bfloat16, with_bias=False)
+
+
+def test_projection_longformer_base_full():
+    """The layer's six projections at the longformer-base size: 4096 tokens,
+    768 features (12 heads of 64)."""
+    check(3, 4096, 768, 6, torch.bfloat16)
+
+
+def test_projections_then_attention():
+    """Projections feeding the forward, against the oracles chained the same
+    way (the oracle's projections rounded to bf16 before its attention)."""
+    B, n, H = 1, 600, 4
+    C = 64 * H
+    x, w, b = workloads.projection_problem(21, B * n, C, 6, torch.bfloat16)
+    mask = torch.ones((B, n), dtype=torch.int8)
+    mask[0, [0, 333]] = 2
+    d = torch.device("cuda")
+    y = lf.project(x.to(d), w.to(d), b.to(d))
+    t = [y[i].view(B, n, H, 64) for i in range(6)]
+    # attention order: q, k, v, q_g, k_g, v_g
+    out = lf.forward(*t, mask=mask.to(d), window=50)
+    torch.cuda.synchronize()
+    yr = oracle.project(x.float().numpy(), w.float().numpy(), b.numpy())
+    yr = torch.from_numpy(yr).to(torch.bfloat16).float().numpy()
+    ref, _ = oracle.forward(*[yr[i].reshape(B, n, H, 64) for i in range(6)], mask.numpy(), 50)
+    err = np.abs(out.float().cpu().numpy() - ref).max()
+    _say(f"      chained max abs err {err:.3e}")
+    assert err <= 2e-2

@@ -91,6 +91,17 @@ def upstream_grad(seed: int, shape, dtype: torch.dtype) -> torch.Tensor:
     return _draw(np.random.Generator(np.random.PCG64(seed + 1000)), shape, dtype)
 
 
+def projection_problem(seed: int, M: int, C: int, P: int, dtype: torch.dtype = torch.bfloat16):
+    """Hidden states x [M, C] ~ N(0, 1), stacked weights w [P*C, C] ~
+    N(0, 1/C) (outputs of unit scale) and an fp32 bias ~ N(0, 0.1^2), all in
+    ``dtype`` except the bias."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = _draw(rng, (M, C), dtype)
+    w = torch.from_numpy((rng.standard_normal((P * C, C), dtype=np.float32) / np.float32(np.sqrt(C)))).to(dtype)
+    bias = torch.from_numpy(rng.standard_normal(P * C, dtype=np.float32) * np.float32(0.1))
+    return x, w, bias
+
+
 def random_problem(
     seed: int,
     B: int,
