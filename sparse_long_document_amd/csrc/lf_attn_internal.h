@@ -96,18 +96,6 @@ struct BwdParams {
 int launch_backward(const BwdParams& bp, void* stream);
 int launch_backward_f16(const BwdParams& bp, void* stream);
 
-// Input projections: y[p][m][c] = x[m] . w[p*C + c] + bias[p*C + c].
-struct ProjParams {
-  const void* x;      // [M, C]
-  const void* w;      // [N, C], N = P * C
-  const float* bias;  // [N] or null
-  void* out;          // [P, M, C]
-  int32_t M, C, N, dtype;
-};
-
-// Launches the projection GEMM (bf16 or f16).  Returns the hipError_t value.
-int launch_project(const ProjParams& pp, void* stream);
-
 // Launches the forward kernel.  Returns the hipError_t value as int.
 int launch_forward(const KernelParams& kp, int dtype, void* stream);
 

@@ -18,7 +18,7 @@
 
 #include <stdint.h>
 
-#include "lf_attn_internal.h"
+#include "lf_proj_internal.h"
 
 namespace lf {
 namespace {
