@@ -1,7 +1,9 @@
 /*
- * lf_attn.h — C ABI of the MI355X (gfx950) Longformer attention forward.
+ * lf_attn.h — C ABI of the MI355X (gfx950) Longformer attention layer.
  *
- * One operation: the forward pass of Longformer's combined attention layer,
+ * The forward pass of Longformer's combined attention layer (lf_attn_forward,
+ * lf_attn_forward_lse), its gradients (lf_attn_backward) and the layer's
+ * input projections (lf_attn_project).  The forward is
  * i.e. a sliding window over a fixed number of diagonals of QK^T (optionally
  * dilated per head, optionally causal) merged with symmetric global
  * attention on a few selected tokens that uses its own Q_g/K_g/V_g
