@@ -97,6 +97,21 @@ class Runner:
             raise RuntimeError(f"lf_attn_forward failed with status {st}")
 
 
+def backward_bytes(prob) -> float:
+    """Bytes the backward must move once: q, k, v, out and dout read and the
+    six fp32 gradients written per (token, head); k_g, v_g of batch rows
+    with a global token and q_g of the global rows; the row log-sum-exp
+    (4 B per row); the mask."""
+    B, n, H, D = prob.shape
+    elt = prob.q.element_size()
+    g = (prob.mask == 2).sum(dim=1)
+    total = B * n * H * (5.0 * D * elt + 6.0 * D * 4 + 4) + B * n
+    for b in range(B):
+        if int(g[b]) > 0:
+            total += 2.0 * n * H * D * elt + int(g[b]) * H * D * elt
+    return total
+
+
 def backward_flops(prob) -> float:
     """Useful band FLOPs of one backward: per scored window pair, the score
     recomputed once and the four gradient products dP, dV, dQ, dK, each
@@ -477,6 +492,16 @@ def report_backward(args, prob, run, ms, mode, t_wall):
     achieved = flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS
     dname = {torch.bfloat16: "bf16", torch.float16: "f16"}[prob.q.dtype]
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            ent = json.load(f).get(f"{args.workload}:backward")
+        import sparse_long_document_amd as lf
+
+        if ent and ent.get("kernel_hash") == lf.backward_source_hash():
+            traffic = ent["bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
     result = {
         "metric": "sliding-window attn bwd tokens/s (all six input gradients), bf16; MFMA util %",
         "value": B * n / (ms * 1e-3),
@@ -495,9 +520,9 @@ def report_backward(args, prob, run, ms, mode, t_wall):
                    "globals_per_row": [int(x) for x in (prob.mask == 2).sum(dim=1).tolist()],
                    "timing": mode, "wall_s": round(t_wall, 3)},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None,
+                     "frac": achieved / peak, "traffic": traffic,
                      "kernel": f"lf_attn_bwd<{dname}> (whole backward: 2 launches)",
-                     "flops_per_launch": flops},
+                     "flops_per_launch": flops, "algorithmic_bytes": backward_bytes(prob)},
     }
     if not args.no_check:
         result["parity"] = check_backward(prob, run)

@@ -33,17 +33,26 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblf_attn.
 KERNEL_SOURCES = ("csrc/lf_attn_kernels.hip", "csrc/lf_attn_kernels_f16.hip", "csrc/lf_attn_internal.h")
 
 
-def kernel_source_hash() -> str:
-    """Short digest of the device-code sources; counter measurements are
-    tagged with it so that a later kernel change invalidates them."""
+BACKWARD_SOURCES = ("csrc/lf_attn_bwd.hip", "csrc/lf_attn_bwd_f16.hip", "csrc/lf_attn_internal.h")
+
+
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
+    """Short digest of the device-code sources (by default the forward's);
+    counter measurements are tagged with it so that a later kernel change
+    invalidates them."""
     import hashlib
 
     h = hashlib.sha256()
     base = os.path.dirname(os.path.abspath(__file__))
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(base, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def backward_source_hash() -> str:
+    """Digest of the backward kernels' sources."""
+    return kernel_source_hash(BACKWARD_SOURCES)
 
 LF_OK, LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED, LF_ERR_WORKSPACE, LF_ERR_HIP = range(5)
 LF_F32, LF_BF16, LF_F16 = 0, 1, 2

@@ -99,14 +99,20 @@ def cmd_traffic(args):
     known_kib = float(args.mib << 10)
     cf, _ = counter_per_dispatch(args.copy_fetch, "FETCH_SIZE", args.copy_match)
     cw, _ = counter_per_dispatch(args.copy_write, "WRITE_SIZE", args.copy_match)
-    kf, nf = counter_per_dispatch(args.fetch, "FETCH_SIZE", KERNEL_MATCH)
-    kw, nw = counter_per_dispatch(args.write, "WRITE_SIZE", KERNEL_MATCH)
+    # one launch may be several kernels (comma-separated): their per-dispatch
+    # medians add up
+    kf = kw = 0.0
+    nf = nw = 0
+    for name in args.kernel.split(","):
+        f1, n1 = counter_per_dispatch(args.fetch, "FETCH_SIZE", name)
+        w1, m1 = counter_per_dispatch(args.write, "WRITE_SIZE", name)
+        kf, kw, nf, nw = kf + f1, kw + w1, max(nf, n1), max(nw, m1)
     ff, fw = known_kib / cf, known_kib / cw
     fetch_b, write_b = kf * ff * 1024.0, kw * fw * 1024.0
     if args.kernel_hash is None:
-        from sparse_long_document_amd import kernel_source_hash
+        from sparse_long_document_amd import backward_source_hash, kernel_source_hash
 
-        args.kernel_hash = kernel_source_hash()
+        args.kernel_hash = backward_source_hash() if args.kernel.startswith("lf_attn_bwd") else kernel_source_hash()
     ent = {"kernel_hash": args.kernel_hash,
            "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
            "dispatches_fetch": nf, "dispatches_write": nw,
@@ -125,7 +131,7 @@ def cmd_traffic(args):
     print(json.dumps({args.workload: ent}))
     if args.md:
         cmds = open(args.commands).read().strip() if args.commands else ""
-        lines = [f"# HBM traffic of lf_attn_fwd: {args.workload}", "",
+        lines = [f"# HBM traffic of {args.kernel}: {args.workload}", "",
                  "Commands (from the repository root, after `cd /tmp && export TMPDIR=/tmp`), one counter per run:",
                  "", "```", cmds, "```", "",
                  f"Calibration: an elementwise copy of {args.mib} MiB ({known_kib:.0f} KiB read and written per "
@@ -138,8 +144,7 @@ def cmd_traffic(args):
                  f"| total | | | **{(fetch_b + write_b) / 1e6:.2f} MB** |", ""]
         if args.algorithmic_bytes:
             a = float(args.algorithmic_bytes)
-            lines += [f"Algorithmic bytes per launch (q, k, v read and out written per (token, head); k_g, v_g "
-                      f"of the batch row; q_g of the global rows; the mask): {a / 1e6:.2f} MB.  "
+            lines += [f"Algorithmic bytes per launch ({args.alg_desc}): {a / 1e6:.2f} MB.  "
                       f"Counted / algorithmic = {(fetch_b + write_b) / a:.3f}.", ""]
         if args.avg_us:
             t = float(args.avg_us) * 1e-6
@@ -175,6 +180,9 @@ def main(argv=None):
     t.add_argument("--avg-us", default=None)
     t.add_argument("--algorithmic-bytes", default=None)
     t.add_argument("--commands", default=None)
+    t.add_argument("--kernel", default=KERNEL_MATCH, help="kernel-name substring the counters are taken for")
+    t.add_argument("--alg-desc", default="q, k, v read and out written per (token, head); k_g, v_g of the "
+                   "batch row; q_g of the global rows; the mask")
     args = ap.parse_args(argv)
     {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic}[args.cmd](args)
 

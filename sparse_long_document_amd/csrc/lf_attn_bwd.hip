@@ -52,6 +52,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kLdsRow = 72;           // staged row: 64 head dims + 16 B of padding
 constexpr int kSentinel = -(1 << 29); // residue index of a key outside the row's class
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kXcds = 8;              // MI355X: accelerator complex dies, one L2 each
+constexpr int kXcdGroup = 32;         // consecutive units kept on one XCD
 
 __device__ __forceinline__ f32x16 mma(e16x8 a, e16x8 b, f32x16 c) {
 #if LF_HALF_F16
@@ -343,7 +345,20 @@ __device__ void bwd_body(const BwdParams& p) {
   const int lane = threadIdx.x & 63, c = lane & 31, hl = lane >> 5;
   const int n = p.n;
   const size_t rs = (size_t)p.H * 64;
+  // Workgroups go to the 8 XCDs round-robin (id % 8).  Remap so that groups
+  // of kXcdGroup consecutive units run on one XCD, the groups dealt to the
+  // XCDs in turn: neighbouring tiles share most of their window rows, which
+  // then stay in that XCD's L2 instead of being fetched from HBM by every
+  // XCD, and every XCD still gets an even share of each role.  A bijection
+  // on [0, 8 * kXcdGroup * full); the remainder keeps its index.
   int bid = blockIdx.x;
+  {
+    const int span = kXcds * kXcdGroup;
+    if (bid < (int)(gridDim.x / span) * span) {
+      const int x = bid % kXcds, s = bid / kXcds;
+      bid = ((s / kXcdGroup) * kXcds + x) * kXcdGroup + s % kXcdGroup;
+    }
+  }
   const e16* Q = reinterpret_cast<const e16*>(p.q);
   const e16* K = reinterpret_cast<const e16*>(p.k);
   const e16* V = reinterpret_cast<const e16*>(p.v);
