@@ -3,8 +3,9 @@
  *
  * The forward pass of Longformer's combined attention layer (lf_attn_forward,
  * lf_attn_forward_lse), its gradients (lf_attn_backward) and the layer's
- * input projections (lf_attn_project).  The forward is a sliding window over a fixed number of diagonals of QK^T (optionally
- * dilated per head, optionally causal) merged with symmetric global
+ * input projections (lf_attn_project).  The forward is a sliding window
+ * over a fixed number of diagonals of QK^T (optionally dilated per head,
+ * optionally causal) merged with symmetric global
  * attention on a few selected tokens that uses its own Q_g/K_g/V_g
  * projections.  Sources for the definition:
  *   - sliding window, dilation, global attention, separate global
