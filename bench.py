@@ -8,7 +8,19 @@ Default workload: the longformer-base layer shape, B=1, n=4096, H=12, D=64,
 one-sided window 256, bf16, token 0 global.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu-baseline] [--no-check] [--eager] [--pass backward]
+                  [--no-cpu-baseline] [--no-check] [--no-cold] [--eager]
+                  [--pass forward|backward|projections] [--sweep]
+
+The timed value is warm: graph replays of the launch with its inputs
+resident.  The line also carries a cold figure (each launch after a 512 MB
+write that evicts the caches), the scored pairs of the launch split into
+window, global-column and global-row pairs with their exact FLOPs, and the
+CPU-baseline leg: the fp64 oracle on whole (batch row, head) pairs of the
+workload, timed, whose rows are also compared with the timed output (the
+parity field).  Only that leg touches the oracle.
+
+With --sweep it times the longformer-base layer shape at n = 1024 ... 16384
+(linear growth in n) and prints one line per length.
 
 With --pass projections a step is one lf_attn_project: the six input
 projections (Q_s, K_s, V_s, Q_g, K_g, V_g) of the workload's B*n tokens
@@ -57,6 +69,58 @@ def algorithmic_bytes(prob) -> float:
         if int(g[b]) > 0:
             total += 2.0 * n * H * D * elt + int(g[b]) * H * D * elt
     return total
+
+
+def window_valid_counts(prob, b, h):
+    """Per query row of (b, h): the number of valid keys (mask != 0) in its
+    window W(i) = {i + k d : -w <= k <= w (causal: <= 0), 0 <= i + k d < n},
+    from prefix sums over each residue class.  Host-side accounting of the
+    measured work (it splits the kernel's row_nnz into window and global
+    pairs); no part of the attention."""
+    import numpy as np
+
+    B, n, H, D = prob.shape
+    d = prob.dilation[h] if prob.dilation else 1
+    w = prob.window
+    w_hi = 0 if prob.causal else w
+    valid = (prob.mask[b].numpy() != 0).astype(np.int64)
+    out = np.zeros(n, dtype=np.int64)
+    for r in range(min(d, n)):
+        sub = valid[r::d]
+        pre = np.concatenate([[0], np.cumsum(sub)])
+        t = np.arange(sub.size)
+        lo = np.clip(t - w, 0, sub.size)
+        hi = np.clip(t + w_hi + 1, 0, sub.size)
+        out[r::d] = pre[hi] - pre[lo]
+    return out
+
+
+def pair_accounting(prob, row_nnz):
+    """Scored pairs of the measured launch (the kernel's row_nnz, checked
+    bit-exact against the oracle by the parity tests) split into window
+    pairs of local rows, global columns of local rows and global rows, and
+    the exact FLOPs 4 D P of each (QK^T and P V, 2 D each per pair)."""
+    import numpy as np
+
+    B, n, H, D = prob.shape
+    c = row_nnz.cpu().numpy().astype(np.int64)
+    m = prob.mask.numpy()
+    if prob.causal:
+        m = np.where(m == 2, 1, m)
+    win = glob_cols = glob_rows = 0
+    for b in range(B):
+        loc = m[b] == 1
+        gl = m[b] == 2
+        for h in range(H):
+            wv = window_valid_counts(prob, b, h)
+            win += int(wv[loc].sum())
+            glob_cols += int((c[b, h][loc] - wv[loc]).sum())
+            glob_rows += int(c[b, h][gl].sum())
+    total = win + glob_cols + glob_rows
+    return {"pairs": total, "pairs_window": win, "pairs_global_columns": glob_cols,
+            "pairs_global_rows": glob_rows, "flops_exact": 4.0 * D * total,
+            "flops_window": 4.0 * D * win, "flops_global_columns": 4.0 * D * glob_cols,
+            "flops_global_rows": 4.0 * D * glob_rows}
 
 
 class Runner:
@@ -197,8 +261,6 @@ def report_projections(args, prob, run, ms, mode, t_wall):
     import numpy as np
     import torch
 
-    import oracle
-
     flops = 2.0 * run.M * run.C * run.P * run.C
     achieved = flops / (ms * 1e-3) / 1e12
     dname = {torch.bfloat16: "bf16", torch.float16: "f16"}[prob.q.dtype]
@@ -215,33 +277,37 @@ def report_projections(args, prob, run, ms, mode, t_wall):
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
                      "kernel": f"lf_proj_{dname}", "flops_per_launch": flops},
     }
-    if not args.no_check:
-        rows = np.linspace(0, run.M - 1, 64).astype(np.int64)
-        ref = oracle.project(run.x_cpu.float().numpy()[rows], run.w_cpu.float().numpy(), run.b_cpu.numpy())
-        got = run.out[:, torch.from_numpy(rows).to(run.out.device)].float().cpu().numpy()
-        excess = float((np.abs(got - ref) - (2.0 ** -8 * np.abs(ref) + 1e-3)).max())
-        result["parity"] = {"kind": "64 sampled rows of all six projections vs the fp64 oracle",
-                            "max_abs_err": float(np.abs(got - ref).max()), "ok": excess <= 0}
     if not args.no_cpu_baseline:
+        # the CPU-baseline leg: the fp64 oracle on the whole job, timed; its
+        # result is also compared with the timed output
         from threadpoolctl import threadpool_info
+
+        import oracle
 
         xs, ws, bs = run.x_cpu.float().numpy(), run.w_cpu.float().numpy(), run.b_cpu.numpy()
         reps, t0 = 0, time.perf_counter()
         while reps < 3 or time.perf_counter() - t0 < 2.0:
-            oracle.project(xs, ws, bs)
+            ref = oracle.project(xs, ws, bs)
             reps += 1
         dt = (time.perf_counter() - t0) / reps
         threads = max([int(t.get("num_threads", 1)) for t in threadpool_info()] or [1])
         result["cpu_baseline"] = {"value": run.M / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                                   "sample": f"the whole job ({run.M} tokens, six projections), fp64 NumPy "
                                             f"matmul on {threads} BLAS threads, mean of {reps} runs"}
+        if not args.no_check:
+            got = run.out.float().cpu().numpy()
+            excess = float((np.abs(got - ref) - (2.0 ** -8 * np.abs(ref) + 1e-3)).max())
+            result["parity"] = {"kind": "every row of all six projections vs the fp64 oracle run of the "
+                                        "CPU-baseline leg", "max_abs_err": float(np.abs(got - ref).max()),
+                                "ok": excess <= 0}
     print(json.dumps(result), flush=True)
 
 
 def check_backward(prob, run):
-    """Closed forms that hold at any size, on every head: summed over
-    tokens, dv equals the upstream gradient summed over local rows (dv_g:
-    over global rows), and dk sums to zero (relative to its column mass)."""
+    """Closed forms that hold at any size, on every head (no oracle): summed
+    over tokens, dv equals the upstream gradient summed over local rows
+    (dv_g: over global rows), and dk and dk_g sum to zero (relative to their
+    column mass)."""
     import numpy as np
 
     dq, dk, dv, dqg, dkg, dvg = [g.double().cpu().numpy() for g in run.grads]
@@ -253,145 +319,128 @@ def check_backward(prob, run):
         for h in range(H):
             ref = do[b, m[b] == 1, h].sum(0)
             worst = max(worst, np.abs(dv[b, :, h].sum(0) - ref).max() / max(np.abs(ref).max(), 1e-3))
-            refg = do[b, m[b] == 2, h].sum(0)
-            if (m[b] == 2).any():
-                worst = max(worst, np.abs(dvg[b, :, h].sum(0) - refg).max() / max(np.abs(refg).max(), 1e-3))
             mass = np.abs(dk[b, :, h]).sum(0).max()
             worst = max(worst, np.abs(dk[b, :, h].sum(0)).max() / max(mass, 1e-30))
-    return {"kind": "closed-form column sums, every (b, h)", "max_rel_err": float(worst),
+            if (m[b] == 2).any():
+                refg = do[b, m[b] == 2, h].sum(0)
+                worst = max(worst, np.abs(dvg[b, :, h].sum(0) - refg).max() / max(np.abs(refg).max(), 1e-3))
+                massg = np.abs(dkg[b, :, h]).sum(0).max()
+                worst = max(worst, np.abs(dkg[b, :, h].sum(0)).max() / max(massg, 1e-30))
+    return {"kind": "closed-form column sums of dv, dv_g, dk, dk_g, every (b, h)", "max_rel_err": float(worst),
             "tol": 2e-2, "ok": bool(worst <= 2e-2)}
 
 
-def cpu_baseline_backward(prob):
-    """The fp64 gradient oracle on one host thread, on one (b, h) of the
-    workload at full length, scaled to tokens/s of the whole job."""
+def cpu_baseline_backward(prob, run=None):
+    """The CPU-baseline leg of the backward: the fp64 gradient oracle on
+    batch row 0 and heads 0 and H-1 at full length (NumPy BLAS on every core
+    it finds), scaled to tokens/s of the whole job.  Its six gradients of
+    those heads are compared, every element, with the timed run's (tolerance
+    2e-2 of each gradient's largest entry, the test suite's bound)."""
     import numpy as np
-    import torch
 
-    import oracle
-    import workloads
-
-    torch.set_num_threads(1)
-    t = [x.float().numpy() for x in (prob.q, prob.k, prob.v, prob.q_g, prob.k_g, prob.v_g)]
-    dout = workloads.upstream_grad(2, prob.shape, prob.q.dtype).float().numpy()
-    B, n, H, D = prob.shape
-    t0 = time.perf_counter()
-    hs = list(range(min(H, 2)))
-    oracle.backward(*[x[:1] for x in t], prob.mask.numpy()[:1], dout[:1], prob.window,
-                    dilation=prob.dilation, causal=prob.causal, scale=prob.scale, heads=hs)
-    dt = time.perf_counter() - t0
-    return {"value": B * n * len(hs) / (dt * H * B), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"batch row 0, heads 0..{len(hs) - 1} of {H}, all {n} tokens ({dt:.1f} s), "
-                      "scaled to B*H"}
-
-
-def check_parity(prob, out, row_nnz, max_rows=48):
-    """Sampled rows of the timed output against the fp64 oracle."""
-    import numpy as np
-    import torch
-
-    import oracle
-
-    B, n, H, D = prob.shape
-    arrs = [x.float().numpy() for x in (prob.q, prob.k, prob.v, prob.q_g, prob.k_g, prob.v_g)]
-    mask = prob.mask.numpy()
-    o = out.float().cpu().numpy()
-    c = row_nnz.cpu().numpy()
-    rng = np.random.default_rng(1)
-    worst, nnz_ok = 0.0, True
-    for b in range(B):
-        for h in sorted({0, H // 2, H - 1}):
-            rows = sorted(set([0, 1, n - 1, n // 2] + [int(x) for x in rng.integers(0, n, size=max_rows)]
-                              + [int(x) for x in np.flatnonzero(mask[b] == 2)[:8]]))
-            ref, rc = oracle.forward_rows(*arrs, mask, prob.window, b, h, rows, dilation=prob.dilation,
-                                          causal=prob.causal, scale=prob.scale)
-            worst = max(worst, float(np.abs(o[b, rows, h] - ref).max()))
-            nnz_ok &= bool(np.array_equal(c[b, h, rows], rc))
-    tol = {torch.bfloat16: 2e-2, torch.float16: 5e-3}.get(prob.q.dtype, 1e-4)
-    return {"max_abs_err_sampled": worst, "tolerance": tol, "row_nnz_exact": nnz_ok,
-            "ok": bool(worst <= tol and nnz_ok)}
-
-
-def cpu_baseline(prob, min_s=10.0, max_s=30.0):
-    """The fp64 oracle as it stands, on a bounded sample of the same workload:
-    whole (batch row, head) pairs, all rows each, taken in order and
-    cyclically until at least min_s seconds of work (stopping early at
-    max_s); single BLAS thread; scaled to tokens/s of the full job."""
     import oracle
 
     try:
-        from threadpoolctl import threadpool_limits
+        from threadpoolctl import threadpool_info
+        threads = max([int(t.get("num_threads", 1)) for t in threadpool_info()] or [1])
     except ImportError:  # pragma: no cover
-        threadpool_limits = None
+        threads = os.cpu_count() or 1
+    t = [x.float().numpy() for x in (prob.q, prob.k, prob.v, prob.q_g, prob.k_g, prob.v_g)]
+    dout = run.dout.float().cpu().numpy()
+    B, n, H, D = prob.shape
+    hs = sorted({0, H - 1})
+    t0 = time.perf_counter()
+    ref = oracle.backward(*[x[:1] for x in t], prob.mask.numpy()[:1], dout[:1], prob.window,
+                          dilation=prob.dilation, causal=prob.causal, scale=prob.scale, heads=hs)
+    dt = time.perf_counter() - t0
+    out = {"value": B * n * len(hs) / (dt * H * B), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"batch row 0, heads {hs} of {H}, all {n} tokens ({dt:.1f} s, NumPy BLAS on "
+                     f"{threads} threads), scaled to B*H"}
+    parity = None
+    if run is not None:
+        worst = 0.0
+        for g, r in zip(run.grads, ref):
+            gg = g[:1, :, hs].double().cpu().numpy()
+            rr = r[:, :, hs]
+            worst = max(worst, float(np.abs(gg - rr).max()) / max(float(np.abs(rr).max()), 1e-3))
+        parity = {"kind": f"all six gradients of batch row 0, heads {hs}, every element, vs the oracle run "
+                          "of the CPU-baseline leg", "max_rel_err": worst, "tol": 2e-2, "ok": worst <= 2e-2}
+    return out, parity
+
+
+def cpu_baseline(prob, out=None, row_nnz=None, min_s=10.0, max_s=30.0):
+    """The CPU-baseline leg: the fp64 oracle as it stands, on a bounded
+    sample of the same workload: whole (batch row, head) pairs, all rows
+    each, taken in order and cyclically until at least min_s seconds of
+    work and three pairs (stopping early at max_s); NumPy's BLAS on every
+    host core it finds (its own default).  The time per pair is the median
+    over the pairs run, scaled to tokens/s of the full job.  When the timed
+    run's out and row_nnz are given, every row of the sampled pairs is
+    compared with the oracle's (max |out - oracle| within the parity
+    tolerance, row_nnz bit-exact).  Returns (baseline, parity)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(t.get("num_threads", 1)) for t in threadpool_info()] or [1])
+    except ImportError:  # pragma: no cover
+        threads = os.cpu_count() or 1
     B, n, H, D = prob.shape
     arrs = [x.float().numpy() for x in (prob.q, prob.k, prob.v, prob.q_g, prob.k_g, prob.v_g)]
     mask = prob.mask.numpy()
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    o = out.float().cpu().numpy() if out is not None else None
+    c = row_nnz.cpu().numpy() if row_nnz is not None else None
     pairs = [(b, h) for b in range(B) for h in range(H)]
-    done, t0 = 0, time.perf_counter()
-    try:
-        if ctx:
-            ctx.__enter__()
-        while True:
-            b, h = pairs[done % len(pairs)]
-            oracle.forward_rows(*arrs, mask, prob.window, b, h, range(n), dilation=prob.dilation,
-                                causal=prob.causal, scale=prob.scale)
-            done += 1
-            el = time.perf_counter() - t0
-            if el >= min_s or el + el / done > max_s:
-                break
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
+    # head 0 first, then spread over the job
+    order = [pairs[(k * 7) % len(pairs)] for k in range(len(pairs))] if len(pairs) % 7 else pairs
+    per, t0 = [], time.perf_counter()
+    worst, nnz_ok, seen = 0.0, True, []
+    while True:
+        b, h = order[len(per) % len(order)]
+        t1 = time.perf_counter()
+        ref, rc = oracle.forward_rows(*arrs, mask, prob.window, b, h, range(n), dilation=prob.dilation,
+                                      causal=prob.causal, scale=prob.scale)
+        per.append(time.perf_counter() - t1)
+        if o is not None and (b, h) not in seen:
+            worst = max(worst, float(np.abs(o[b, :, h] - ref).max()))
+            nnz_ok &= bool(np.array_equal(c[b, h], rc))
+            seen.append((b, h))
+        el = time.perf_counter() - t0
+        if (el >= min_s and len(per) >= 3) or el + el / len(per) > max_s:
+            break
     el = time.perf_counter() - t0
-    full = el / done * len(pairs)  # seconds for the whole job at the sampled rate
-    return {"value": B * n / full, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} (batch row, head) pairs of the {len(pairs)} in the job (cycled in order), "
-                      f"all {n} query rows each, {el:.1f} s on one thread; value = tokens of the full "
-                      f"job / ({len(pairs)} x seconds per pair)"}
+    med = float(np.median(per))
+    full = med * len(pairs)  # seconds for the whole job at the sampled rate
+    base = {"value": B * n / full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(per)} (batch row, head) pairs of the {len(pairs)} in the job, all {n} query rows "
+                      f"each, {el:.1f} s with NumPy BLAS on {threads} threads (os.cpu_count() = "
+                      f"{os.cpu_count()}); value = tokens of the full job / ({len(pairs)} x median seconds "
+                      "per pair)"}
+    parity = None
+    if o is not None:
+        tol = {torch.bfloat16: 2e-2, torch.float16: 5e-3}.get(prob.q.dtype, 1e-4)
+        parity = {"kind": f"every row of (batch row, head) pairs {seen} vs the oracle run of the CPU-baseline leg",
+                  "max_abs_err": worst, "tolerance": tol, "row_nnz_exact": nnz_ok,
+                  "ok": bool(worst <= tol and nnz_ok)}
+    return base, parity
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="longformer_base_n4096")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-check", action="store_true")
-    ap.add_argument("--eager", action="store_true", help="time direct launches instead of a graph replay")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "projections"], default="forward")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU layout of this "
-              "path is a design note, not a measured configuration", file=sys.stderr)
-        sys.exit(2)
-
+def time_graph(run, K, eager=False, bwd=False):
+    """Time exactly K launches (graph replays of up to 50 launches, or eager
+    launches), inputs resident in HBM.  Returns (ms per launch, mode, wall s)."""
     import torch
 
-    import sparse_long_document_amd as lf
-    import workloads
-
-    prob = workloads.by_name(args.workload)
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    bwd = args.which != "forward"  # a runner with out_t, compared across graph replays
-    run = {"forward": Runner, "backward": BwdRunner, "projections": ProjRunner}[args.which](prob, dev)
-    for _ in range(max(1, args.warmup)):
-        run.launch()
-    torch.cuda.synchronize()
-
-    K = args.steps
-    mode = "eager"
-    graph = None
-    if not args.eager:
+    mode, graph, per = "eager", None, 1
+    if not eager:
         try:
             ref = (run.out_t if bwd else run.out).clone()
             per = max(d for d in range(1, min(K, 50) + 1) if K % d == 0)
             s = torch.cuda.Stream()
             s.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(s):
-                run.stream = s.cuda_stream
                 run.args = run.args[:-1] + (ctypes.c_void_p(s.cuda_stream),)
                 graph = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(graph, stream=s):
@@ -408,26 +457,119 @@ def main():
         except Exception as e:  # fall back to eager timing
             print(f"graph capture unavailable ({e}); timing eager launches", file=sys.stderr)
             graph = None
-            run.args = run.args[:-1] + (ctypes.c_void_p(torch.cuda.current_stream().cuda_stream),)
-
+        # later eager launches go to torch's current stream again
+        run.args = run.args[:-1] + (ctypes.c_void_p(torch.cuda.current_stream().cuda_stream),)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
+    start.record()
     if graph is not None:
-        reps = K // per
-        start.record()
-        for _ in range(reps):
+        for _ in range(K // per):
             graph.replay()
-        end.record()
     else:
-        start.record()
         for _ in range(K):
             run.launch()
-        end.record()
+    end.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms = start.elapsed_time(end) / K
+    return start.elapsed_time(end) / K, mode, t_wall
+
+
+def time_cold(run, launches=30, scratch_mb=512):
+    """Each launch timed alone (its own event pair on the launch stream)
+    right after a 512 MB write that evicts the L2 caches and the 256 MB
+    Infinity Cache: inputs come from HBM.  Median ms per launch."""
+    import numpy as np
+    import torch
+
+    scratch = torch.empty(scratch_mb << 20, dtype=torch.uint8, device=run.out.device if hasattr(run, "out")
+                          else run.out_t.device)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    ts = []
+    for i in range(launches):
+        scratch.fill_(i & 0xFF)
+        e0.record()
+        run.launch()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del scratch
+    return float(np.median(ts))
+
+
+def sweep(args):
+    """Linear growth in n (ultralytics glossary, "How Longformer attention
+    works": the cost grows linearly with the sequence): the longformer-base
+    layer shape (H12, w=256, token 0 global) at n = 1024 ... 16384, one JSON
+    line per length, then the ratios t(n) / t(n/2)."""
+    import torch
+
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    rows = []
+    for n in workloads.SWEEP_N:
+        prob = workloads.longformer_base_len(n)
+        run = Runner(prob, dev)
+        for _ in range(max(1, args.warmup)):
+            run.launch()
+        torch.cuda.synchronize()
+        ms, mode, _ = time_graph(run, args.steps)
+        flops = band_flops(prob)
+        acct = pair_accounting(prob, run.row_nnz)
+        row = {"workload": prob.name, "n": n, "ms_per_launch": ms, "tokens_per_s": n / (ms * 1e-3),
+               "mfma_frac_band": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "timing": mode,
+               "pairs": acct["pairs"]}
+        if rows:
+            row["ratio_to_half_n"] = ms / rows[-1]["ms_per_launch"]
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+        del run
+    print(json.dumps({"sweep": "longformer_base_len", "n": [r["n"] for r in rows],
+                      "ms": [r["ms_per_launch"] for r in rows],
+                      "ratios": [r.get("ratio_to_half_n") for r in rows[1:]]}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="longformer_base_n4096")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time direct launches instead of a graph replay")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "projections"], default="forward")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the longformer-base layer at n = 1024 ... 16384 instead (one line each)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU layout of this "
+              "path is a design note, not a measured configuration", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_long_document_amd as lf
+    import workloads
+
+    if args.sweep:
+        return sweep(args)
+    prob = workloads.by_name(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    bwd = args.which != "forward"  # a runner with out_t, compared across graph replays
+    run = {"forward": Runner, "backward": BwdRunner, "projections": ProjRunner}[args.which](prob, dev)
+    for _ in range(max(1, args.warmup)):
+        run.launch()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ms, mode, t_wall = time_graph(run, K, eager=args.eager, bwd=bwd)
 
     B, n, H, D = prob.shape
     if args.which == "backward":
@@ -477,10 +619,21 @@ def main():
                 "peak_GBs": PEAK_HBM_GBS,
                 "counted_frac": None if traffic is None else traffic / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
     }
-    if not args.no_check:
-        result["parity"] = check_parity(prob, run.out, run.row_nnz)
+    result["pairs"] = pair_accounting(prob, run.row_nnz)
+    result["flops_exact_frac"] = result["pairs"]["flops_exact"] / (ms * 1e-3) / 1e12 / peak
+    if not args.no_cold:
+        cold = time_cold(run)
+        result["cold"] = {"ms_per_launch": cold, "tokens_per_s": B * n / (cold * 1e-3),
+                          "mfma_frac_band": flops / (cold * 1e-3) / 1e12 / peak,
+                          "algorithmic_GBs": algorithmic_bytes(prob) / (cold * 1e-3) / 1e9,
+                          "method": "median of 30 launches, each after a 512 MB write "
+                                    "(evicts L2 and Infinity Cache), one event pair per launch"}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(prob)
+        base, parity = cpu_baseline(prob, None if args.no_check else run.out,
+                                    None if args.no_check else run.row_nnz)
+        result["cpu_baseline"] = base
+        if parity is not None:
+            result["parity"] = parity
     print(json.dumps(result), flush=True)
 
 
@@ -525,9 +678,12 @@ def report_backward(args, prob, run, ms, mode, t_wall):
                      "flops_per_launch": flops, "algorithmic_bytes": backward_bytes(prob)},
     }
     if not args.no_check:
-        result["parity"] = check_backward(prob, run)
+        result["closed_forms"] = check_backward(prob, run)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_backward(prob)
+        base, parity = cpu_baseline_backward(prob, None if args.no_check else run)
+        result["cpu_baseline"] = base
+        if parity is not None:
+            result["parity"] = parity
     print(json.dumps(result), flush=True)
 
 

@@ -154,6 +154,12 @@ size_t lf_attn_backward_workspace_bytes(const lf_attn_params* p);
  *   - workspace holds lf_attn_backward_workspace_bytes(p) bytes; its first
  *     256 bytes are the device status word (lf_attn_workspace_init clears
  *     it, lf_attn_device_status reads it); the rest needs no initialisation.
+ *   - A batch row with more than max_global mask-2 tokens sets
+ *     LF_DEV_TOO_MANY_GLOBALS in this status word, and that row's gradients
+ *     are then incomplete: the tokens past the first max_global get no dk
+ *     and dv from the local rows and no global-row work (the forward drops
+ *     them likewise and flags its own status word).  Size max_global to the
+ *     mask (the Python binding derives it when validating).
  *   - Asynchronous like lf_attn_forward; the same argument errors. */
 lf_status lf_attn_backward(const lf_attn_params* p,
                            const void* q, const void* k, const void* v,

@@ -25,8 +25,8 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "forward", "backward", "project", "workspace_bytes", "device_status", "pad_to_window_size",
-    "merge_masks", "library", "LfError", "LF_MAX_GLOBAL", "LF_MAX_HEADS",
+    "forward", "backward", "project", "workspace_bytes", "make_workspace", "device_status",
+    "pad_to_window_size", "merge_masks", "library", "LfError", "LF_MAX_GLOBAL", "LF_MAX_HEADS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblf_attn.so")
@@ -155,18 +155,35 @@ def workspace_bytes(B: int, n: int, H: int, window: int, dilation=None, causal=F
 
 
 _ws_cache = {}
+_bwd_ws = {}
 _ws_lock = threading.Lock()
+
+
+def _capturing() -> bool:
+    try:
+        return bool(torch.cuda.is_current_stream_capturing())
+    except Exception:  # pragma: no cover - older torch
+        return False
+
+
+_CAPTURE_MSG = ("{what} would allocate and clear a workspace inside a HIP graph capture (the clear "
+                "would be recorded into the graph and the buffer would come from the graph's memory "
+                "pool): create one beforehand with make_workspace(...) and pass it as workspace=")
 
 
 def _workspace(nbytes: int, device: torch.device, stream: int, layout) -> torch.Tensor:
     """A zero-initialised workspace of at least nbytes, cached per
     (device, stream): calls on one stream are ordered, so they may share it.
     Each call leaves its arrival counters at zero, but where they sit depends
-    on (B, H), so a change of layout re-initialises the buffer."""
+    on (B, H), so a change of layout re-initialises the buffer.  Under graph
+    capture nothing is allocated or cleared: the cached buffer must already
+    fit, else this raises."""
     key = (device.index, stream)
     with _ws_lock:
         ws, last = _ws_cache.get(key, (None, None))
         if ws is None or ws.numel() < nbytes or last != layout:
+            if _capturing():
+                raise RuntimeError(_CAPTURE_MSG.format(what="forward"))
             if ws is None or ws.numel() < nbytes:
                 ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
             st = library().lf_attn_workspace_init(ctypes.c_void_p(ws.data_ptr()),
@@ -176,6 +193,40 @@ def _workspace(nbytes: int, device: torch.device, stream: int, layout) -> torch.
                 raise LfError(st, "lf_attn_workspace_init")
             _ws_cache[key] = (ws, layout)
         return ws
+
+
+def make_workspace(B: int, n: int, H: int, window: int, dilation=None, causal=False, scale=None,
+                   max_global: int = 0, dtype=torch.bfloat16, device=None, backward: bool = False,
+                   D: int = LF_HEAD_DIM) -> torch.Tensor:
+    """Allocate a workspace for ``forward`` (or, with backward=True, for
+    ``backward``) on the current stream and zero it (``lf_attn_workspace_init``),
+    outside any graph capture.  Pass it as ``workspace=`` to calls with the
+    same B and H, for instance inside ``torch.cuda.graph``: each forward call
+    leaves its arrival counters back at zero, so replays may reuse it."""
+    if _capturing():
+        raise RuntimeError("make_workspace must be called outside a graph capture")
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    p, _keep = make_params(B, n, H, D, window, dilation, causal, scale, max_global, dtype)
+    lib = library()
+    need = int((lib.lf_attn_backward_workspace_bytes if backward else lib.lf_attn_workspace_bytes)(
+        ctypes.byref(p)))
+    if need == 0:
+        raise LfError(LF_ERR_INVALID_ARG, "workspace size")
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream(device).cuda_stream
+    st = lib.lf_attn_workspace_init(ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+                                    ctypes.c_void_p(stream))
+    if st != LF_OK:
+        raise LfError(st, "lf_attn_workspace_init")
+    return ws
+
+
+def _given_workspace(ws: torch.Tensor, need: int, device: torch.device) -> torch.Tensor:
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or ws.device != device:
+        raise ValueError("workspace must be a uint8 tensor on the inputs' device (see make_workspace)")
+    if not ws.is_contiguous() or ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {need} needed")
+    return ws
 
 
 def _check_tensor(name, t, shape, dtype, device):
@@ -201,7 +252,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             max_global: Optional[int] = None, return_row_nnz: bool = False,
             validate: bool = True, out: Optional[torch.Tensor] = None,
             row_nnz: Optional[torch.Tensor] = None, return_lse: bool = False,
-            lse: Optional[torch.Tensor] = None):
+            lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Longformer attention forward (``lf_attn_forward``).
 
     q, k, v, q_g, k_g, v_g: [B, n, H, 64] bf16, f16 or fp32 GPU tensors, contiguous
@@ -215,6 +266,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     validate=True checks mask contents on the host (one device sync) and
     derives max_global from the mask; validate=False trusts the caller
     (max_global then defaults to the library limit unless given).
+    workspace: a buffer from ``make_workspace`` (needed under graph capture);
+    by default one is cached per (device, stream).
     """
     if q.dim() != 4:
         raise ValueError("q must be [B, n, H, D]")
@@ -248,7 +301,10 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if need == 0:
         raise LfError(LF_ERR_INVALID_ARG, "lf_attn_workspace_bytes")
     stream = torch.cuda.current_stream(device).cuda_stream
-    ws = _workspace(need, device, stream, (B, H))
+    if workspace is not None:
+        ws = _given_workspace(workspace, need, device)
+    else:
+        ws = _workspace(need, device, stream, (B, H))
     vp = ctypes.c_void_p
     args = [ctypes.byref(p), vp(q.data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()),
             vp(q_g.data_ptr()), vp(k_g.data_ptr()), vp(v_g.data_ptr()), vp(mask.data_ptr()),
@@ -327,21 +383,20 @@ def _prep_mask(mask, B, n, device, causal, max_global, validate):
     return mask, max_global
 
 
-_bwd_ws = {}
-
-
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
              q_g: Optional[torch.Tensor], k_g: Optional[torch.Tensor], v_g: Optional[torch.Tensor],
              mask: Optional[torch.Tensor], out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
              window: int = 256, dilation: Optional[Sequence[int]] = None, causal: bool = False,
              scale: Optional[float] = None, max_global: Optional[int] = None,
-             validate: bool = True, grads: Optional[Sequence[torch.Tensor]] = None):
+             validate: bool = True, grads: Optional[Sequence[torch.Tensor]] = None,
+             workspace: Optional[torch.Tensor] = None):
     """Gradients of the forward (``lf_attn_backward``): returns fp32
     (dq, dk, dv, dq_g, dk_g, dv_g), each [B, n, H, 64].  q..v_g, out and dout
     are bf16 or f16; out and lse are what ``forward(..., return_lse=True)``
     returned for the same inputs.  When q_g/k_g/v_g are None (aliasing
     q/k/v) the gradient of a shared tensor is the sum of its two results.
-    ``grads`` may supply the six output tensors."""
+    ``grads`` may supply the six output tensors; ``workspace`` a buffer from
+    ``make_workspace(..., backward=True)`` (needed under graph capture)."""
     if q.dim() != 4:
         raise ValueError("q must be [B, n, H, D]")
     B, n, H, D = q.shape
@@ -369,8 +424,10 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     stream = torch.cuda.current_stream(device).cuda_stream
     key = (device.index, stream)
     with _ws_lock:
-        ws = _bwd_ws.get(key)
+        ws = _bwd_ws.get(key) if workspace is None else _given_workspace(workspace, need, device)
         if ws is None or ws.numel() < need:
+            if _capturing():
+                raise RuntimeError(_CAPTURE_MSG.format(what="backward"))
             ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
             st = lib.lf_attn_workspace_init(ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
                                             ctypes.c_void_p(stream))
@@ -386,20 +443,37 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return tuple(grads)
 
 
-def device_status(device: Optional[torch.device] = None) -> int:
-    """Synchronise and read the device status word of the workspace used on
-    the current stream (``lf_attn_device_status``); 0 = nothing flagged."""
+def device_status(device: Optional[torch.device] = None, kind: str = "any",
+                  workspace: Optional[torch.Tensor] = None) -> int:
+    """Synchronise and read a device status word (``lf_attn_device_status``);
+    0 = nothing flagged.  kind="forward" or "backward" reads the workspace
+    that ``forward`` or ``backward`` used on the current stream, "any" the OR
+    of both; ``workspace`` reads that buffer instead.  The words are sticky:
+    a flag stays set until the workspace is re-initialised."""
     device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
     stream = torch.cuda.current_stream(device).cuda_stream
-    ws, _layout = _ws_cache.get((device.index, stream), (None, None))
-    if ws is None:
-        return 0
-    val = ctypes.c_int32(0)
-    st = library().lf_attn_device_status(ctypes.c_void_p(ws.data_ptr()), ctypes.c_void_p(stream),
-                                         ctypes.byref(val))
-    if st != LF_OK:
-        raise LfError(st, "lf_attn_device_status")
-    return int(val.value)
+    if kind not in ("any", "forward", "backward"):
+        raise ValueError("kind must be 'any', 'forward' or 'backward'")
+    bufs = []
+    if workspace is not None:
+        bufs.append(workspace)
+    else:
+        key = (device.index, stream)
+        if kind in ("any", "forward"):
+            bufs.append(_ws_cache.get(key, (None, None))[0])
+        if kind in ("any", "backward"):
+            bufs.append(_bwd_ws.get(key))
+    word = 0
+    for ws in bufs:
+        if ws is None:
+            continue
+        val = ctypes.c_int32(0)
+        st = library().lf_attn_device_status(ctypes.c_void_p(ws.data_ptr()), ctypes.c_void_p(stream),
+                                             ctypes.byref(val))
+        if st != LF_OK:
+            raise LfError(st, "lf_attn_device_status")
+        word |= int(val.value)
+    return word
 
 
 def pad_to_window_size(x: torch.Tensor, mask: torch.Tensor, attention_window: int, pad_value=0):

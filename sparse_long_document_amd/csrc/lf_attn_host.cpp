@@ -134,7 +134,13 @@ lf_status forward_impl(const lf_attn_params* p, const void* q, const void* k, co
     if (row_nnz && overlaps(lse, lb, row_nnz, nb)) return LF_ERR_INVALID_ARG;
   }
   if (!workspace || workspace_bytes < pl.ws_bytes) return LF_ERR_WORKSPACE;
-  if (overlaps(workspace, pl.ws_bytes, out, tb)) return LF_ERR_INVALID_ARG;
+  // the kernel writes tickets and partial records into the workspace: it
+  // may overlap no input and no output
+  for (const void* in : ins)
+    if (overlaps(workspace, pl.ws_bytes, in, tb)) return LF_ERR_INVALID_ARG;
+  if (overlaps(workspace, pl.ws_bytes, mask, mb) || overlaps(workspace, pl.ws_bytes, out, tb))
+    return LF_ERR_INVALID_ARG;
+  if (row_nnz && overlaps(workspace, pl.ws_bytes, row_nnz, nb)) return LF_ERR_INVALID_ARG;
   if (lse && overlaps(workspace, pl.ws_bytes, lse, (size_t)p->B * p->H * p->n * sizeof(float)))
     return LF_ERR_INVALID_ARG;
 

@@ -812,7 +812,10 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 __device__ __forceinline__ int xcd_remap(int x, int N) {
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous range of tiles so neighbouring tiles (which share K/V
-  // halos) share one L2.
+  // halos) share one L2.  x is the band index blockIdx.x - n_glob: every x
+  // of one class x % 8 has blockIdx.x % 8 = (x + n_glob) % 8, so each class
+  // runs on one XCD whatever n_glob is (the class is a relabelling of the
+  // XCD index), and the classes are dealt contiguous ranges of tiles.
   const int per = N / 8, rem = N % 8;
   const int xcd = x % 8, y = x / 8;
   return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + y;
@@ -1700,7 +1703,15 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
 
   // Arrival: the last split of (b, h) merges all partials.  Every thread's
   // record stores have completed (at the coherence point) before the
-  // barrier that precedes the ticket increment.
+  // barrier that precedes the ticket increment.  The hardware guarantee
+  // this rests on: an agent-scope store is written through the XCD's L2 to
+  // the device coherence point, and the vector-memory counter counts a
+  // store down only when the memory system acknowledges it there; so after
+  // each thread's vmcnt(0) and the barrier, every record of this split is
+  // visible to agent-scope loads from any XCD before the relaxed ticket
+  // increment is issued.  The last arriver's agent-scope loads read the
+  // coherence point, not a stale L2 line.  (A release/acquire fence pair
+  // would give the same order, at the cost of writing back the whole L2.)
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   wait_vmem_all();
   __syncthreads();

@@ -138,6 +138,21 @@ def test_workspace_errors():
     assert lib.lf_attn_device_status(None, None, None) == lf.LF_ERR_INVALID_ARG
 
 
+def test_workspace_overlapping_any_buffer_rejected():
+    # the kernel writes tickets and partial records into the workspace, so it
+    # may overlap none of the six inputs, the mask, out, row_nnz or lse
+    p, _k = _params(B=2, max_global=64)
+    tb = 2 * 4096 * 12 * 64 * 2
+    for name, addr in (("q", FAKE), ("k", FAKE + (1 << 32)), ("v", FAKE + (2 << 32)),
+                       ("mask", FAKE + (3 << 32)), ("out", FAKE + (4 << 32))):
+        assert _forward(p, {"ws": addr + 64}) == lf.LF_ERR_INVALID_ARG, name
+    for name in ("qg", "kg", "vg"):
+        other = FAKE + (7 << 32)
+        assert _forward(p, {name: other, "ws": other + tb - 256}) == lf.LF_ERR_INVALID_ARG, name
+    nnz = FAKE + (8 << 32)
+    assert _forward(p, {"ws": nnz + 16}, row_nnz=nnz) == lf.LF_ERR_INVALID_ARG
+
+
 def test_forward_refuses_cpu_tensors():
     x = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):

@@ -51,7 +51,8 @@ def run_gpu(prob, dout):
     grads = lf.backward(*t, mask, out, dout.to(d), lse, window=prob.window, dilation=prob.dilation,
                         causal=prob.causal, scale=prob.scale)
     torch.cuda.synchronize()
-    assert lf.device_status() == 0
+    assert lf.device_status(kind="forward") == 0
+    assert lf.device_status(kind="backward") == 0
     return lse.cpu().numpy().astype(np.float64), [g.cpu().numpy().astype(np.float64) for g in grads]
 
 
@@ -129,3 +130,24 @@ def test_backward_rejects_fp32():
     out, lse = lf.forward(*t, window=8, return_lse=True)
     with pytest.raises(lf.LfError):
         lf.backward(*t, None, None, None, None, out, out, lse, window=8)
+
+
+def test_backward_too_many_globals_flagged():
+    """More mask-2 tokens in a row than max_global: the backward flags its own
+    status word (the forward, given the right bound, flags nothing)."""
+    prob = workloads.random_problem(13, B=1, n=300, H=1, window=10, n_global=5, name="bwd_toomany")
+    d = torch.device("cuda")
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()  # fresh stream: fresh workspaces with clear status words
+    with torch.cuda.stream(s):
+        t = [x.to(d) for x in (prob.q, prob.k, prob.v, prob.q_g, prob.k_g, prob.v_g)]
+        mask = prob.mask.to(d)
+        out, lse = lf.forward(*t, mask=mask, window=10, return_lse=True, max_global=5)
+        dout = workloads.upstream_grad(13, prob.shape, prob.q.dtype).to(d)
+        lf.backward(*t, mask, out, dout, lse, window=10, validate=False, max_global=2)
+        assert lf.device_status(kind="forward") == 0
+        assert lf.device_status(kind="backward") & lf.LF_DEV_TOO_MANY_GLOBALS
+    s2 = torch.cuda.Stream()
+    with torch.cuda.stream(s2):
+        lf.backward(*t, mask, out, dout, lse, window=10, validate=False, max_global=5)
+        assert lf.device_status(kind="backward") == 0

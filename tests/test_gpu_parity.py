@@ -192,11 +192,11 @@ def test_too_many_globals_flagged():
     with torch.cuda.stream(s):
         t, g, mask = _dev(prob)
         lf.forward(*t, *g, mask=mask, window=10, validate=False, max_global=2)
-        assert lf.device_status() & lf.LF_DEV_TOO_MANY_GLOBALS
+        assert lf.device_status(kind="forward") & lf.LF_DEV_TOO_MANY_GLOBALS
     s2 = torch.cuda.Stream()
     with torch.cuda.stream(s2):
         lf.forward(*t, *g, mask=mask, window=10, validate=False, max_global=5)
-        assert lf.device_status() == 0
+        assert lf.device_status(kind="forward") == 0
 
 
 # ---------------------------------------------------------------------------
