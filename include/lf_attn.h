@@ -189,6 +189,27 @@ lf_status lf_attn_backward(const lf_attn_params* p,
 lf_status lf_attn_project(int32_t M, int32_t C, int32_t P, int32_t dtype,
                           const void* x, const void* w, const float* bias, void* out, void* stream);
 
+/* Size of the device scratch that lf_attn_forward_noalloc uses instead of a
+ * workspace (one copy per device, held until the process ends). */
+#define LF_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/* lf_attn_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and outputs without the workspace, which
+ * lives in a static device array of this library instead.  Allocates and
+ * frees nothing.  Each call enqueues a small clearing kernel and then the
+ * forward on `stream`.  Every call on one GPU shares that GPU's scratch:
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * and must be ordered by the caller.  Returns LF_ERR_WORKSPACE when
+ * lf_attn_workspace_bytes(p) exceeds LF_NOALLOC_SCRATCH_BYTES (the global
+ * rows' partial records grow with B * H * max_global * ceil(n / 512)), and
+ * otherwise the errors of lf_attn_forward.  The too-many-globals condition
+ * is not reported by this variant: size max_global to the mask. */
+lf_status lf_attn_forward_noalloc(const lf_attn_params* p,
+                                  const void* q, const void* k, const void* v,
+                                  const void* q_g, const void* k_g, const void* v_g,
+                                  const int8_t* mask, void* out, int32_t* row_nnz, void* stream);
+
 /* Debug helper: synchronise `stream`, then read the device status word of
  * `workspace` into *status (LF_DEV_* bits; 0 = no condition seen). */
 lf_status lf_attn_device_status(const void* workspace, void* stream, int32_t* status);

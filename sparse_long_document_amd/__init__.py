@@ -65,8 +65,9 @@ LF_MAX_PROJ = 6
 
 SYMBOLS = ("lf_attn_workspace_bytes", "lf_attn_workspace_init", "lf_attn_forward",
            "lf_attn_forward_lse", "lf_attn_backward_workspace_bytes", "lf_attn_backward",
-           "lf_attn_project",
+           "lf_attn_project", "lf_attn_forward_noalloc",
            "lf_attn_device_status", "lf_status_str")
+LF_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class LfError(RuntimeError):
@@ -119,6 +120,9 @@ def library() -> ctypes.CDLL:
             i32 = ctypes.c_int32
             lib.lf_attn_project.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
             lib.lf_attn_project.restype = ctypes.c_int
+            lib.lf_attn_forward_noalloc.argtypes = [ctypes.POINTER(Params), vp, vp, vp, vp, vp, vp,
+                                                    vp, vp, vp, vp]
+            lib.lf_attn_forward_noalloc.restype = ctypes.c_int
             lib.lf_attn_device_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
             lib.lf_attn_device_status.restype = ctypes.c_int
             lib.lf_status_str.argtypes = [ctypes.c_int32]

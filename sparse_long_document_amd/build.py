@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblf_attn.so")
 
 SOURCES = ["lf_attn_host.cpp", "lf_attn_kernels.hip", "lf_attn_kernels_f16.hip", "lf_attn_bwd.hip",
-           "lf_attn_bwd_f16.hip", "lf_proj.hip"]
+           "lf_attn_bwd_f16.hip", "lf_proj.hip", "lf_attn_noalloc.hip"]
 
 # Device code is built without packed fp32 instructions; the host pass of
 # hipcc does not know the feature and warns, which is harmless.

@@ -104,10 +104,13 @@ lf_status lf_attn_workspace_init(void* workspace, size_t workspace_bytes, void* 
 
 namespace {
 
-lf_status forward_impl(const lf_attn_params* p, const void* q, const void* k, const void* v, const void* q_g,
-                       const void* k_g, const void* v_g, const int8_t* mask, void* out, int32_t* row_nnz,
-                       float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  Plan pl;
+// Every argument check of the forward (no HIP call); with_ws = false skips
+// the checks of the workspace (a library-owned one cannot overlap the
+// caller's buffers).
+lf_status check_forward(const lf_attn_params* p, Plan& pl, const void* q, const void* k, const void* v,
+                        const void* q_g, const void* k_g, const void* v_g, const int8_t* mask, const void* out,
+                        const int32_t* row_nnz, const float* lse, const void* workspace, size_t workspace_bytes,
+                        bool with_ws) {
   const lf_status st = make_plan(p, pl);
   if (st != LF_OK) return st;
   if (!q || !k || !v || !mask || !out) return LF_ERR_INVALID_ARG;
@@ -133,6 +136,7 @@ lf_status forward_impl(const lf_attn_params* p, const void* q, const void* k, co
     if (overlaps(lse, lb, out, tb) || overlaps(lse, lb, mask, mb)) return LF_ERR_INVALID_ARG;
     if (row_nnz && overlaps(lse, lb, row_nnz, nb)) return LF_ERR_INVALID_ARG;
   }
+  if (!with_ws) return LF_OK;
   if (!workspace || workspace_bytes < pl.ws_bytes) return LF_ERR_WORKSPACE;
   // the kernel writes tickets and partial records into the workspace: it
   // may overlap no input and no output
@@ -143,6 +147,19 @@ lf_status forward_impl(const lf_attn_params* p, const void* q, const void* k, co
   if (row_nnz && overlaps(workspace, pl.ws_bytes, row_nnz, nb)) return LF_ERR_INVALID_ARG;
   if (lse && overlaps(workspace, pl.ws_bytes, lse, (size_t)p->B * p->H * p->n * sizeof(float)))
     return LF_ERR_INVALID_ARG;
+  return LF_OK;
+}
+
+lf_status forward_impl(const lf_attn_params* p, const void* q, const void* k, const void* v, const void* q_g,
+                       const void* k_g, const void* v_g, const int8_t* mask, void* out, int32_t* row_nnz,
+                       float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan pl;
+  const lf_status st =
+      check_forward(p, pl, q, k, v, q_g, k_g, v_g, mask, out, row_nnz, lse, workspace, workspace_bytes, true);
+  if (st != LF_OK) return st;
+  if (!q_g) q_g = q;
+  if (!k_g) k_g = k;
+  if (!v_g) v_g = v;
 
   lf::KernelParams kp;
   std::memset(&kp, 0, sizeof(kp));
@@ -196,6 +213,29 @@ lf_status forward_impl(const lf_attn_params* p, const void* q, const void* k, co
 }
 
 }  // namespace
+
+namespace lf {
+
+lf_status check_forward_args(const lf_attn_params* p, const void* q, const void* k, const void* v,
+                             const void* q_g, const void* k_g, const void* v_g, const int8_t* mask,
+                             const void* out, const int32_t* row_nnz, size_t* workspace_bytes) {
+  Plan pl;
+  const lf_status st =
+      check_forward(p, pl, q, k, v, q_g, k_g, v_g, mask, out, row_nnz, nullptr, nullptr, 0, false);
+  if (st == LF_OK && workspace_bytes) *workspace_bytes = pl.ws_bytes;
+  return st;
+}
+
+// The forward with a workspace the caller has already sized and cleared
+// (used by the no-allocation entry point).
+lf_status forward_with_workspace(const lf_attn_params* p, const void* q, const void* k, const void* v,
+                                 const void* q_g, const void* k_g, const void* v_g, const int8_t* mask,
+                                 void* out, int32_t* row_nnz, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return forward_impl(p, q, k, v, q_g, k_g, v_g, mask, out, row_nnz, nullptr, workspace, workspace_bytes, stream);
+}
+
+}  // namespace lf
 
 extern "C" {
 

@@ -108,4 +108,17 @@ int64_t resident_workgroups(int dtype);
 int launch_forward_f16(const KernelParams& kp, void* stream);
 int64_t resident_workgroups_f16();
 
+// Every argument check of lf_attn_forward except those of the workspace (no
+// HIP call); on LF_OK, *workspace_bytes gets the workspace size needed.
+lf_status check_forward_args(const lf_attn_params* p, const void* q, const void* k, const void* v,
+                             const void* q_g, const void* k_g, const void* v_g, const int8_t* mask,
+                             const void* out, const int32_t* row_nnz, size_t* workspace_bytes);
+
+// lf_attn_forward on a caller-provided workspace that is already large
+// enough and cleared (arguments validated as by lf_attn_forward).
+lf_status forward_with_workspace(const lf_attn_params* p, const void* q, const void* k, const void* v,
+                                 const void* q_g, const void* k_g, const void* v_g, const int8_t* mask,
+                                 void* out, int32_t* row_nnz, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 }  // namespace lf
