@@ -127,18 +127,20 @@ def backward(q, k, v, q_g, k_g, v_g, mask, dout, window: int,
 
 
 def row_lse(q, k, q_g, k_g, mask, window: int, dilation: Optional[Sequence[int]] = None,
-            causal: bool = False, scale: Optional[float] = None):
+            causal: bool = False, scale: Optional[float] = None, heads: Optional[Sequence[int]] = None):
     """log sum_{j in S(i)} exp(s <q_i, k_j>) per row, fp64 [B, H, n]; -inf
-    for mask-0 rows (empty key set)."""
+    for mask-0 rows (empty key set).  ``heads`` restricts the work to those
+    heads (the others stay -inf), as in ``backward``."""
     B, n, H, D, mask, dil = _check(q, mask, window, dilation, causal)
     s = 1.0 / math.sqrt(D) if scale is None else float(scale)
     out = np.full((B, H, n), -np.inf)
+    hs = range(H) if heads is None else heads
     for b in range(B):
         mb = mask[b]
         loc = np.flatnonzero(mb == 1)
         glo = np.flatnonzero(mb == 2)
         valid = np.flatnonzero(mb != 0)
-        for h in range(H):
+        for h in hs:
             kb = _f64(k[b, :, h])
             for r0 in range(0, loc.size, ROW_BLOCK):
                 rows = loc[r0:r0 + ROW_BLOCK]

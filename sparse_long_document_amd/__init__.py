@@ -29,7 +29,10 @@ __all__ = [
     "pad_to_window_size", "merge_masks", "library", "LfError", "LF_MAX_GLOBAL", "LF_MAX_HEADS",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblf_attn.so")
+# The built library; LF_ATTN_LIBRARY names another build of the same C ABI
+# (the test suite's sanitizer build of the host code uses it).
+LIB_PATH = os.environ.get("LF_ATTN_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                             "liblf_attn.so")
 KERNEL_SOURCES = ("csrc/lf_attn_kernels.hip", "csrc/lf_attn_kernels_f16.hip", "csrc/lf_attn_internal.h")
 
 

@@ -46,5 +46,27 @@ def build(verbose: bool = False, arch: str = "gfx950") -> str:
     return LIB
 
 
+def build_host_sanitized(out_path: str, verbose: bool = False) -> str:
+    """The host part of the library alone (argument validation, workspace
+    layout, launch planning: lf_attn_host.cpp) built with g++ under the
+    address and undefined-behaviour sanitizers, the device entry points
+    replaced by stubs that report no device (lf_host_stubs.cpp).  A CPU test
+    runs the C-ABI tests against it (LF_ATTN_LIBRARY points the binding at
+    it, and libasan is preloaded into that Python process)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-I", CSRC, "-I", os.path.join(rocm, "include"),
+           os.path.join(CSRC, "lf_attn_host.cpp"), os.path.join(CSRC, "lf_host_stubs.cpp"),
+           "-L", os.path.join(rocm, "lib"), "-Wl,-rpath," + os.path.join(rocm, "lib"), "-lamdhip64",
+           "-o", out_path]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("g++ failed:\n" + r.stdout + r.stderr)
+    return out_path
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

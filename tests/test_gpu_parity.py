@@ -237,6 +237,12 @@ def test_workload_sampled_parity(name):
             err = np.abs(out[b, rows, h] - ref).max()
             worst = max(worst, err)
             assert err <= TOL[prob.q.dtype], (b, h, err)
+    # pair counts of every (b, h) against the oracle's count of the same key
+    # sets (exact integers)
+    for b in range(B):
+        for h in range(H):
+            dil = prob.dilation[h] if prob.dilation else 1
+            assert int(nnz[b, h].sum()) == oracle.pair_count(mask[b], prob.window, dil, prob.causal), (b, h)
     # pair counts: closed forms where the workload has one
     if name == "longformer_base_n4096":
         assert nnz.sum() == 2043134 * 12
@@ -277,3 +283,27 @@ def test_longformer_base_two_heads_full():
         err = np.abs(out[0, :, h] - ref).max()
         _say(f"      head {h}: max abs err {err:.3e}")
         assert err <= 2e-2
+
+
+@pytest.mark.parametrize("name,pairs", [
+    ("qa_padded_b2_n4096", [(0, 0), (1, 11)]),
+    ("charlm_causal_dilated_n23040", [(0, 0), (0, 7)]),
+    ("led_large_n16384", [(0, 0), (0, 15)]),
+    ("charlm_causal_dilated_n32256", [(0, 5), (0, 6)]),
+])
+def test_workload_two_heads_full(name, pairs):
+    """Every row of two (batch row, head) pairs of each full-size workload
+    against the oracle (the dilated workloads: one undilated and one dilated
+    head), in the launch configuration the benchmark times."""
+    prob = workloads.by_name(name)
+    out, nnz = run_gpu(prob, validate=False, max_global=prob.max_global())
+    arrs = _np(prob)
+    mask = prob.mask.numpy()
+    n = prob.shape[1]
+    for b, h in pairs:
+        ref, rnnz = oracle.forward_rows(*arrs, mask, prob.window, b, h, range(n), dilation=prob.dilation,
+                                        causal=prob.causal, scale=prob.scale)
+        np.testing.assert_array_equal(nnz[b, h], rnnz)
+        err = np.abs(out[b, :, h] - ref).max()
+        _say(f"      {name} (b {b}, h {h}): max abs err {err:.3e}")
+        assert err <= TOL[prob.q.dtype], (b, h, err)
