@@ -257,6 +257,58 @@ class ProjRunner:
             raise RuntimeError(f"lf_attn_project failed with status {st}")
 
 
+class EncRunner:
+    """The encoder attention sublayer as one step: the six input projections,
+    the attention and the output projection (three launches), on the LED
+    encoder workload's shape."""
+
+    def __init__(self, prob, device):
+        import torch
+
+        import sparse_long_document_amd as lf
+        import workloads
+
+        self.lf = lf
+        self.enc = workloads.led_encoder_n16384() if prob is None else prob
+        e = self.enc
+        B, n, C = e.shape
+        self.x, self.w, self.bias = e.x.to(device), e.w.to(device), e.bias.to(device)
+        self.w_out, self.b_out = e.w_out.to(device), e.b_out.to(device)
+        self.mask = e.mask.to(device)
+        self.mg = e.max_global()
+        self.ws = lf.make_workspace(B, n, e.H, e.window, max_global=self.mg, dtype=e.x.dtype)
+        self.out_t = torch.empty((B, n, C), dtype=e.x.dtype, device=device)
+        self.args = (None,)  # the stream is torch's current one
+
+    def launch(self):
+        y = self.lf.encoder_attention(self.x, self.w, self.bias, self.mask, self.enc.window, max_global=self.mg,
+                                      validate=False, w_out=self.w_out, b_out=self.b_out, workspace=self.ws)
+        self.out_t.copy_(y)
+
+
+def report_encoder(args, run, ms, mode, t_wall):
+    import torch
+
+    e = run.enc
+    B, n, C = e.shape
+    H = e.H
+    flops_proj = 2.0 * B * n * C * 7 * C  # six input projections and the output projection
+    flops_band = 4.0 * B * n * (2 * e.window + 1) * 64 * H
+    result = {
+        "metric": "LED encoder attention sublayer tokens/s (projections, attention, output projection), bf16",
+        "value": B * n / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) hidden states, N(0,1/C) weights, token 0 + 16 random global)",
+        "config": {"workload": e.name, "pass": "encoder", "B": B, "n": n, "C": C, "H": H, "w": e.window,
+                   "globals_per_row": [int(x) for x in (e.mask == 2).sum(dim=1).tolist()],
+                   "timing": mode, "wall_s": round(t_wall, 3)},
+        "flops": {"projections": flops_proj, "attention_band": flops_band},
+        "mfma_frac": (flops_proj + flops_band) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def report_projections(args, prob, run, ms, mode, t_wall):
     import numpy as np
     import torch
@@ -542,7 +594,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time direct launches instead of a graph replay")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "projections"], default="forward")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "projections", "encoder"],
+                    default="forward")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing")
     ap.add_argument("--sweep", action="store_true",
                     help="time the longformer-base layer at n = 1024 ... 16384 instead (one line each)")
@@ -559,11 +612,12 @@ def main():
 
     if args.sweep:
         return sweep(args)
-    prob = workloads.by_name(args.workload)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     bwd = args.which != "forward"  # a runner with out_t, compared across graph replays
-    run = {"forward": Runner, "backward": BwdRunner, "projections": ProjRunner}[args.which](prob, dev)
+    prob = None if args.which == "encoder" else workloads.by_name(args.workload)
+    run = {"forward": Runner, "backward": BwdRunner, "projections": ProjRunner,
+           "encoder": EncRunner}[args.which](prob, dev)
     for _ in range(max(1, args.warmup)):
         run.launch()
     torch.cuda.synchronize()
@@ -571,6 +625,8 @@ def main():
     K = args.steps
     ms, mode, t_wall = time_graph(run, K, eager=args.eager, bwd=bwd)
 
+    if args.which == "encoder":
+        return report_encoder(args, run, ms, mode, t_wall)
     B, n, H, D = prob.shape
     if args.which == "backward":
         return report_backward(args, prob, run, ms, mode, t_wall)

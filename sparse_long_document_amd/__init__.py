@@ -25,7 +25,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "forward", "backward", "project", "workspace_bytes", "make_workspace", "device_status",
+    "forward", "backward", "project", "encoder_attention", "workspace_bytes", "make_workspace", "device_status",
     "pad_to_window_size", "merge_masks", "library", "LfError", "LF_MAX_GLOBAL", "LF_MAX_HEADS",
 ]
 
@@ -361,6 +361,39 @@ def project(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = Non
     if st != LF_OK:
         raise LfError(st, "lf_attn_project")
     return out.view((P,) + tuple(shape[:-1]) + (C,))
+
+
+def encoder_attention(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], mask: Optional[torch.Tensor],
+                      window: int, dilation: Optional[Sequence[int]] = None, scale: Optional[float] = None,
+                      max_global: Optional[int] = None, validate: bool = True,
+                      w_out: Optional[torch.Tensor] = None, b_out: Optional[torch.Tensor] = None,
+                      return_intermediate: bool = False, workspace: Optional[torch.Tensor] = None):
+    """The attention sublayer of a Longformer/LED encoder layer as a chain
+    of the C ABI's calls on the current stream: ``lf_attn_project`` (the six
+    input projections Q_s, K_s, V_s, Q_g, K_g, V_g of x [B, n, C] in one
+    launch, w [6C, C] stacked in that order, bias fp32 [6C] or None), then
+    ``lf_attn_forward`` on the six [B, n, H, 64] views of its output (H =
+    C / 64), then, when w_out [C, C] is given, the output projection with
+    ``lf_attn_project`` (P = 1, bias b_out fp32 [C] or None).  Returns
+    [B, n, C] (and, with return_intermediate, the projections [6, B, n, C]
+    and the attention output [B, n, H, 64]).  workspace: the attention's,
+    from make_workspace (needed under graph capture)."""
+    if x.dim() != 3:
+        raise ValueError("x must be [B, n, C]")
+    B, n, C = x.shape
+    if C % LF_HEAD_DIM != 0:
+        raise ValueError("C must be a multiple of 64")
+    H = C // LF_HEAD_DIM
+    if w.shape != (6 * C, C):
+        raise ValueError("w must be [6C, C]: Q_s, K_s, V_s, Q_g, K_g, V_g stacked")
+    proj = project(x, w, bias)  # [6, B, n, C]
+    heads = [proj[i].view(B, n, H, LF_HEAD_DIM) for i in range(6)]
+    attn = forward(*heads, mask=mask, window=window, dilation=dilation, scale=scale, max_global=max_global,
+                   validate=validate, workspace=workspace)
+    y = attn.view(B, n, C)
+    if w_out is not None:
+        y = project(y, w_out, b_out)[0]
+    return (y, proj, attn) if return_intermediate else y
 
 
 def _prep_mask(mask, B, n, device, causal, max_global, validate):

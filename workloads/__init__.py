@@ -257,6 +257,68 @@ def longformer_base_n4096_f16() -> Problem:
     return p
 
 
+@dataclasses.dataclass
+class EncoderProblem:
+    """Inputs of one encoder attention sublayer: hidden states, the six
+    stacked input projections (Q_s, K_s, V_s, Q_g, K_g, V_g) with their
+    bias, the output projection with its bias, and the 0/1/2 mask."""
+
+    name: str
+    x: torch.Tensor       # [B, n, C]
+    w: torch.Tensor       # [6C, C]
+    bias: torch.Tensor    # fp32 [6C]
+    w_out: torch.Tensor   # [C, C]
+    b_out: torch.Tensor   # fp32 [C]
+    mask: torch.Tensor    # int8 [B, n]
+    H: int
+    window: int
+
+    @property
+    def shape(self):
+        return tuple(self.x.shape)
+
+    def max_global(self) -> int:
+        return int((self.mask == 2).sum(dim=1).max().item())
+
+
+def encoder_problem(seed: int, B: int, n: int, H: int, window: int, n_global: int = 0,
+                    dtype: torch.dtype = torch.bfloat16, name: str = "encoder",
+                    copied_global: bool = False) -> EncoderProblem:
+    """Hidden states x ~ N(0, 1) [B, n, C] (C = 64 H), stacked projection
+    weights ~ N(0, 1/C) [6C, C] with an fp32 bias ~ N(0, 0.1^2), an output
+    projection of the same kind, global tokens at position 0 and n_global - 1
+    further distinct random positions per batch row.  copied_global: the
+    global projections start as copies of the local ones (weights and bias),
+    their initial state on the pages (segmentfault Longformer summary,
+    "Linear projections for global attention")."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    C = H * D_HEAD
+    x = _draw(rng, (B, n, C), dtype)
+    w = rng.standard_normal((6 * C, C), dtype=np.float32) / np.float32(np.sqrt(C))
+    bias = rng.standard_normal(6 * C, dtype=np.float32) * np.float32(0.1)
+    if copied_global:
+        w[3 * C:] = w[:3 * C]
+        bias[3 * C:] = bias[:3 * C]
+    w_out = rng.standard_normal((C, C), dtype=np.float32) / np.float32(np.sqrt(C))
+    b_out = rng.standard_normal(C, dtype=np.float32) * np.float32(0.1)
+    mask = torch.ones((B, n), dtype=torch.int8)
+    for b in range(B):
+        if n_global > 0:
+            mask[b, 0] = 2
+            if n_global > 1:
+                g = rng.choice(np.arange(1, n), size=n_global - 1, replace=False)
+                mask[b, torch.from_numpy(g.astype(np.int64))] = 2
+    return EncoderProblem(name, x, torch.from_numpy(w).to(dtype), torch.from_numpy(bias),
+                          torch.from_numpy(w_out).to(dtype), torch.from_numpy(b_out), mask, H, window)
+
+
+def led_encoder_n16384() -> EncoderProblem:
+    """The LED-large encoder attention sublayer at 16K tokens: B1 n16384 H16
+    (C = 1024), w = 512 per side, bf16, token 0 plus 16 random positions
+    global (the LED workload's mask recipe).  Seed 7."""
+    return encoder_problem(7, 1, 16384, 16, 512, n_global=17, name="led_encoder_n16384")
+
+
 SWEEP_N = (1024, 2048, 4096, 8192, 16384)
 
 
