@@ -21,7 +21,7 @@
  *     to a multiple of the window: allenai/longformer README, "Usage".
  *
  * Definition computed, for every batch row b and head h (d = dilation[h],
- * s = scale, D = 64), with W(i) = { i + k*d : -w <= k <= (causal ? 0 : w),
+ * s = scale, D the head dim), with W(i) = { i + k*d : -w <= k <= (causal ? 0 : w),
  * 0 <= i + k*d < n }, Valid = { j : mask[b,j] != 0 }, G = { j : mask[b,j] == 2 }:
  *   mask[b,i] == 1 (local row):  S(i) = (W(i) u G) n Valid,
  *       out[b,i,h] = sum_{j in S(i)} softmax_j(s <q[b,i,h], k[b,j,h]>) v[b,j,h]
@@ -59,7 +59,7 @@ extern "C" {
 typedef enum {
   LF_OK = 0,
   LF_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, bad window/dilation/scale, aliasing */
-  LF_ERR_UNSUPPORTED = 2, /* D != 64, unknown dtype, a size above the limits below */
+  LF_ERR_UNSUPPORTED = 2, /* D not a supported head dim, unknown dtype, a size above the limits below */
   LF_ERR_WORKSPACE = 3,   /* workspace missing or smaller than lf_attn_workspace_bytes */
   LF_ERR_HIP = 4          /* the HIP runtime refused the launch */
 } lf_status;
@@ -69,8 +69,14 @@ typedef enum {
  * the element type (fp32, bf16 or f16). */
 typedef enum { LF_F32 = 0, LF_BF16 = 1, LF_F16 = 2 } lf_dtype;
 
-/* Limits of this build. */
-#define LF_HEAD_DIM 64
+/* Limits of this build.  The forward takes head dims D = 32, 64 and 128 (a
+ * kernel build each).  The pages print no head size: they name the
+ * longformer-base and led-base checkpoints (allenai/longformer README,
+ * "Usage"; segmentfault summary, the LED models), whose heads are 64 wide,
+ * and the window and global pattern never depend on D.  The backward takes
+ * D = LF_BWD_HEAD_DIM only. */
+#define LF_HEAD_DIM 64       /* the default head dim (longformer-base) */
+#define LF_BWD_HEAD_DIM 64
 #define LF_MAX_HEADS 64
 #define LF_MAX_GLOBAL 1024   /* global tokens per batch row */
 #define LF_MAX_SEQ (1 << 24)
@@ -80,7 +86,7 @@ typedef enum { LF_F32 = 0, LF_BF16 = 1, LF_F16 = 2 } lf_dtype;
 #define LF_DEV_TOO_MANY_GLOBALS 1 /* a batch row held more than max_global tokens with mask 2 */
 
 typedef struct {
-  int32_t B, n, H, D;        /* B, n, H >= 1; D must be 64 */
+  int32_t B, n, H, D;        /* B, n, H >= 1; D is 32, 64 or 128 */
   int32_t window;            /* one-sided w >= 0; the pages' attention_window is 2w */
   const int32_t* dilation;   /* HOST array [H], each >= 1; NULL means all 1 */
   int32_t causal;            /* 0 or 1 */
@@ -143,7 +149,9 @@ size_t lf_attn_backward_workspace_bytes(const lf_attn_params* p);
  *   dS_ij = P_ij (<dout_i, v_j> - D_i),
  *   dq_i = s sum_j dS_ij k_j,  dk_j = s sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i,
  * with (q, k, v) for local rows and (q_g, k_g, v_g) for global rows.
- *   - dtype must be LF_BF16 or LF_F16 (LF_ERR_UNSUPPORTED otherwise); q..v_g,
+ *   - D must be LF_BWD_HEAD_DIM and dtype LF_BF16 or LF_F16
+ *     (LF_ERR_UNSUPPORTED otherwise, and lf_attn_backward_workspace_bytes
+ *     returns 0); q..v_g,
  *     out and dout are [B, n, H, D] of that type; out and lse are what
  *     lf_attn_forward_lse wrote for the same inputs and parameters.
  *   - dq, dk, dv, dq_g, dk_g, dv_g are fp32 [B, n, H, D], caller-owned, each

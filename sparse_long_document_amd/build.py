@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblf_attn.so")
 
-SOURCES = ["lf_attn_host.cpp", "lf_attn_kernels.hip", "lf_attn_kernels_f16.hip", "lf_attn_bwd.hip",
+SOURCES = ["lf_attn_host.cpp", "lf_attn_kernels.hip", "lf_attn_kernels_f16.hip", "lf_attn_kernels_d32.hip",
+           "lf_attn_kernels_f16_d32.hip", "lf_attn_kernels_d128.hip", "lf_attn_kernels_f16_d128.hip", "lf_attn_bwd.hip",
            "lf_attn_bwd_f16.hip", "lf_proj.hip", "lf_attn_noalloc.hip"]
 
 # Device code is built without packed fp32 instructions; the host pass of

@@ -37,7 +37,7 @@ lf_status make_plan(const lf_attn_params* p, Plan& pl) {
   if (p->causal != 0 && p->causal != 1) return LF_ERR_INVALID_ARG;
   if (!std::isfinite(p->scale) || p->scale < 0.f) return LF_ERR_INVALID_ARG;
   if (p->max_global < 0) return LF_ERR_INVALID_ARG;
-  if (p->D != LF_HEAD_DIM) return LF_ERR_UNSUPPORTED;
+  if (p->D != 32 && p->D != 64 && p->D != 128) return LF_ERR_UNSUPPORTED;
   if (p->dtype != LF_F32 && p->dtype != LF_BF16 && p->dtype != LF_F16) return LF_ERR_UNSUPPORTED;
   if (p->H > LF_MAX_HEADS || p->max_global > LF_MAX_GLOBAL || p->n > LF_MAX_SEQ) return LF_ERR_UNSUPPORTED;
   const int64_t tokens = (int64_t)p->B * p->n;
@@ -73,7 +73,7 @@ lf_status make_plan(const lf_attn_params* p, Plan& pl) {
   pl.ws_partials_off = pl.ws_tickets_off + align_up(bh * sizeof(int32_t), kAlign);
   size_t partial_bytes = 0;
   if (pl.use_globals)
-    partial_bytes = bh * (size_t)p->max_global * (size_t)pl.S * lf::kPartialStride * sizeof(float);
+    partial_bytes = bh * (size_t)p->max_global * (size_t)pl.S * lf::partial_stride(p->D) * sizeof(float);
   pl.ws_bytes = pl.ws_partials_off + align_up(partial_bytes, kAlign);
   return LF_OK;
 }
@@ -192,7 +192,7 @@ lf_status forward_impl(const lf_attn_params* p, const void* q, const void* k, co
   // resident at once, long ones otherwise (both fit the workspace).
   int chunk = lf::kGlobalChunkLong;
   if (pl.use_globals) {
-    const int64_t resident = lf::resident_workgroups(p->dtype);
+    const int64_t resident = lf::resident_workgroups(p->dtype, p->D);
     const int64_t short_splits = (int64_t)p->B * p->H * pl.S;
     if (resident > 0 && (int64_t)kp.n_band + short_splits <= resident) chunk = lf::kGlobalChunkShort;
   }
@@ -208,7 +208,7 @@ lf_status forward_impl(const lf_attn_params* p, const void* q, const void* k, co
   for (int h = 1; h < p->H; ++h)
     if (pl.dil[h] != pl.dil[0]) kp.uni_dil = 0;
   kp.tiles_per_head = kp.uni_dil > 0 ? pl.tile0[1] - pl.tile0[0] : 0;
-  const int e = lf::launch_forward(kp, p->dtype, stream);
+  const int e = lf::launch_forward(kp, p->dtype, p->D, stream);
   return e == 0 ? LF_OK : LF_ERR_HIP;
 }
 
@@ -278,7 +278,7 @@ extern "C" {
 
 size_t lf_attn_backward_workspace_bytes(const lf_attn_params* p) {
   Plan pl;
-  if (make_plan(p, pl) != LF_OK) return 0;
+  if (make_plan(p, pl) != LF_OK || p->D != LF_BWD_HEAD_DIM) return 0;
   return bwd_layout(p).bytes;
 }
 
@@ -291,6 +291,7 @@ lf_status lf_attn_backward(const lf_attn_params* p, const void* q, const void* k
   const lf_status st = make_plan(p, pl);
   if (st != LF_OK) return st;
   if (p->dtype != LF_BF16 && p->dtype != LF_F16) return LF_ERR_UNSUPPORTED;
+  if (p->D != LF_BWD_HEAD_DIM) return LF_ERR_UNSUPPORTED;
   if (!q || !k || !v || !mask || !out || !dout || !lse) return LF_ERR_INVALID_ARG;
   if (!dq || !dk || !dv || !dq_g || !dk_g || !dv_g) return LF_ERR_INVALID_ARG;
   if (!q_g) q_g = q;

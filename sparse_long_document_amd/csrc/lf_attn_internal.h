@@ -10,7 +10,6 @@
 namespace lf {
 
 // Tiling constants shared by the host planner and the kernels.
-constexpr int kHeadDim = 64;       // D
 constexpr int kTileQ = 64;         // query rows of one band workgroup (two halves of 32)
 constexpr int kBlockK = 32;        // keys per inner block (M of the 32x32 MFMA)
 constexpr int kWaves = 4;          // waves per workgroup: query half x key parity
@@ -20,7 +19,9 @@ constexpr int kThreads = 64 * kWaves;
 // fewer records to merge).  The workspace is sized for the short one.
 constexpr int kGlobalChunkShort = 512;
 constexpr int kGlobalChunkLong = 1024;
-constexpr int kPartialStride = 68; // floats per partial record: m, l, count, pad, O[64]
+// Floats per partial record of a global-row split at head dim D: m, l,
+// count, pad, O[D].
+constexpr int partial_stride(int D) { return 4 + D; }
 
 // Everything one launch needs, passed by value as the kernel argument.
 struct KernelParams {
@@ -36,7 +37,7 @@ struct KernelParams {
   float* lse;          // may be null: natural log-sum-exp of each row's scores [B][H][n]
   int32_t* status;     // device status word
   int32_t* tickets;    // [B*H] arrival counters of the global-row splits
-  float* partials;     // [B][H][max_global][S][kPartialStride]
+  float* partials;     // [B][H][max_global][S][partial_stride(D)]
   int32_t B, n, H, w, causal, max_global, use_globals;
   float c;             // score scale * log2(e)
   int32_t tiles_per_b; // band workgroups per batch row
@@ -96,17 +97,28 @@ struct BwdParams {
 int launch_backward(const BwdParams& bp, void* stream);
 int launch_backward_f16(const BwdParams& bp, void* stream);
 
-// Launches the forward kernel.  Returns the hipError_t value as int.
-int launch_forward(const KernelParams& kp, int dtype, void* stream);
+// Launches the forward kernel of head dim D (32, 64 or 128) for dtype.
+// Returns the hipError_t value as int.
+int launch_forward(const KernelParams& kp, int dtype, int D, void* stream);
 
-// Workgroups of the forward kernel that the current device holds at once
+// Workgroups of that forward kernel that the current device holds at once
 // (compute units times workgroups per unit), or 0 if the runtime cannot say.
-int64_t resident_workgroups(int dtype);
+int64_t resident_workgroups(int dtype, int D);
 
-// The same two for the f16 kernel, which the kernel source yields when it is
-// compiled a second time with LF_HALF_F16 (lf_attn_kernels_f16.hip).
-int launch_forward_f16(const KernelParams& kp, void* stream);
-int64_t resident_workgroups_f16();
+// The units behind the two: lf_attn_kernels.hip compiled once per head dim
+// D (LF_KD = D) into namespace d<D>, for bf16 and fp32 elements, and once
+// more with LF_HALF_F16 for f16 elements (lf_attn_kernels*.hip).
+#define LF_FORWARD_UNITS(ns)                                          \
+  namespace ns {                                                      \
+  int launch(const KernelParams& kp, int dtype, void* stream);        \
+  int64_t resident(int dtype);                                        \
+  int launch_f16(const KernelParams& kp, void* stream);               \
+  int64_t resident_f16();                                             \
+  }
+LF_FORWARD_UNITS(d32)
+LF_FORWARD_UNITS(d64)
+LF_FORWARD_UNITS(d128)
+#undef LF_FORWARD_UNITS
 
 // Every argument check of lf_attn_forward except those of the workspace (no
 // HIP call); on LF_OK, *workspace_bytes gets the workspace size needed.

@@ -43,6 +43,12 @@
 //
 // The fp32 instantiation computes in true fp32 (v_mfma_f32_32x32x2_f32, P
 // kept in fp32).
+//
+// Head dim: the source is compiled once per head dim D = LF_KD (32, 64 or
+// 128; 64 when not defined) into its own namespace lf::d<D>.  The pages
+// describe the layer with one head size (64 in the longformer-base shape)
+// and the window and global pattern never look at the head dim, so D only
+// sets the fragment counts, the stage sizes and the swizzles below.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,8 +58,20 @@
 
 #include "lf_attn_internal.h"
 
+#ifndef LF_KD
+#define LF_KD 64
+#endif
+#define LF_CAT2(a, b) a##b
+#define LF_CAT(a, b) LF_CAT2(a, b)
+
 namespace lf {
+namespace LF_CAT(d, LF_KD) {
 namespace {
+
+constexpr int kD = LF_KD;     // head dim of this instantiation
+constexpr int kND = kD / 32;  // 32-dim blocks of O^T (kD x 32 queries) per wave
+static_assert(kD == 32 || kD == 64 || kD == 128, "head dims 32, 64 and 128");
+constexpr int kPartialStride = partial_stride(kD);
 
 // The 16-bit element type of this translation unit: bf16, or f16 when the
 // source is compiled with LF_HALF_F16 (which then yields the f16 kernel).
@@ -104,14 +122,17 @@ __device__ __forceinline__ float row_lse(float M, float L) {
 }
 
 // LDS staging of key blocks.  A stage holds one block's K rows then its V
-// rows (32 rows of 64 head dims each); each key parity owns a ring of
+// rows (32 rows of kD head dims each); each key parity owns a ring of
 // kStages stages, filled by direct-to-LDS loads while older stages are
 // consumed.
 template <bool B16>
 struct Lay {
   static constexpr int kElt = B16 ? 2 : 4;
-  static constexpr int kRowBytes = kHeadDim * kElt;      // 128 | 256
+  static constexpr int kRowBytes = kD * kElt;            // 64 .. 512
   static constexpr int kChunks = kRowBytes / 16;         // 16-byte chunks per row
+  // rows that share one 256-byte span of the LDS banks (1, 2 or 4)
+  static constexpr int kRowsPerSpan = kRowBytes >= 256 ? 1 : 256 / kRowBytes;
+  static_assert(kRowsPerSpan == 1 || kRowsPerSpan == 2 || kRowsPerSpan == 4, "row sizes 64 B and up");
   static constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows covered by one wave-wide load
   static constexpr int kLoads = kBlockK / kRowsPerLoad;  // loads per block and tensor
   static constexpr int kHalfLoads = kLoads / 2;          // of those, issued by one wave of the pair
@@ -122,32 +143,41 @@ struct Lay {
 };
 
 // Chunk swizzles (the LDS position of 16-byte chunk c of row `row` is
-// c ^ swz(row)).  K: 16 consecutive rows at one chunk index land on
-// distinct banks, for the K fragment reads.  V (bf16): the transposed reads
-// of a half-wave land on distinct banks.  V (fp32) is read along rows.
+// c ^ swz(row)).  With R rows per 256-byte bank span, row `row` starts at
+// span offset (row % R) * rowbytes.  K: 16 consecutive rows at one chunk
+// index land on distinct 16-byte slots of the span (R offsets times 16 / R
+// swizzle values), for the K fragment reads.  V (16-bit): the transposed
+// reads of a half-wave cover 4 consecutive rows (key rows 4a + e, e < 4) at
+// one 64-byte column group, which land on distinct 64-byte quarters of the
+// span (R offsets times 4 / R swizzle values of the group index).  V (fp32)
+// is read along rows.
 template <bool B16>
 __device__ __forceinline__ int kswz(int row) {
-  return B16 ? ((row >> 1) & 7) : (row & 15);
+  constexpr int R = Lay<B16>::kRowsPerSpan;
+  constexpr int lgR = R == 4 ? 2 : (R == 2 ? 1 : 0);
+  return (row >> lgR) & (16 / R - 1);
 }
 template <bool B16>
 __device__ __forceinline__ int vswz(int row) {
-  return B16 ? (((row >> 1) & 1) << 2) : 0;
+  constexpr int R = Lay<B16>::kRowsPerSpan;
+  constexpr int lgR = R == 4 ? 2 : (R == 2 ? 1 : 0);
+  return B16 ? (((row >> lgR) & (4 / R - 1)) << 2) : 0;
 }
 
 template <bool B16>
 using elem_t = typename std::conditional<B16, h16, float>::type;
 
-// Per-lane operand fragment of 64 head dims of one row (query or key) for
-// the QK^T contraction; the head dims a lane holds depend on lane / 32.
+// Per-lane operand fragment of the kD head dims of one row (query or key)
+// for the QK^T contraction; the head dims a lane holds depend on lane / 32.
 template <bool B16>
 struct Frag;
 template <>
 struct Frag<true> {
-  h16x8 x[4];  // dims 16s + 8*(lane/32) + [0, 8)
+  h16x8 x[kD / 16];  // dims 16s + 8*(lane/32) + [0, 8)
 };
 template <>
 struct Frag<false> {
-  float x[32];  // dims 32*(lane/32) + [0, 32)
+  float x[kD / 2];  // dims (kD/2)*(lane/32) + [0, kD/2)
 };
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
@@ -187,13 +217,13 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 __device__ __forceinline__ void load_frag(Frag<true>& f, const h16* row, int hh) {
   const h16x8* p = reinterpret_cast<const h16x8*>(row);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) f.x[s] = p[2 * s + hh];
+  for (int s = 0; s < kD / 16; ++s) f.x[s] = p[2 * s + hh];
 }
 
 __device__ __forceinline__ void load_frag(Frag<false>& f, const float* row, int hh) {
-  const f32x4* p = reinterpret_cast<const f32x4*>(row + 32 * hh);
+  const f32x4* p = reinterpret_cast<const f32x4*>(row + (kD / 2) * hh);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kD / 8; ++i) {
     f32x4 t = p[i];
     f.x[4 * i + 0] = t[0];
     f.x[4 * i + 1] = t[1];
@@ -202,15 +232,15 @@ __device__ __forceinline__ void load_frag(Frag<false>& f, const float* row, int 
   }
 }
 
-// acc (32 keys x 32 queries) += K Q^T over the 64 head dims.
+// acc (32 keys x 32 queries) += K Q^T over the kD head dims.
 __device__ __forceinline__ void qk(f32x16& acc, const Frag<true>& kf, const Frag<true>& qf) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) acc = mfma16(kf.x[s], qf.x[s], acc);
+  for (int s = 0; s < kD / 16; ++s) acc = mfma16(kf.x[s], qf.x[s], acc);
 }
 
 __device__ __forceinline__ void qk(f32x16& acc, const Frag<false>& kf, const Frag<false>& qf) {
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.x[i], qf.x[i], acc, 0, 0, 0);
+  for (int i = 0; i < kD / 2; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.x[i], qf.x[i], acc, 0, 0, 0);
 }
 
 // Accumulator element r of a lane holds key row c_r + 4*(lane/32) of the
@@ -254,11 +284,11 @@ template <bool B16>
 struct VtFrag;
 template <>
 struct VtFrag<true> {
-  h16x8 a[2][2];
+  h16x8 a[kND][2];
 };
 template <>
 struct VtFrag<false> {
-  float a[2][16];
+  float a[kND][16];
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -267,15 +297,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // Per-lane LDS addresses of the fragment reads of stage 0 of a ring (the
 // other stage is kStageBytes further, an immediate offset).
-//   K: key row lane % 32, 16-byte chunks 2s + lane/32 (s = 0..3), swizzled;
+//   K: key row lane % 32, 16-byte chunks 2s + lane/32 (s < kD/16), swizzled;
 //   V: ds_read_b64_tr_b16: in each group of 16 lanes, lane j receives
 //   element j%4 of the 8-byte chunk addressed by lane 4e + j/4, as its
 //   element e.  Lane 4e+q of group g points at key row 16ks + 8half +
 //   4(g/2) + e, head dims 32db + 16(g%2) + 4q .. +3, so lane j of the group
 //   gets head dim 32db + 16(g%2) + j for keys e = 0..3.
 struct FragAddr {
-  uint32_t k[4];
-  uint32_t v[2];
+  uint32_t k[kD / 16];
+  uint32_t v[kND];
 };
 
 __device__ __forceinline__ FragAddr frag_addr(const unsigned char* ring, int lane) {
@@ -286,16 +316,18 @@ __device__ __forceinline__ FragAddr frag_addr(const unsigned char* ring, int lan
   const uint32_t kbase = lds_addr(ring) + (uint32_t)(row * L::kRowBytes);
   const int sw = kswz<true>(row);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) fa.k[s] = kbase + (uint32_t)(((2 * s + hh) ^ sw) << 4);
+  for (int s = 0; s < kD / 16; ++s) fa.k[s] = kbase + (uint32_t)(((2 * s + hh) ^ sw) << 4);
   const int g = lane >> 4;
   const int row0 = 4 * (g >> 1) + ((lane & 15) >> 2);
   const int byte0 = 32 * (g & 1) + 8 * (lane & 3);
-  const int vsw = vswz<true>(row0);  // rows 16ks + 8half + row0 share bit 1 with row0
+  // vswz depends on the row mod 4 only, so rows 16ks + 8half + row0 share
+  // row0's swizzle
+  const int vsw = vswz<true>(row0);
   const uint32_t vbase = lds_addr(ring + L::kBlockBytes);
 #pragma unroll
-  for (int db = 0; db < 2; ++db) {
+  for (int db = 0; db < kND; ++db) {
     const int byte = 64 * db + byte0;
-    fa.v[db] = vbase + (uint32_t)(row0 * 128 + (((byte >> 4) ^ vsw) << 4) + (byte & 15));
+    fa.v[db] = vbase + (uint32_t)(row0 * L::kRowBytes + (((byte >> 4) ^ vsw) << 4) + (byte & 15));
   }
   return fa;
 }
@@ -305,11 +337,90 @@ __device__ __forceinline__ FragAddr frag_addr(const unsigned char* ring, int lan
 // compiler cannot tell these reads from the direct-to-LDS loads still in
 // flight into the other stage and would otherwise wait for all of them
 // first; the caller has waited for this stage's loads (and the barrier
-// after which the other wave's share is visible).
+// after which the other wave's share is visible).  V rows 16ks + 8half sit
+// kV8 (ks = 0, half = 1), 2 kV8 and 3 kV8 bytes past the first.
+constexpr int kV8 = 8 * Lay<true>::kRowBytes;
+
+// r[4db + 2ks + half] back into the V^T operand
+__device__ __forceinline__ void assemble_vt(VtFrag<true>& vt, const u32x2* r) {
+#pragma unroll
+  for (int db = 0; db < kND; ++db)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x2 lo = r[4 * db + 2 * ks], hi = r[4 * db + 2 * ks + 1];
+      vt.a[db][ks] = __builtin_bit_cast(h16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
+}
+
+#if LF_KD == 32
+template <int kOff>
+__device__ __forceinline__ void read_frags_at(Frag<true>& kf, VtFrag<true>& vt, const FragAddr& fa) {
+  u32x4 k[2];
+  u32x2 r[4];
+  asm volatile(
+      "ds_read_b128 %0, %6 offset:%9\n"
+      "ds_read_b128 %1, %7 offset:%9\n"
+      "ds_read_b64_tr_b16 %2, %8 offset:%9\n"
+      "ds_read_b64_tr_b16 %3, %8 offset:%10\n"
+      "ds_read_b64_tr_b16 %4, %8 offset:%11\n"
+      "ds_read_b64_tr_b16 %5, %8 offset:%12\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(fa.k[0]), "v"(fa.k[1]), "v"(fa.v[0]), "i"(kOff), "i"(kOff + kV8), "i"(kOff + 2 * kV8),
+        "i"(kOff + 3 * kV8)
+      : "memory");
+#pragma unroll
+  for (int s = 0; s < 2; ++s) kf.x[s] = __builtin_bit_cast(h16x8, k[s]);
+  assemble_vt(vt, r);
+}
+#elif LF_KD == 128
+template <int kOff>
+__device__ __forceinline__ void read_frags_at(Frag<true>& kf, VtFrag<true>& vt, const FragAddr& fa) {
+  u32x4 k[8];
+  u32x2 r[16];
+  asm volatile(
+      "ds_read_b128 %0, %24 offset:%36\n"
+      "ds_read_b128 %1, %25 offset:%36\n"
+      "ds_read_b128 %2, %26 offset:%36\n"
+      "ds_read_b128 %3, %27 offset:%36\n"
+      "ds_read_b128 %4, %28 offset:%36\n"
+      "ds_read_b128 %5, %29 offset:%36\n"
+      "ds_read_b128 %6, %30 offset:%36\n"
+      "ds_read_b128 %7, %31 offset:%36\n"
+      "ds_read_b64_tr_b16 %8, %32 offset:%36\n"
+      "ds_read_b64_tr_b16 %9, %32 offset:%37\n"
+      "ds_read_b64_tr_b16 %10, %32 offset:%38\n"
+      "ds_read_b64_tr_b16 %11, %32 offset:%39\n"
+      "ds_read_b64_tr_b16 %12, %33 offset:%36\n"
+      "ds_read_b64_tr_b16 %13, %33 offset:%37\n"
+      "ds_read_b64_tr_b16 %14, %33 offset:%38\n"
+      "ds_read_b64_tr_b16 %15, %33 offset:%39\n"
+      "ds_read_b64_tr_b16 %16, %34 offset:%36\n"
+      "ds_read_b64_tr_b16 %17, %34 offset:%37\n"
+      "ds_read_b64_tr_b16 %18, %34 offset:%38\n"
+      "ds_read_b64_tr_b16 %19, %34 offset:%39\n"
+      "ds_read_b64_tr_b16 %20, %35 offset:%36\n"
+      "ds_read_b64_tr_b16 %21, %35 offset:%37\n"
+      "ds_read_b64_tr_b16 %22, %35 offset:%38\n"
+      "ds_read_b64_tr_b16 %23, %35 offset:%39\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]), "=&v"(k[7]),
+        "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+        "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]),
+        "=&v"(r[15])
+      : "v"(fa.k[0]), "v"(fa.k[1]), "v"(fa.k[2]), "v"(fa.k[3]), "v"(fa.k[4]), "v"(fa.k[5]), "v"(fa.k[6]),
+        "v"(fa.k[7]), "v"(fa.v[0]), "v"(fa.v[1]), "v"(fa.v[2]), "v"(fa.v[3]), "i"(kOff), "i"(kOff + kV8),
+        "i"(kOff + 2 * kV8), "i"(kOff + 3 * kV8)
+      : "memory");
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kf.x[s] = __builtin_bit_cast(h16x8, k[s]);
+  assemble_vt(vt, r);
+}
+#else
 template <int kOff>
 __device__ __forceinline__ void read_frags_at(Frag<true>& kf, VtFrag<true>& vt, const FragAddr& fa) {
   u32x4 k[4];
-  u32x2 r[8];  // [db][ks][lo, hi]: key rows 16ks + 8half at +2048ks + 1024half
+  u32x2 r[8];  // [db][ks][lo, hi]: key rows 16ks + 8half at +2 kV8 ks + kV8 half
   asm volatile(
       "ds_read_b128 %0, %12 offset:%18\n"
       "ds_read_b128 %1, %13 offset:%18\n"
@@ -327,18 +438,13 @@ __device__ __forceinline__ void read_frags_at(Frag<true>& kf, VtFrag<true>& vt, 
       : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]),
         "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
       : "v"(fa.k[0]), "v"(fa.k[1]), "v"(fa.k[2]), "v"(fa.k[3]), "v"(fa.v[0]), "v"(fa.v[1]), "i"(kOff),
-        "i"(kOff + 1024), "i"(kOff + 2048), "i"(kOff + 3072)
+        "i"(kOff + kV8), "i"(kOff + 2 * kV8), "i"(kOff + 3 * kV8)
       : "memory");
 #pragma unroll
   for (int s = 0; s < 4; ++s) kf.x[s] = __builtin_bit_cast(h16x8, k[s]);
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x2 lo = r[4 * db + 2 * ks], hi = r[4 * db + 2 * ks + 1];
-      vt.a[db][ks] = __builtin_bit_cast(h16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-    }
+  assemble_vt(vt, r);
 }
+#endif
 
 __device__ __forceinline__ void read_frags(Frag<true>& kf, VtFrag<true>& vt, const FragAddr& fa,
                                            const unsigned char*, int stage) {
@@ -360,8 +466,8 @@ __device__ __forceinline__ void read_frags(Frag<false>& kf, VtFrag<false>& vt, c
   const unsigned char* rp = stage + row * L::kRowBytes;
   const int sw = kswz<false>(row);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const f32x4 t = *reinterpret_cast<const f32x4*>(rp + (((8 * hh + j) ^ sw) << 4));
+  for (int j = 0; j < kD / 8; ++j) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(rp + ((((kD / 8) * hh + j) ^ sw) << 4));
     kf.x[4 * j + 0] = t[0];
     kf.x[4 * j + 1] = t[1];
     kf.x[4 * j + 2] = t[2];
@@ -369,9 +475,9 @@ __device__ __forceinline__ void read_frags(Frag<false>& kf, VtFrag<false>& vt, c
   }
   const float* vs = reinterpret_cast<const float*>(stage + L::kBlockBytes);
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
+  for (int db = 0; db < kND; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) vt.a[db][r] = vs[(acc_c(r) + 4 * hh) * kHeadDim + 32 * db + (lane & 31)];
+    for (int r = 0; r < 16; ++r) vt.a[db][r] = vs[(acc_c(r) + 4 * hh) * kD + 32 * db + (lane & 31)];
 }
 
 // Zero the V^T operand entries of keys whose bit is clear in keymask, so
@@ -389,7 +495,7 @@ __device__ __forceinline__ void zero_dead_keys(VtFrag<true>& vt, uint32_t keymas
       keep[d] = (((km >> k0) & 1u) ? 0x0000ffffu : 0u) | (((km >> (k0 + 1)) & 1u) ? 0xffff0000u : 0u);
     }
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < kND; ++db)
       vt.a[db][ks] = __builtin_bit_cast(h16x8, __builtin_bit_cast(u32x4, vt.a[db][ks]) & keep);
   }
 }
@@ -399,8 +505,8 @@ __device__ __forceinline__ void zero_dead_keys(VtFrag<false>& vt, uint32_t keyma
 #pragma unroll
   for (int r = 0; r < 16; ++r)
     if (!((km >> acc_c(r)) & 1u)) {
-      vt.a[0][r] = 0.f;
-      vt.a[1][r] = 0.f;
+#pragma unroll
+      for (int db = 0; db < kND; ++db) vt.a[db][r] = 0.f;
     }
 }
 
@@ -426,14 +532,14 @@ __device__ __forceinline__ uint32_t above_span(uint32_t u, uint32_t span) {
 __device__ __forceinline__ void zero_dead_krow(Frag<true>& kf, uint32_t keymask, int lane) {
   if (!((keymask >> (lane & 31)) & 1u)) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kf.x[s] = h16x8{};
+    for (int s = 0; s < kD / 16; ++s) kf.x[s] = h16x8{};
   }
 }
 
 __device__ __forceinline__ void zero_dead_krow(Frag<false>& kf, uint32_t keymask, int lane) {
   if (!((keymask >> (lane & 31)) & 1u)) {
 #pragma unroll
-    for (int j = 0; j < 32; ++j) kf.x[j] = 0.f;
+    for (int j = 0; j < kD / 2; ++j) kf.x[j] = 0.f;
   }
 }
 
@@ -451,7 +557,7 @@ struct PFrag<false> {
 
 // Running state of one wave: 32 query columns.
 struct HalfState {
-  f32x16 o[2];  // O^T of head dims 32db + ..., per dim half db
+  f32x16 o[kND];  // O^T of head dims 32db + ..., per 32-dim block db
   float m;      // reference max (log2 domain) of the lane's query
   float l;      // partial row sum of this lane (16 of the 32 keys per block)
   int cnt;      // partial count of scored keys of this lane
@@ -462,23 +568,23 @@ __device__ __forceinline__ void state_init(HalfState& st) {
   st.l = 0.f;
   st.cnt = 0;
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
+  for (int db = 0; db < kND; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.o[db][r] = 0.f;
 }
 
-// O^T (64 dims x 32 queries) += V^T P^T.
-__device__ __forceinline__ void pv(f32x16 (&o)[2], const PFrag<true>& pf, const VtFrag<true>& vt) {
+// O^T (kD dims x 32 queries) += V^T P^T.
+__device__ __forceinline__ void pv(f32x16 (&o)[kND], const PFrag<true>& pf, const VtFrag<true>& vt) {
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
+  for (int db = 0; db < kND; ++db)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
       o[db] = mfma16(vt.a[db][ks], pf.x[ks], o[db]);
 }
 
-__device__ __forceinline__ void pv(f32x16 (&o)[2], const PFrag<false>& pf, const VtFrag<false>& vt) {
+__device__ __forceinline__ void pv(f32x16 (&o)[kND], const PFrag<false>& pf, const VtFrag<false>& vt) {
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
+  for (int db = 0; db < kND; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vt.a[db][r], pf.x[r], o[db], 0, 0, 0);
 }
@@ -507,7 +613,7 @@ __device__ __forceinline__ void softmax_core(HalfState& st, f32x16& s, PFrag<B16
     st.m = mn;
     st.l *= alpha;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < kND; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
   }
@@ -705,10 +811,23 @@ __device__ __forceinline__ int scan_globals(const ScanPre& sp, const MaskRow& m,
   return __builtin_amdgcn_readfirstlane(total);  // the same in every lane
 }
 
-// Partial state of one wave parked in LDS for the merge: the head-dim half
-// of O^T that the partner wave emits, as [g][lane] f32x4, then per query
+// A lane's O^T accumulators hold kND * 16 values; value j = 16 db + 4 g + i
+// (o[db][4g + i]) is head dim 32 db + 8 g + 4 (lane / 32) + i.  The merge
+// splits them in two halves of kHalfO values: key parity kp's wave emits
+// j in [kHalfO kp, kHalfO (kp + 1)).
+constexpr int kHalfO = 8 * kND;
+
+__host__ __device__ constexpr int odim(int j, int hh) { return 32 * (j >> 4) + 8 * ((j >> 2) & 3) + 4 * hh + (j & 3); }
+// Half `part` of the values covers head dims [kD/2 part, kD/2 (part + 1)):
+// odim(kHalfO part + u, hh) = kD/2 part + odim(u, hh) for u < kHalfO.
+static_assert(odim(kHalfO, 0) == kD / 2 && odim(kHalfO + 4, 1) == kD / 2 + odim(4, 1), "halves are contiguous");
+
+__device__ __forceinline__ float oval(const HalfState& st, int j) { return st.o[j >> 4][j & 15]; }
+
+// Partial state of one wave parked in LDS for the merge: the half of O^T
+// that the partner wave emits, as [g][lane] f32x4, then per query
 // (lane % 32) the reference max, the row sum and the key count.
-constexpr int kParkOBytes = 4 * 64 * 16;
+constexpr int kParkOBytes = (kHalfO / 4) * 64 * 16;
 constexpr int kParkBytes = kParkOBytes + 3 * 32 * 4;
 
 template <bool B16>
@@ -724,13 +843,13 @@ struct Shared {
 
 // The two waves of query half qh (key parities 0 and 1) hold partial
 // results for the same 32 queries over disjoint key subsets; wave (qh, kp)
-// emits head-dim half db = kp.  Every wave parks the half its partner
+// emits half kp of the O^T values.  Every wave parks the half its partner
 // emits with its (m, l, count) (after a barrier: the rings it overwrites
 // are no longer read), and after a second barrier combines its own half
 // with the partner's parked one.  It passes, per lane, the merged max M
-// (log2 domain), row sum L, key count and the 16 unnormalised outputs of
-// head dims 32db + 8g + 4(lane/32) + i (in o[4g + i]) to
-// emit(db, M, L, cnt, o).  Both waves of a row form M, L and the outputs
+// (log2 domain), row sum L, key count and the kHalfO unnormalised outputs
+// (o[u] is value j = kHalfO kp + u, head dim odim(j, lane / 32)) to
+// emit(kp, M, L, cnt, o).  Both waves of a row form M, L and the outputs
 // with parity 0's terms first, so the row's two halves share one L.
 template <bool B16, class Emit>
 __device__ void merge_parities(const HalfState& st, Shared<B16>& sh, int qh, int kp, Emit emit) {
@@ -739,9 +858,12 @@ __device__ void merge_parities(const HalfState& st, Shared<B16>& sh, int qh, int
   __syncthreads();
   unsigned char* mine = sh.buf + (2 * kp + qh) * kParkBytes;
   f32x4* po = reinterpret_cast<f32x4*>(mine);
-  const f32x16& give = kp ? st.o[0] : st.o[1];
+  float give[kHalfO];  // the partner's half: values [kHalfO (1 - kp), ...)
 #pragma unroll
-  for (int g = 0; g < 4; ++g) po[g * 64 + lane] = f32x4{give[4 * g], give[4 * g + 1], give[4 * g + 2], give[4 * g + 3]};
+  for (int u = 0; u < kHalfO; ++u) give[u] = kp ? oval(st, u) : oval(st, kHalfO + u);
+#pragma unroll
+  for (int g = 0; g < kHalfO / 4; ++g)
+    po[g * 64 + lane] = f32x4{give[4 * g], give[4 * g + 1], give[4 * g + 2], give[4 * g + 3]};
   const float l = st.l + __shfl_xor(st.l, 32);
   const int cnt = st.cnt + __shfl_xor(st.cnt, 32);
   float* pm = reinterpret_cast<float*>(mine + kParkOBytes);
@@ -764,11 +886,13 @@ __device__ void merge_parities(const HalfState& st, Shared<B16>& sh, int qh, int
   const float fb = __builtin_amdgcn_exp2f(mb - M);
   const float Lsum = la * fa + lb * fb;
   const float f_own = kp ? fb : fa, f_p = kp ? fa : fb;
-  const f32x16& own = kp ? st.o[1] : st.o[0];
-  const f32x4* op = reinterpret_cast<const f32x4*>(pp);
-  float o[16];
+  float own[kHalfO];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
+  for (int u = 0; u < kHalfO; ++u) own[u] = kp ? oval(st, kHalfO + u) : oval(st, u);
+  const f32x4* op = reinterpret_cast<const f32x4*>(pp);
+  float o[kHalfO];
+#pragma unroll
+  for (int g = 0; g < kHalfO / 4; ++g) {
     const f32x4 y = op[g * 64 + lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -821,17 +945,19 @@ __device__ __forceinline__ int xcd_remap(int x, int N) {
   return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + y;
 }
 
-// Output values of one quadrant of a row: head dims 32db + 8g + 4hh + i
-// from o[4g + i], times inv (or zeros).
+// Output values of one quarter of a row (half `part` of the O^T values of
+// lane half hh): head dims odim(kHalfO part + u, hh) from o[u], times inv
+// (or zeros).
 template <bool B16>
-__device__ __forceinline__ void store_quadrant(elem_t<B16>* row, int db, int hh, const float* o, float inv,
+__device__ __forceinline__ void store_quadrant(elem_t<B16>* row, int part, int hh, const float* o, float inv,
                                                bool zero) {
+  elem_t<B16>* dst = row + (kD / 2) * part + 4 * hh;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
+  for (int g = 0; g < kHalfO / 4; ++g) {
     float t[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) t[i] = zero ? 0.f : o[4 * g + i] * inv;
-    store4<B16>(row + 32 * db + 8 * g + 4 * hh, t);
+    store4<B16>(dst + odim(4 * g, 0), t);
   }
 }
 
@@ -1019,9 +1145,11 @@ struct HalfLoop {
   int lane, kp, qh;
   bool solo;
   int lg;  // log2 of the block index step between this wave's blocks (1, or 2 solo)
-  // buffer resources and per-lane offsets of the evenly spaced (affine) path
+  // buffer resources and per-lane offsets of the evenly spaced (affine) path:
+  // load t of a block takes K offset vk[t % kND] (the K swizzle of its rows
+  // cycles with that period) and V offset vv
   __amdgpu_buffer_rsrc_t rk, rv;
-  uint32_t vk0, vk1, vv;
+  uint32_t vk[kND], vv;
   // key-validity bits of this wave's table blocks (entry k: block
   // kp + (k << lg)), filled in the prologue; null when the source has more
   // table blocks than the table holds
@@ -1040,15 +1168,23 @@ struct HalfLoop {
                       int qh_, bool solo_ = false)
       : src(s), kb(k), vb(v), rs(rs_), ring(ring_), lane(lane_id()), kp(kp_), qh(qh_), solo(solo_), lg(solo_ ? 2 : 1),
         ktab(nullptr), tab_cnt(0), full_keys(0), fast_lo(0), fast_hi(0), fast_steps(0) {
-    const uint32_t bytes = (uint32_t)(((size_t)(n - 1) * rs + kHeadDim) * sizeof(T));
+    const uint32_t bytes = (uint32_t)(((size_t)(n - 1) * rs + kD) * sizeof(T));
     rk = make_rsrc(k, bytes);
     rv = make_rsrc(v, bytes);
-    const uint32_t row_off = (uint32_t)src.dstep() * (uint32_t)(lane >> 3) * rs;
-    const int ck = (lane & 7) ^ (lane >> 4);  // kswz of rows 8t + lane/8, t even
-    const int cv = (lane & 7) ^ (((lane >> 4) & 1) << 2);
-    vk0 = 2u * (row_off + 8u * (uint32_t)ck);
-    vk1 = 2u * (row_off + 8u * (uint32_t)(ck ^ 4));
-    vv = 2u * (row_off + 8u * (uint32_t)cv);
+    // 16-bit rows: lane l of load t takes chunk c = l % kChunks of row
+    // kRowsPerLoad t + l / kChunks.  With R rows per bank span, the row's
+    // span index is 4 t + x, x = (l / kChunks) / R < 4, so its K swizzle is
+    // ((4 t) mod kChunks) ^ x: 4 (t % kND) ^ x; its V swizzle does not
+    // depend on t.
+    constexpr uint32_t C = L::kChunks, R = L::kRowsPerSpan;
+    const uint32_t ul = (uint32_t)lane;
+    const uint32_t row_off = (uint32_t)src.dstep() * (ul / C) * rs;
+    const uint32_t x = (ul / C) / R;
+    const uint32_t ck = (ul % C) ^ x;
+    const uint32_t cv = (ul % C) ^ ((x & (kND - 1)) << 2);
+#pragma unroll
+    for (int vi = 0; vi < kND; ++vi) vk[vi] = 2u * (row_off + 8u * (ck ^ (4u * vi)));
+    vv = 2u * (row_off + 8u * cv);
     if constexpr (B16) fa = frag_addr(ring, lane);
     src.fast_range(fast_lo, fast_hi);
     int base;
@@ -1072,8 +1208,10 @@ struct HalfLoop {
         if (u >= L::kHalfLoads && !solo) break;
         const int t = (solo ? 0 : qh * L::kHalfLoads) + u;
         const uint32_t sot = __builtin_amdgcn_readfirstlane(so + t * step);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)(dst + 1024 * t), 16, (t & 1) ? vk1 : vk0, sot,
-                                                 0, 0);
+        // t % kND = u % kND: the first load qh kHalfLoads of a wave's share is
+        // a multiple of kND (kHalfLoads = kND for 16-bit rows)
+        static_assert(!B16 || L::kHalfLoads % kND == 0, "K offset of load t is vk[u % kND]");
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)(dst + 1024 * t), 16, vk[u % kND], sot, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS_AS void*)(dst + L::kBlockBytes + 1024 * t), 16, vv, sot,
                                                  0, 0);
       }
@@ -1265,22 +1403,29 @@ struct HalfLoop {
 // wave of each query half scores them after the block loop with dot
 // products on the vector unit.  Their K and V rows are staged in LDS by one
 // direct-to-LDS load as soon as the global list is known (after the scan),
-// in the unused tail of the list: 1 KB per query half, the K rows then the
-// V rows, 128 B each.
+// in the unused tail of the list: kVecBytes per query half, the K rows then
+// the V rows, 2 kD bytes each.  Head dims up to 64 only (the rows of both
+// halves must fit in the list's tail); larger ones take the key blocks.
 // ---------------------------------------------------------------------------
 constexpr int kVecGlobals = 4;
+constexpr int kVecRowBytes = 2 * kD;
+constexpr int kVecBytes = 2 * kVecGlobals * kVecRowBytes;
+constexpr int kVecChunks = kVecRowBytes / 16;  // 16-byte chunks per row
+constexpr bool kVecOk = 16 * 4 + 2 * kVecBytes <= LF_MAX_GLOBAL * 4 && kVecBytes <= 64 * 16;
 
 __device__ __forceinline__ unsigned char* vec_rows(int* G, int qh) {
-  return reinterpret_cast<unsigned char*>(G + 16) + 1024 * qh;
+  return reinterpret_cast<unsigned char*>(G + 16) + kVecBytes * qh;
 }
 
-// Lane l fetches 16-byte chunk l % 8 of the K (l < 32) or V (l >= 32) row of
-// global token (l / 8) % 4 (clamped to the last one); it lands at byte 16 l.
+// Lane l < kVecBytes / 16 fetches 16-byte chunk l % kVecChunks of the K (l <
+// kVecBytes / 32) or V row of global token (l / kVecChunks) % 4 (clamped to
+// the last one); it lands at byte 16 l.
 __device__ __forceinline__ void issue_vec_rows(const h16* kb, const h16* vb, uint32_t rs, const int* G, int nG,
                                                unsigned char* dst) {
   const int l = lane_id_here();
-  const int key = min((l >> 3) & 3, nG - 1);
-  const h16* src = ((l >> 5) ? vb : kb) + (size_t)G[key] * rs + 8 * (l & 7);
+  if (l >= kVecBytes / 16) return;
+  const int key = min((l / kVecChunks) & 3, nG - 1);
+  const h16* src = ((l >= kVecBytes / 32) ? vb : kb) + (size_t)G[key] * rs + 8 * (l % kVecChunks);
   __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)dst, 16, 0, 0);
 }
 
@@ -1298,12 +1443,12 @@ __device__ void vec_global_columns(HalfState& st, const Frag<true>& qf, const Ba
   const uint32_t span = 2u * (uint32_t)src.wd;
   for (int gi = 0; gi < src.nG; ++gi) {
     const int g = src.G[gi];
-    const unsigned char* kr = rows + 128 * gi;
-    const unsigned char* vr = rows + 512 + 128 * gi;
-    // q . k over this lane's 32 head dims (16 s + 8 hh + [0, 8))
+    const unsigned char* kr = rows + kVecRowBytes * gi;
+    const unsigned char* vr = rows + kVecBytes / 2 + kVecRowBytes * gi;
+    // q . k over this lane's kD / 2 head dims (16 s + 8 hh + [0, 8))
     float acc = 0.f;
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
+    for (int s4 = 0; s4 < kD / 16; ++s4) {
       const h16x8 kk = *reinterpret_cast<const h16x8*>(kr + 32 * s4 + 16 * hh);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -1321,7 +1466,7 @@ __device__ void vec_global_columns(HalfState& st, const Frag<true>& qf, const Ba
       st.m = mn;
       st.l *= alpha;
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+      for (int db = 0; db < kND; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
     }
@@ -1330,9 +1475,9 @@ __device__ void vec_global_columns(HalfState& st, const Frag<true>& qf, const Ba
       st.l += pr;
       st.cnt += take ? 1 : 0;
     }
-    // O^T element r of dim half db: head dim 32 db + 8 (r / 4) + 4 hh + r % 4
+    // O^T element r of dim block db: head dim 32 db + 8 (r / 4) + 4 hh + r % 4
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < kND; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const h16x4 vv = *reinterpret_cast<const h16x4*>(vr + 2 * (32 * db + 8 * g4 + 4 * hh));
@@ -1399,8 +1544,8 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
   const bool causal = p.causal != 0;
   const int w_hi = causal ? 0 : w;
   const int8_t* mrow = p.mask + (size_t)b * n;
-  const uint32_t rs = (uint32_t)p.H * kHeadDim;  // elements between tokens
-  const size_t head = (size_t)b * n * rs + (size_t)h * kHeadDim;
+  const uint32_t rs = (uint32_t)p.H * kD;  // elements between tokens
+  const size_t head = (size_t)b * n * rs + (size_t)h * kD;
   const T* qbase = reinterpret_cast<const T*>(p.q) + head;
   T* out = reinterpret_cast<T*>(p.out) + head;
 
@@ -1496,8 +1641,8 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
       nG = p.max_global;
     }
     src.nG = __builtin_amdgcn_readfirstlane(nG);  // uniform (the status write above diverges)
-    vec_g = B16 && src.nG > 0 && src.nG <= kVecGlobals;
-    if constexpr (B16) {
+    vec_g = B16 && kVecOk && src.nG > 0 && src.nG <= kVecGlobals;
+    if constexpr (B16 && kVecOk) {
       if (vec_g && kp == 0 && active)
         issue_vec_rows(reinterpret_cast<const h16*>(p.k) + head, reinterpret_cast<const h16*>(p.v) + head, rs,
                        sh.G, src.nG, vrows);
@@ -1529,7 +1674,7 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
     loop.run(st, qf, end, p.c, active);
   }
   __builtin_amdgcn_s_setprio(2);
-  if constexpr (B16) {
+  if constexpr (B16 && kVecOk) {
     if (vec_g && kp == 0 && active) vec_global_columns(st, qf, src, vrows, p.c);
   }
   merge_parities<B16>(st, sh, qh, kp, [&](int db, float M, float Lsum, int cnt, const float* o) {
@@ -1543,19 +1688,20 @@ __device__ void band_tile(const KernelParams& p, int L, Shared<B16>& sh) {
 }
 
 // Partial record of one (global token, split): merged max, row sum, key
-// count, then the unnormalised outputs; this lane writes head dims
-// 32 db + 8 g + 4 hh + e from o[4 g + e].
-__device__ __forceinline__ void write_record(float* rec, int db, int hh, float M, float Lsum, int cnt,
+// count, then the unnormalised outputs in head-dim order; this lane writes
+// head dims odim(kHalfO part + u, hh) from o[u].
+__device__ __forceinline__ void write_record(float* rec, int part, int hh, float M, float Lsum, int cnt,
                                              const float* o) {
-  if (db == 0 && hh == 0) {
+  if (part == 0 && hh == 0) {
     st_agent(rec, M);
     st_agent(rec + 1, Lsum);
     st_agent(rec + 2, __builtin_bit_cast(float, cnt));
   }
+  float* dst = rec + 4 + (kD / 2) * part + 4 * hh;
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+  for (int g = 0; g < kHalfO / 4; ++g)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) st_agent(rec + 4 + 32 * db + 8 * g + 4 * hh + e, o[4 * g + e]);
+    for (int e = 0; e < 4; ++e) st_agent(dst + odim(4 * g, 0) + e, o[4 * g + e]);
 }
 
 // Second merge round of a solo split (below): waves (0, kp) and (1, kp)
@@ -1575,7 +1721,8 @@ __device__ void merge_halves(Shared<B16>& sh, int qh, int kp, float M, float L, 
   float* pm = reinterpret_cast<float*>(r2 + kParkOBytes);
   if (qh == 1) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) po[g * 64 + lane] = f32x4{o[4 * g], o[4 * g + 1], o[4 * g + 2], o[4 * g + 3]};
+    for (int g = 0; g < kHalfO / 4; ++g)
+      po[g * 64 + lane] = f32x4{o[4 * g], o[4 * g + 1], o[4 * g + 2], o[4 * g + 3]};
     if ((lane >> 5) == 0) {
       pm[lane] = M;
       pm[32 + lane] = L;
@@ -1590,9 +1737,9 @@ __device__ void merge_halves(Shared<B16>& sh, int qh, int kp, float M, float L, 
   const float fa = __builtin_amdgcn_exp2f(M - Mm);
   const float fb = __builtin_amdgcn_exp2f(mb - Mm);
   const float Lm = L * fa + lb * fb;
-  float om[16];
+  float om[kHalfO];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
+  for (int g = 0; g < kHalfO / 4; ++g) {
     const f32x4 y = po[g * 64 + lane];
 #pragma unroll
     for (int e = 0; e < 4; ++e) om[4 * g + e] = __builtin_fmaf(o[4 * g + e], fa, y[e] * fb);
@@ -1625,8 +1772,8 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
   const int n = p.n;
   const int8_t* mrow = p.mask + (size_t)b * n;
 
-  const uint32_t rs = (uint32_t)p.H * kHeadDim;
-  const size_t head = (size_t)b * n * rs + (size_t)h * kHeadDim;
+  const uint32_t rs = (uint32_t)p.H * kD;
+  const size_t head = (size_t)b * n * rs + (size_t)h * kD;
   const T* qg = reinterpret_cast<const T*>(p.qg) + head;
   ChunkSrc src;
   src.mrow = mrow;
@@ -1671,14 +1818,14 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
     __builtin_amdgcn_s_setprio(0);
     loop.run_solo(st, qf, nblk, c, true);
     __builtin_amdgcn_s_setprio(2);
-    float M1 = 0.f, L1 = 0.f, o1[16];
+    float M1 = 0.f, L1 = 0.f, o1[kHalfO];
     int c1 = 0;
     merge_parities<B16>(st, sh, qh, kp, [&](int, float M, float Lsum, int cnt, const float* o) {
       M1 = M;
       L1 = Lsum;
       c1 = cnt;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o1[r] = o[r];
+      for (int r = 0; r < kHalfO; ++r) o1[r] = o[r];
     });
     merge_halves<B16>(sh, qh, kp, M1, L1, c1, o1, [&](float M, float Lsum, int cnt, const float* o) {
       if (gi < nG) write_record(part_bh + ((size_t)gi * S + cidx) * kPartialStride, kp, hh, M, Lsum, cnt, o);
@@ -1722,14 +1869,15 @@ __device__ void global_split(const KernelParams& p, int gid, Shared<B16>& sh) {
   __syncthreads();
   if (!sh.flag) return;
 
-  // Merge: a group of 16 lanes per global token, each lane four head dims;
-  // every split's record of the token is loaded before any is used (the
-  // agent-scope loads go to the coherence point, so the merge is bound by
-  // how many of them are in flight).
+  // Merge: a group of kD / 4 lanes per global token, each lane four head
+  // dims; every split's record of the token is loaded before any is used
+  // (the agent-scope loads go to the coherence point, so the merge is bound
+  // by how many of them are in flight).
   T* out = reinterpret_cast<T*>(p.out) + head;
-  const int tid = 64 * wv + lane_id_here();
-  const int q4 = tid & 15;
-  for (int gj = tid >> 4; gj < nG; gj += kThreads / 16) {
+  const uint32_t tid = 64u * (uint32_t)wv + (uint32_t)lane_id_here();
+  constexpr uint32_t kLanesPerTok = kD / 4;
+  const int q4 = (int)(tid % kLanesPerTok);
+  for (int gj = (int)(tid / kLanesPerTok); gj < nG; gj += kThreads / kLanesPerTok) {
     // online log-sum-exp merge of the S partials, 8 at a time
     const float* recs = part_bh + (size_t)gj * S * kPartialStride;
     float M = kNegInf, Lsum = 0.f;
@@ -1789,15 +1937,24 @@ __device__ __forceinline__ void fwd_body(const KernelParams& p) {
   band_tile<B16>(p, xcd_remap(bid - p.n_glob, p.n_band), sh);
 }
 
+// Waves per SIMD: four workgroups (16 waves) per CU at head dims up to 64
+// (at most 128 VGPRs, under 40 KB of LDS at D = 64); two at D = 128, whose
+// rings take 64 KB of LDS and whose fragments and accumulators twice the
+// registers.
+#if LF_KD == 128
+#define LF_WAVES_PER_EU 2
+#else
+#define LF_WAVES_PER_EU 4
+#endif
+
 #if LF_HALF_F16
 // f16: the 16-bit kernel built for f16 elements.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void lf_attn_fwd_f16(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LF_WAVES_PER_EU))) void lf_attn_fwd_f16(
     const KernelParams p) {
   fwd_body<true>(p);
 }
 #else
-// bf16: four workgroups (16 waves) per CU: at most 128 VGPRs, under 40 KB of LDS.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void lf_attn_fwd_bf16(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LF_WAVES_PER_EU))) void lf_attn_fwd_bf16(
     const KernelParams p) {
   fwd_body<true>(p);
 }
@@ -1826,27 +1983,24 @@ static int64_t resident_of(const void* kernel, std::atomic<int64_t>* cache) {
 }
 
 #if LF_HALF_F16
-int64_t resident_workgroups_f16() {
+int64_t resident_f16() {
   static std::atomic<int64_t> cache[32];
   return resident_of(reinterpret_cast<const void*>(lf_attn_fwd_f16), cache);
 }
 
-int launch_forward_f16(const KernelParams& kp, void* stream) {
+int launch_f16(const KernelParams& kp, void* stream) {
   hipLaunchKernelGGL(lf_attn_fwd_f16, dim3(kp.n_band + kp.n_glob), dim3(kThreads), 0,
                      reinterpret_cast<hipStream_t>(stream), kp);
   return (int)hipGetLastError();
 }
 #else
-
-int64_t resident_workgroups(int dtype) {
+int64_t resident(int dtype) {
   static std::atomic<int64_t> cache_bf16[32], cache_f32[32];
-  if (dtype == LF_F16) return resident_workgroups_f16();
   return dtype == LF_BF16 ? resident_of(reinterpret_cast<const void*>(lf_attn_fwd_bf16), cache_bf16)
                           : resident_of(reinterpret_cast<const void*>(lf_attn_fwd_f32), cache_f32);
 }
 
-int launch_forward(const KernelParams& kp, int dtype, void* stream) {
-  if (dtype == LF_F16) return launch_forward_f16(kp, stream);
+int launch(const KernelParams& kp, int dtype, void* stream) {
   const int grid = kp.n_band + kp.n_glob;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == LF_BF16)
@@ -1854,6 +2008,30 @@ int launch_forward(const KernelParams& kp, int dtype, void* stream) {
   else
     hipLaunchKernelGGL(lf_attn_fwd_f32, dim3(grid), dim3(kThreads), 0, s, kp);
   return (int)hipGetLastError();
+}
+#endif
+
+}  // namespace LF_CAT(d, LF_KD)
+
+#if !LF_HALF_F16 && LF_KD == 64
+// The forward of head dim D and element type dtype (the units of each head
+// dim are declared in lf_attn_internal.h).
+int launch_forward(const KernelParams& kp, int dtype, int D, void* stream) {
+  switch (D) {
+    case 32: return dtype == LF_F16 ? d32::launch_f16(kp, stream) : d32::launch(kp, dtype, stream);
+    case 64: return dtype == LF_F16 ? d64::launch_f16(kp, stream) : d64::launch(kp, dtype, stream);
+    case 128: return dtype == LF_F16 ? d128::launch_f16(kp, stream) : d128::launch(kp, dtype, stream);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+int64_t resident_workgroups(int dtype, int D) {
+  switch (D) {
+    case 32: return dtype == LF_F16 ? d32::resident_f16() : d32::resident(dtype);
+    case 64: return dtype == LF_F16 ? d64::resident_f16() : d64::resident(dtype);
+    case 128: return dtype == LF_F16 ? d128::resident_f16() : d128::resident(dtype);
+    default: return 0;
+  }
 }
 #endif
 

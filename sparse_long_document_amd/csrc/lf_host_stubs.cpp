@@ -11,10 +11,10 @@
 
 namespace lf {
 
-int launch_forward(const KernelParams&, int, void*) { return (int)hipErrorNoDevice; }
+int launch_forward(const KernelParams&, int, int, void*) { return (int)hipErrorNoDevice; }
 int launch_backward(const BwdParams&, void*) { return (int)hipErrorNoDevice; }
 int launch_project(const ProjParams&, void*) { return (int)hipErrorNoDevice; }
-int64_t resident_workgroups(int) { return 0; }
+int64_t resident_workgroups(int, int) { return 0; }
 
 }  // namespace lf
 

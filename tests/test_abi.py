@@ -79,6 +79,23 @@ def test_workspace_bytes_layout():
     assert lf.library().lf_attn_workspace_bytes(ctypes.byref(p)) == 512
 
 
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_workspace_bytes_per_head_dim(D):
+    # a partial record holds (m, l, count, pad) and the D outputs
+    p, _k = _params(B=1, n=1000, H=3, D=D, max_global=5)
+    rec = 1 * 3 * 5 * 2 * (4 + D) * 4
+    assert lf.library().lf_attn_workspace_bytes(ctypes.byref(p)) == 256 + 256 + (rec + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("D", [32, 128])
+def test_backward_takes_head_dim_64_only(D):
+    # the forward takes these head dims; the gradient kernels do not
+    p, _k = _params(D=D)
+    assert lf.library().lf_attn_workspace_bytes(ctypes.byref(p)) > 0
+    assert lf.library().lf_attn_backward_workspace_bytes(ctypes.byref(p)) == 0
+    assert _backward(p) == lf.LF_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), lf.LF_ERR_INVALID_ARG),
     (dict(n=0), lf.LF_ERR_INVALID_ARG),
@@ -89,8 +106,11 @@ def test_workspace_bytes_layout():
     (dict(scale=float("inf")), lf.LF_ERR_INVALID_ARG),
     (dict(scale=-0.5), lf.LF_ERR_INVALID_ARG),
     (dict(max_global=-1), lf.LF_ERR_INVALID_ARG),
-    (dict(D=32), lf.LF_ERR_UNSUPPORTED),
-    (dict(D=128), lf.LF_ERR_UNSUPPORTED),
+    (dict(D=16), lf.LF_ERR_UNSUPPORTED),
+    (dict(D=48), lf.LF_ERR_UNSUPPORTED),
+    (dict(D=96), lf.LF_ERR_UNSUPPORTED),
+    (dict(D=256), lf.LF_ERR_UNSUPPORTED),
+    (dict(D=1), lf.LF_ERR_UNSUPPORTED),
     (dict(dtype=torch.float64), lf.LF_ERR_UNSUPPORTED),
     (dict(H=65, dilation=None), lf.LF_ERR_UNSUPPORTED),
     (dict(max_global=2000), lf.LF_ERR_UNSUPPORTED),

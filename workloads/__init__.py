@@ -334,9 +334,28 @@ def longformer_base_len(n: int) -> Problem:
     return Problem(f"longformer_base_len{n}", *t, mask, 256, None, False, None)
 
 
+HEAD_DIMS = (32, 64, 128)
+
+
+def longformer_base_n4096_dim(D: int) -> Problem:
+    """The longformer-base layer shape (B1 n4096 H12, w=256 per side, bf16,
+    token 0 global) with head dim D in place of 64: the head-dim variants.
+    Seed 2000 + D."""
+    if D == D_HEAD:
+        return longformer_base_n4096()
+    rng = np.random.Generator(np.random.PCG64(2000 + D))
+    shape = (1, 4096, 12, D)
+    t = [_draw(rng, shape, torch.bfloat16) for _ in range(6)]
+    mask = torch.ones((1, 4096), dtype=torch.int8)
+    mask[0, 0] = 2
+    return Problem(f"longformer_base_n4096_d{D}", *t, mask, 256, None, False, None)
+
+
 def by_name(name: str) -> Problem:
     if name.startswith("longformer_base_len"):
         return longformer_base_len(int(name[len("longformer_base_len"):]))
+    if name.startswith("longformer_base_n4096_d"):
+        return longformer_base_n4096_dim(int(name[len("longformer_base_n4096_d"):]))
     return {
         "single_head_fp32_n512": single_head_fp32_n512,
         "longformer_base_n4096": longformer_base_n4096,
