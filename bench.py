@@ -22,6 +22,9 @@ parity field).  Only that leg touches the oracle.
 With --sweep it times the longformer-base layer shape at n = 1024 ... 16384
 (linear growth in n) and prints one line per length.
 
+--workload longformer_base_n4096_d128 (or _d32) times the same layer shape
+with head dim 128 (32) in place of 64.
+
 With --pass projections a step is one lf_attn_project: the six input
 projections (Q_s, K_s, V_s, Q_g, K_g, V_g) of the workload's B*n tokens
 from C = H*64 hidden features.
