@@ -135,7 +135,8 @@ lf_status lf_attn_forward_lse(const lf_attn_params* p,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace lf_attn_backward needs (status word, the global
- * token list of each batch row, one fp32 per row for <dout, out>).  Returns
+ * token list of each batch row, two fp32 per row: <dout, out> and the row's
+ * lse in base 2).  Returns
  * 0 if the parameters are invalid. */
 size_t lf_attn_backward_workspace_bytes(const lf_attn_params* p);
 

@@ -12,25 +12,26 @@
 // D_i = <dout_i, out_i>, de_j = p_j (dp_j - D_i); dq_i = s sum_j de_j k_j,
 // dk_j += s de_j q_i, dv_j += p_j dout_i.
 //
-// Work is split so that every gradient row has one owner and no atomics,
-// except where a few rows collect from the whole sequence:
-//   role Q  (local rows):   one wave per 32 query rows of one residue class
-//                           of one head; walks the rows' window key blocks
-//                           and the global key blocks; writes dq.
-//   role KV (local keys):   one wave per 32 keys of one residue class; walks
-//                           the query blocks whose windows hold those keys;
-//                           writes dk, dv of non-global keys.
-//   role GK (global keys):  one wave per 32 global tokens and 512 rows;
-//                           adds every local row's dk, dv to the global
-//                           tokens' rows (atomic fp32 adds; the rows were
-//                           zeroed by the preparation kernel).
-//   role GQ (global rows):  one wave per 32 global rows and 512 keys; adds
-//                           to dq_g (atomic fp32 adds onto zeroed rows).
-//   role GKV (their keys):  one wave per 32 tokens; walks the global rows;
-//                           writes dk_g, dv_g.
-// Each block step is three or four 32x32x16 MFMA chains: scores and dP from
-// row-major fragments loaded straight from HBM, then the gradient product,
-// whose transposed operand is read column-wise from rows staged in LDS.
+// Three launches:
+//   * preparation: the global token list of each batch row, D_i per row,
+//     and zeroed rows for the gradients that the global-token work adds to;
+//   * band kernel: 4-wave workgroups over tiles of 128 consecutive rows of
+//     one residue class of one head (a dilated window is a plain window over
+//     its residue class: segmentfault summary, "Dilated sliding window").
+//     A dq workgroup owns 128 query rows (wave w: 32 of them) and streams the
+//     key blocks of its window span and then the batch row's global tokens
+//     through LDS; a dk/dv workgroup owns 128 key rows and streams the query
+//     blocks whose windows reach them, with their lse and D.  Each staged
+//     block is read by all four waves; every gradient row has one owner, and
+//     S and dP are formed once per (block, wave) in each of the two roles;
+//   * global-token kernel (only with global work): single-wave units that
+//     add the local rows' dk, dv of global tokens and the global rows' dq_g
+//     (fp32 atomics onto zeroed rows), and write dk_g, dv_g:
+//       GKV: one wave per 32 tokens; walks the global rows; writes dk_g, dv_g.
+//       GQ:  one wave per 32 global rows and 512 keys; adds to dq_g.
+//       GK:  one wave per 32 global tokens and 512 rows; adds to dk, dv.
+// Block products are 32x32x16 MFMA chains; the transposed operands come from
+// staged rows through ds_read_b64_tr_b16.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -50,10 +51,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLdsRow = 72;           // staged row: 64 head dims + 16 B of padding
-constexpr int kSentinel = -(1 << 29); // residue index of a key outside the row's class
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kXcds = 8;              // MI355X: accelerator complex dies, one L2 each
-constexpr int kXcdGroup = 32;         // consecutive units kept on one XCD
 
 __device__ __forceinline__ f32x16 mma(e16x8 a, e16x8 b, f32x16 c) {
 #if LF_HALF_F16
@@ -100,6 +98,12 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// The global-token units below run one per wave: the rows a wave stages in
+// LDS are read back only by lanes of the same wave, whose LDS operations
+// complete in order; the wave waits for its own LDS operations and the
+// compiler moves no memory access across this point.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Row fragment: lane (c, hl) holds head dims 16 s + 8 hl .. + 7 of row c, the
 // operand layout of the 32x32x16 MFMA with the row as M (A) or N (B).
 __device__ __forceinline__ void load_frag(e16x8 (&f)[4], const e16* row, bool ok, int hl) {
@@ -140,11 +144,6 @@ __device__ __forceinline__ e16x8 col_frag(const BwdShared& sh, int which, int t,
   return __builtin_bit_cast(e16x8, v);
 }
 
-__device__ __forceinline__ bool in_win(int qt, int kt, int w, int causal) {
-  const int d = qt - kt;
-  return causal ? (d >= 0 && d <= w) : (d >= -w && d <= w);
-}
-
 // Query-owning wave: 32 query rows (lane c's row at qpos, residue index qt,
 // type qty), nblk key blocks described by keyof(j, slot) -> (pos, t, slot code),
 // membership member(qty, qt, kty, kt).  Returns dq^T in acc: lane (c, hl)
@@ -177,7 +176,7 @@ __device__ void q_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16*
     keep_frag(vf, kty != 0);
     if (hl == 0) sh.info[c] = make_int4(kpos, kt, kty, 0);
     stage_frag(sh, 0, c, hl, kf);
-    __syncthreads();
+    wave_lds_sync();
     // the next block's rows fly during this block's products: their loads
     // depend on positions only, not on the mask bytes loaded beside them
     int npos = -1, nt = 0, ncode = 0;
@@ -211,7 +210,7 @@ __device__ void q_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16*
     for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int t = 0; t < 2; ++t) acc[half] = mma(col_frag(sh, 0, t, lane, half), ds8[t], acc[half]);
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       kf[s] = nkf[s];
@@ -247,8 +246,8 @@ __device__ void kv_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16
     code = 0;
     if (j < nblk) rowof(j, c, pos, tt, code);
     // loads depend on the position only; the mask type applies at use
-    l2 = pos >= 0 ? lse_bh[pos] : 0.f;
-    dd = pos >= 0 ? d_bh[pos] : 0.f;
+    l2 = pos >= 0 ? -p.c * lse_bh[pos] : 0.f;  // lse in base 2
+    dd = pos >= 0 ? -d_bh[pos] : 0.f;
     load_frag(a, qb + (size_t)(pos >= 0 ? pos : 0) * rs, pos >= 0, hl);
     load_frag(b, dob + (size_t)(pos >= 0 ? pos : 0) * rs, pos >= 0, hl);
   };
@@ -259,11 +258,11 @@ __device__ void kv_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16
     keep_frag(df, qty != 0);
     if (hl == 0) {
       sh.info[c] = make_int4(qpos, qt, qty, 0);
-      sh.stat[c] = qty ? make_float2(ql * kLog2e, qd) : make_float2(0.f, 0.f);
+      sh.stat[c] = qty ? make_float2(ql, qd) : make_float2(0.f, 0.f);
     }
     stage_frag(sh, 0, c, hl, qf);
     stage_frag(sh, 1, c, hl, df);
-    __syncthreads();
+    wave_lds_sync();
     int npos, nt, ncode;
     float nl, nd;
     e16x8 nqf[4], ndf[4];
@@ -302,7 +301,7 @@ __device__ void kv_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16
         acc_v[half] = mma(p8[t], col_frag(sh, 1, t, lane, half), acc_v[half]);
         acc_k[half] = mma(ds8[t], col_frag(sh, 0, t, lane, half), acc_k[half]);
       }
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       qf[s] = nqf[s];
@@ -316,49 +315,16 @@ __device__ void kv_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16
   }
 }
 
-// Residue tile of a batch row's role-Q / role-KV work: head, residue class,
-// first residue index and class length.
-struct ResTile {
-  int h, r, t0, len, d;
-};
-
-__device__ __forceinline__ ResTile decode_res(const BwdParams& p, int idx) {
-  ResTile t;
-  int h = 0;
-  while (h + 1 < p.H && p.tile0[h + 1] <= idx) ++h;
-  const int d = p.dil[h];
-  const int local = idx - p.tile0[h];
-  t.h = h;
-  t.d = d;
-  t.r = local / p.rtiles[h];
-  t.t0 = (local % p.rtiles[h]) * 32;
-  t.len = t.r < p.n ? (p.n - t.r + d - 1) / d : 0;
-  return t;
-}
-
 __device__ __forceinline__ void store_f4(float* dst, const float* v) {
   *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
 }
 
-__device__ void bwd_body(const BwdParams& p) {
-  __shared__ BwdShared sh;
+// Work on the global tokens: unit `bid` of the single-wave units (GKV,
+// then GQ and GK), run by one wave with its own staging area sh.
+__device__ void bwd_global_unit(const BwdParams& p, BwdShared& sh, int bid) {
   const int lane = threadIdx.x & 63, c = lane & 31, hl = lane >> 5;
   const int n = p.n;
   const size_t rs = (size_t)p.H * 64;
-  // Workgroups go to the 8 XCDs round-robin (id % 8).  Remap so that groups
-  // of kXcdGroup consecutive units run on one XCD, the groups dealt to the
-  // XCDs in turn: neighbouring tiles share most of their window rows, which
-  // then stay in that XCD's L2 instead of being fetched from HBM by every
-  // XCD, and every XCD still gets an even share of each role.  A bijection
-  // on [0, 8 * kXcdGroup * full); the remainder keeps its index.
-  int bid = blockIdx.x;
-  {
-    const int span = kXcds * kXcdGroup;
-    if (bid < (int)(gridDim.x / span) * span) {
-      const int x = bid % kXcds, s = bid / kXcds;
-      bid = ((s / kXcdGroup) * kXcds + x) * kXcdGroup + s % kXcdGroup;
-    }
-  }
   const e16* Q = reinterpret_cast<const e16*>(p.q);
   const e16* K = reinterpret_cast<const e16*>(p.k);
   const e16* V = reinterpret_cast<const e16*>(p.v);
@@ -366,114 +332,6 @@ __device__ void bwd_body(const BwdParams& p) {
   const e16* KG = reinterpret_cast<const e16*>(p.kg);
   const e16* VG = reinterpret_cast<const e16*>(p.vg);
   const e16* DO = reinterpret_cast<const e16*>(p.dout);
-  const int w = p.w, causal = p.causal, ug = p.use_globals;
-
-  if (bid < 2 * p.n_res) {
-    const bool own_q = bid < p.n_res;
-    if (!own_q) bid -= p.n_res;
-    const int b = bid / p.tiles_per_b;
-    const ResTile rt = decode_res(p, bid - b * p.tiles_per_b);
-    if (rt.t0 >= rt.len) return;  // a class shorter than the longest owns no rows here
-    const size_t boff = (size_t)b * n * rs + (size_t)rt.h * 64;
-    const int8_t* mb = p.mask + (size_t)b * n;
-    const float* lse_bh = p.lse + ((size_t)b * p.H + rt.h) * n;
-    const float* d_bh = p.Dsum + ((size_t)b * p.H + rt.h) * n;
-    const int nG = ug ? p.gcount[b] : 0;
-    const int32_t* gl = p.glist + (size_t)b * p.gstride;
-    // this lane's own slot: query (role Q) or key (role KV) t0 + c of the class
-    const int myt = rt.t0 + c;
-    const int mypos = myt < rt.len ? rt.r + rt.d * myt : -1;
-    const int myty = mypos >= 0 ? eff_mask(mb[mypos], ug) : 0;
-    auto res_slot = [&](int t, int& pos, int& tt, int& code) {
-      const bool in = t >= 0 && t < rt.len;
-      const int sp = in ? rt.r + rt.d * t : 0;
-      code = (uint8_t)mb[sp];
-      pos = in ? sp : -1;
-      tt = t;
-    };
-    if (own_q) {
-      // window keys of the tile's rows, clipped to the class
-      const int base = max(rt.t0 - w, 0);
-      const int last = min(rt.t0 + 31 + (causal ? 0 : w), rt.len - 1);
-      const int nwin = (last - base + 32) / 32;
-      const int ngb = (nG + 31) / 32;
-      auto keyof = [&](int j, int slot, int& pos, int& tt, int& code) {
-        if (j < nwin) {
-          res_slot(base + 32 * j + slot, pos, tt, code);
-        } else {
-          const int g = 32 * (j - nwin) + slot;
-          pos = g < nG ? gl[g] : -1;
-          const int rel = pos - rt.r;
-          tt = (pos >= rt.r && rel % rt.d == 0) ? rel / rt.d : kSentinel;
-          // type 6 marks a global-column slot (window slots carry the mask
-          // byte's type, 1 or 2)
-          code = 256 + 6;
-        }
-      };
-      // window slots: any valid key in W(i); global-column slots (type 6):
-      // global keys not already in W(i)
-      auto member = [&](int qty, int qt, int kty, int kt) {
-        if (qty != 1 || kty == 0) return false;
-        return kty == 6 ? !in_win(qt, kt, w, causal) : in_win(qt, kt, w, causal);
-      };
-      const float lse2 = myty ? lse_bh[mypos] * kLog2e : 0.f;
-      const float dd = myty ? d_bh[mypos] : 0.f;
-      f32x16 acc[2];
-      // a window block is full when its 32 keys lie in every window of the
-      // tile's 32 rows: first key >= t0 + 31 - w, last key <= t0 (+ w)
-      auto geom = [&](int j) {
-        const int k0 = base + 32 * j;
-        return j < nwin && k0 >= rt.t0 + 31 - w && k0 + 31 <= rt.t0 + (causal ? 0 : w);
-      };
-      q_owner(p, sh, rs, Q + boff, DO + boff, K + boff, V + boff, mypos, myt, myty, lse2, dd, nwin + ngb, keyof,
-              member, geom, 1, -1, acc);
-      if (mypos >= 0) {
-        float* dst = p.dq + boff + (size_t)mypos * rs;
-        const float sc = myty == 1 ? p.scale : 0.f;
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float v4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v4[e] = sc * acc[half][4 * g + e];
-            store_f4(dst + 32 * half + 8 * g + 4 * hl, v4);
-          }
-      }
-    } else {
-      // rows whose windows hold the tile's keys, clipped to the class
-      const int base = causal ? rt.t0 : max(rt.t0 - w, 0);
-      const int last = min(rt.t0 + 31 + w, rt.len - 1);
-      const int nq = (last - base + 32) / 32;
-      auto rowof = [&](int j, int slot, int& pos, int& tt, int& code) { res_slot(base + 32 * j + slot, pos, tt, code); };
-      auto member = [&](int qty, int qt, int kty, int kt) { return qty == 1 && kty == 1 && in_win(qt, kt, w, causal); };
-      if (hl == 0) sh.opos[c] = (myty == 2) ? -1 : mypos;
-      f32x16 ak[2], av[2];
-      // a query block is full when its 32 rows' windows all hold the tile's
-      // 32 keys: first row >= t0 + 31 - (causal ? 0 : w), last row <= t0 + w
-      auto geom = [&](int j) {
-        const int r0 = base + 32 * j;
-        return r0 >= rt.t0 + 31 - (causal ? 0 : w) && r0 + 31 <= rt.t0 + w;
-      };
-      kv_owner(p, sh, rs, K + boff, V + boff, Q + boff, DO + boff, lse_bh, d_bh, mypos, myt, myty, nq, rowof,
-               member, geom, 1, 1, ak, av);
-      __syncthreads();
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int pos = sh.opos[acc_row(r, hl)];
-        if (pos < 0) continue;
-        float* dk = p.dk + boff + (size_t)pos * rs;
-        float* dv = p.dv + boff + (size_t)pos * rs;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          dk[32 * half + c] = p.scale * ak[half][r];
-          dv[32 * half + c] = av[half][r];
-        }
-      }
-    }
-    return;
-  }
-  bid -= 2 * p.n_res;
 
   // global roles: GKV (key blocks of every (b, h)), then GQ and GK
   if (bid < p.n_gkv) {
@@ -496,9 +354,9 @@ __device__ void bwd_body(const BwdParams& p) {
     auto member = [](int qty, int, int kty, int) { return qty == 2 && kty != 0; };
     if (hl == 0) sh.opos[c] = mypos;
     f32x16 ak[2], av[2];
-    kv_owner(p, sh, rs, KG + boff, VG + boff, QG + boff, DO + boff, p.lse + (size_t)bh * n, p.Dsum + (size_t)bh * n,
+    kv_owner(p, sh, rs, KG + boff, VG + boff, QG + boff, DO + boff, p.lneg + (size_t)bh * n, p.dneg + (size_t)bh * n,
              mypos, 0, myty, (nG + 31) / 32, rowof, member, [](int) { return true; }, 2, -1, ak, av);
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int pos = sh.opos[acc_row(r, hl)];
@@ -540,12 +398,12 @@ __device__ void bwd_body(const BwdParams& p) {
     tt = 0;
     code = (uint8_t)mb[t < n ? t : 0];
   };
-  const float* lse_bh = p.lse + (size_t)bh * n;
-  const float* d_bh = p.Dsum + (size_t)bh * n;
+  const float* lse_bh = p.lneg + (size_t)bh * n;  // -lse / scale
+  const float* d_bh = p.dneg + (size_t)bh * n;     // -D
   if (gq) {
     auto member = [](int qty, int, int kty, int) { return qty == 2 && kty != 0; };
-    const float lse2 = gty ? lse_bh[gpos] * kLog2e : 0.f;
-    const float dd = gty ? d_bh[gpos] : 0.f;
+    const float lse2 = gty ? -p.c * lse_bh[gpos] : 0.f;
+    const float dd = gty ? -d_bh[gpos] : 0.f;
     f32x16 acc[2];
     q_owner(p, sh, rs, QG + boff, DO + boff, KG + boff, VG + boff, gpos, 0, gty, lse2, dd, nblk, tok, member,
             [](int) { return true; }, 2, -1, acc);
@@ -563,7 +421,7 @@ __device__ void bwd_body(const BwdParams& p) {
     f32x16 ak[2], av[2];
     kv_owner(p, sh, rs, K + boff, V + boff, Q + boff, DO + boff, lse_bh, d_bh, gpos, 0, gty, nblk, tok, member,
              [](int) { return true; }, 1, 2, ak, av);
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int pos = sh.opos[acc_row(r, hl)];
@@ -577,6 +435,694 @@ __device__ void bwd_body(const BwdParams& p) {
       }
     }
   }
+}
+
+
+// ===========================================================================
+// Band kernel
+// ===========================================================================
+#define LDS_AS __attribute__((address_space(3)))
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kRowB = 128;                   // staged row: 64 head dims of 16 bits
+constexpr int kBlkB = 32 * kRowB;            // one 32-row block of one tensor
+constexpr int kStatB = 256;                  // dk/dv role: -lse / scale then -D of the block's 32 rows
+constexpr int kStageB = 2 * kBlkB + kStatB;  // two tensors and the row statistics
+constexpr int kBandStages = 3;               // blocks i + 1 and i + 2 fly while block i is used
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(LDS_AS const void*)p; }
+
+constexpr int kBandTab = 64;                 // blocks whose row validity is tabulated up front
+
+struct BandShared {
+  __attribute__((aligned(16))) unsigned char ring[kBandStages * kStageB];
+  uint32_t tab[kBandTab];     // row-validity bits of blocks i0 .. i0 + kBandTab - 1 (entry i % kBandTab)
+  int32_t gpos[LF_MAX_GLOBAL];  // dq role: the batch row's global positions
+};
+
+// A 32-bit LDS word read in an asm block that waits for its own read (see
+// the fragment reads below).
+__device__ __forceinline__ uint32_t lds_word(const void* p) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+
+// The validity table for blocks i0 .. i0 + kBandTab - 1 (below nblk): bit
+// row of tab[i % kBandTab] is ok(i, row, mask byte of the row).  Each wave
+// takes blocks i0 + 2 wv + 8 k and the next (lanes 0-31 and 32-63).  The
+// loads are waited for here, and a workgroup barrier ends it.
+template <class Pos, class Ok>
+__device__ __forceinline__ void tab_fill(BandShared& sh, const int8_t* mb, int i0, int nblk, int wv, int lane,
+                                         Pos pos, Ok ok) {
+  const int end = min(nblk, i0 + kBandTab);
+  for (int a = i0 + 2 * wv; a < end; a += 8) {
+    const int i = a + (lane >> 5), row = lane & 31;
+    const bool v = i < end && ok(i, row, (int)mb[pos(i < end ? i : a, row)]);
+    const unsigned long long bits = __ballot(v);
+    if (lane == 0) {
+      sh.tab[a % kBandTab] = (uint32_t)bits;
+      if (a + 1 < end) sh.tab[(a + 1) % kBandTab] = (uint32_t)(bits >> 32);
+    }
+  }
+  __syncthreads();
+}
+
+// 16-byte chunk c of staged row r sits at chunk c ^ bswz(r).  With 128-byte
+// rows two rows share a 256-byte bank span; the swizzle is a bit reversal of
+// (r / 2) mod 8.  Row reads (16 consecutive rows at one chunk) then hit 16
+// distinct 16-byte slots, and the transposed reads of a half-wave (rows
+// 4a .. 4a + 3, one 64-byte column group) 4 distinct 64-byte quarters.
+__device__ __forceinline__ int bswz(int r) {
+  const int x = (r >> 1) & 7;
+  return ((x & 1) << 2) | (x & 2) | (x >> 2);
+}
+
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// at most N vector-memory instructions of this wave outstanding (they
+// complete in issue order)
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 16, "small counts");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+
+// This wave's share (load t = wave of each tensor: rows 8 t .. 8 t + 7) of
+// the direct-to-LDS loads of one 32-row block of two tensors x0, x1 into a
+// stage: lane l fetches chunk (l % 8) ^ bswz(row) of row 8 t + l / 8 (token
+// position pos(row), always a valid row), landing at byte 1024 t + 16 l.
+template <class Pos>
+__device__ __forceinline__ void issue_pair(const e16* x0, const e16* x1, size_t rs, Pos pos, unsigned char* stage,
+                                           int wv, int lane) {
+  const int row = 8 * wv + (lane >> 3);
+  const size_t off = (size_t)pos(row) * rs + 8 * ((lane & 7) ^ bswz(row));
+  __builtin_amdgcn_global_load_lds(x0 + off, (LDS_AS void*)(stage + 1024 * wv), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(x1 + off, (LDS_AS void*)(stage + kBlkB + 1024 * wv), 16, 0, 0);
+}
+
+// Per-lane LDS addresses of the fragment reads of a block at the ring's
+// start (a stage is kStageB further; the second tensor kBlkB).
+//   ro[s]: row operand, lane (row = lane % 32, hl = lane / 32) reads head
+//          dims 16 s + 8 hl .. + 7 of its row;
+//   co[db][half]: transposed operand, ds_read_b64_tr_b16: in each group g of
+//          16 lanes, lane 4 e + q addresses row 4 (g / 2) + e + 8 half,
+//          head dims 32 db + 16 (g % 2) + 4 q .. + 3; lane i of the group
+//          receives head dim 32 db + 16 (g % 2) + i of those four rows.  The
+//          rows 16 further (k-step 1) share the swizzle: + 2048 bytes.
+//   Together lane l gets head dim 32 db + l % 32 of rows 16 ks + {4 hl ..
+//   4 hl + 3, 8 + 4 hl .. 8 + 4 hl + 3}, the row order of a 32x32 result's
+//   registers 8 ks .. 8 ks + 7.
+struct BandAddr {
+  uint32_t ro[4];
+  uint32_t co[2][2];
+};
+
+__device__ __forceinline__ BandAddr band_addr(const unsigned char* ring, int lane) {
+  BandAddr a;
+  const uint32_t base = lds_addr(ring);
+  const int row = lane & 31, hl = lane >> 5;
+  const int sw = bswz(row);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) a.ro[s] = base + (uint32_t)(row * kRowB + (((2 * s + hl) ^ sw) << 4));
+  const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int r = 8 * half + 4 * (g >> 1) + (i >> 2);
+      const int byte = 64 * db + 32 * (g & 1) + 8 * (i & 3);
+      a.co[db][half] = base + (uint32_t)(r * kRowB + ((((byte >> 4) ^ bswz(r)) << 4) | (byte & 15)));
+    }
+  return a;
+}
+
+__device__ __forceinline__ e16x8 as8(u32x4 x) { return __builtin_bit_cast(e16x8, x); }
+__device__ __forceinline__ e16x8 join8(u32x2 lo, u32x2 hi) {
+  return __builtin_bit_cast(e16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// The reads of one staged block (kOff: the stage's byte offset), in asm
+// blocks that wait for their own reads: the compiler cannot tell them from
+// the direct-to-LDS loads still in flight into the other stages and would
+// otherwise wait for those first.
+//   dq role:  rows of tensor 0 (K) and 1 (V), transposed tensor 0 (K^T).
+template <int kOff>
+__device__ __forceinline__ void read_dq(e16x8 (&kf)[4], e16x8 (&vf)[4], e16x8 (&kt)[2][2], const BandAddr& a) {
+  u32x4 k[4], v[4];
+  u32x2 t[8];  // [db][ks][half]
+  asm volatile(
+      "ds_read_b128 %0, %16 offset:%24\n"
+      "ds_read_b128 %1, %17 offset:%24\n"
+      "ds_read_b128 %2, %18 offset:%24\n"
+      "ds_read_b128 %3, %19 offset:%24\n"
+      "ds_read_b128 %4, %16 offset:%25\n"
+      "ds_read_b128 %5, %17 offset:%25\n"
+      "ds_read_b128 %6, %18 offset:%25\n"
+      "ds_read_b128 %7, %19 offset:%25\n"
+      "ds_read_b64_tr_b16 %8, %20 offset:%24\n"
+      "ds_read_b64_tr_b16 %9, %21 offset:%24\n"
+      "ds_read_b64_tr_b16 %10, %20 offset:%26\n"
+      "ds_read_b64_tr_b16 %11, %21 offset:%26\n"
+      "ds_read_b64_tr_b16 %12, %22 offset:%24\n"
+      "ds_read_b64_tr_b16 %13, %23 offset:%24\n"
+      "ds_read_b64_tr_b16 %14, %22 offset:%26\n"
+      "ds_read_b64_tr_b16 %15, %23 offset:%26\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]),
+        "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
+      : "v"(a.ro[0]), "v"(a.ro[1]), "v"(a.ro[2]), "v"(a.ro[3]), "v"(a.co[0][0]), "v"(a.co[0][1]), "v"(a.co[1][0]),
+        "v"(a.co[1][1]), "i"(kOff), "i"(kOff + kBlkB), "i"(kOff + 2048)
+      : "memory");
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    kf[s] = as8(k[s]);
+    vf[s] = as8(v[s]);
+  }
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) kt[db][ks] = join8(t[4 * db + 2 * ks], t[4 * db + 2 * ks + 1]);
+}
+
+//   dk/dv role, in two asm blocks (fewer registers live at once): rows of
+//   tensor 0 (Q) and 1 (dO) with the row statistics (this lane's 16 rows
+//   8 g + 4 hl .. + 3: float4 g of -lse / scale, then of -D, at sa), then
+//   transposed tensor 0 (Q^T) and 1 (dO^T).
+template <int kOff>
+__device__ __forceinline__ void read_dkv_rows(e16x8 (&qf)[4], e16x8 (&df)[4], f32x4 (&ls)[4], f32x4 (&dd)[4],
+                                              const BandAddr& a, uint32_t sa) {
+  u32x4 q[4], d[4];
+  asm volatile(
+      "ds_read_b128 %0, %16 offset:%21\n"
+      "ds_read_b128 %1, %17 offset:%21\n"
+      "ds_read_b128 %2, %18 offset:%21\n"
+      "ds_read_b128 %3, %19 offset:%21\n"
+      "ds_read_b128 %4, %16 offset:%22\n"
+      "ds_read_b128 %5, %17 offset:%22\n"
+      "ds_read_b128 %6, %18 offset:%22\n"
+      "ds_read_b128 %7, %19 offset:%22\n"
+      "ds_read_b128 %8, %20 offset:%23\n"
+      "ds_read_b128 %9, %20 offset:%24\n"
+      "ds_read_b128 %10, %20 offset:%25\n"
+      "ds_read_b128 %11, %20 offset:%26\n"
+      "ds_read_b128 %12, %20 offset:%27\n"
+      "ds_read_b128 %13, %20 offset:%28\n"
+      "ds_read_b128 %14, %20 offset:%29\n"
+      "ds_read_b128 %15, %20 offset:%30\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]),
+        "=&v"(ls[0]), "=&v"(ls[1]), "=&v"(ls[2]), "=&v"(ls[3]), "=&v"(dd[0]), "=&v"(dd[1]), "=&v"(dd[2]),
+        "=&v"(dd[3])
+      : "v"(a.ro[0]), "v"(a.ro[1]), "v"(a.ro[2]), "v"(a.ro[3]), "v"(sa), "i"(kOff), "i"(kOff + kBlkB), "i"(kOff),
+        "i"(kOff + 32), "i"(kOff + 64), "i"(kOff + 96), "i"(kOff + 128), "i"(kOff + 160), "i"(kOff + 192),
+        "i"(kOff + 224)
+      : "memory");
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    qf[s] = as8(q[s]);
+    df[s] = as8(d[s]);
+  }
+}
+
+template <int kOff>
+__device__ __forceinline__ void read_dkv_cols(e16x8 (&qt)[2][2], e16x8 (&dt)[2][2], const BandAddr& a) {
+  u32x2 t[16];  // [tensor][db][ks][half]
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:%20\n"
+      "ds_read_b64_tr_b16 %1, %17 offset:%20\n"
+      "ds_read_b64_tr_b16 %2, %16 offset:%22\n"
+      "ds_read_b64_tr_b16 %3, %17 offset:%22\n"
+      "ds_read_b64_tr_b16 %4, %18 offset:%20\n"
+      "ds_read_b64_tr_b16 %5, %19 offset:%20\n"
+      "ds_read_b64_tr_b16 %6, %18 offset:%22\n"
+      "ds_read_b64_tr_b16 %7, %19 offset:%22\n"
+      "ds_read_b64_tr_b16 %8, %16 offset:%21\n"
+      "ds_read_b64_tr_b16 %9, %17 offset:%21\n"
+      "ds_read_b64_tr_b16 %10, %16 offset:%23\n"
+      "ds_read_b64_tr_b16 %11, %17 offset:%23\n"
+      "ds_read_b64_tr_b16 %12, %18 offset:%21\n"
+      "ds_read_b64_tr_b16 %13, %19 offset:%21\n"
+      "ds_read_b64_tr_b16 %14, %18 offset:%23\n"
+      "ds_read_b64_tr_b16 %15, %19 offset:%23\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7]),
+        "=&v"(t[8]), "=&v"(t[9]), "=&v"(t[10]), "=&v"(t[11]), "=&v"(t[12]), "=&v"(t[13]), "=&v"(t[14]),
+        "=&v"(t[15])
+      : "v"(a.co[0][0]), "v"(a.co[0][1]), "v"(a.co[1][0]), "v"(a.co[1][1]), "i"(kOff), "i"(kOff + kBlkB),
+        "i"(kOff + 2048), "i"(kOff + kBlkB + 2048)
+      : "memory");
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      qt[db][ks] = join8(t[4 * db + 2 * ks], t[4 * db + 2 * ks + 1]);
+      dt[db][ks] = join8(t[8 + 4 * db + 2 * ks], t[8 + 4 * db + 2 * ks + 1]);
+    }
+}
+
+// Zero the entries of a transposed operand whose row is clear in vm (a row
+// outside every pair of the block may hold non-finite values; its products
+// must be exact zeros).
+__device__ __forceinline__ void zero_cols(e16x8 (&t)[2][2], uint32_t vm, int hl) {
+  const uint32_t m = vm >> (4 * hl);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    u32x4 keep;
+#pragma unroll
+    for (int dw = 0; dw < 4; ++dw) {
+      // elements 2 dw, 2 dw + 1; element e is row 16 ks + 8 (e / 4) + e % 4 (+ 4 hl)
+      const int r0 = 16 * ks + 8 * ((2 * dw) >> 2) + ((2 * dw) & 3);
+      keep[dw] = (((m >> r0) & 1u) ? 0x0000ffffu : 0u) | (((m >> (r0 + 1)) & 1u) ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db) t[db][ks] = __builtin_bit_cast(e16x8, __builtin_bit_cast(u32x4, t[db][ks]) & keep);
+  }
+}
+
+// Bits lo .. hi of a word (empty when lo > hi); lo, hi clipped to [0, 31].
+__device__ __forceinline__ uint32_t bit_range(int lo, int hi) {
+  lo = max(lo, 0);
+  hi = min(hi, 31);
+  return lo > hi ? 0u : ((0xffffffffu >> (31 - hi)) & (0xffffffffu << lo));
+}
+
+// Band tile: batch row b, head h (dilation d), residue class r (len rows),
+// rows t0 .. t0 + 127 of the class.
+struct BandTile {
+  int b, h, d, r, t0, len;
+};
+
+__device__ __forceinline__ BandTile decode_band(const BwdParams& p, int tile) {
+  BandTile t;
+  t.b = tile / p.bt_per_b;
+  const int id0 = tile - t.b * p.bt_per_b;
+  int h = 0;
+  while (h + 1 < p.H && p.btile0[h + 1] <= id0) ++h;
+  const int d = p.dil[h];
+  const int id = id0 - p.btile0[h];
+  const int qn = p.n / d, rm = p.n % d;
+  const int T1 = (qn + kBwdBandRows) / kBwdBandRows, T0 = (qn + kBwdBandRows - 1) / kBwdBandRows;
+  if (id < rm * T1) {
+    t.r = id / T1;
+    t.t0 = (id - t.r * T1) * kBwdBandRows;
+    t.len = qn + 1;
+  } else {
+    const int id2 = id - rm * T1;
+    t.r = rm + id2 / T0;
+    t.t0 = (id2 - (t.r - rm) * T0) * kBwdBandRows;
+    t.len = qn;
+  }
+  t.h = h;
+  t.d = d;
+  return t;
+}
+
+// The block loop shared by both roles: blocks i < nblk, block i staged in
+// stage i % 3.  Every wave runs every step (one barrier each) and issues,
+// after the barrier, the direct-to-LDS loads of block i + 2 (issue(i,
+// stage): exactly kLoads vector-memory instructions).  At the start of step
+// i only block i's loads must have landed: block i + 1's, issued after
+// them, may still fly.  prologue() makes the role's own loads; refill(i0)
+// fills the validity table for blocks i0 .. i0 + kBandTab - 1 (every wave,
+// at a barrier).  step(i, stage) uses block i.
+template <int kLoads, class Issue, class Prologue, class Refill, class Step>
+__device__ __forceinline__ void band_loop(int nblk, int pre, Issue issue, Prologue prologue, Refill refill,
+                                          Step step) {
+  // the first two blocks' loads (those that need no table: pre of them)
+  // fly while the prologue's own loads and the table's mask bytes load
+  const int early = min(min(pre, nblk), 2);
+  for (int i = 0; i < early; ++i) issue(i, i);
+  prologue();
+  refill(0);
+  for (int i = early; i < min(nblk, 2); ++i) issue(i, i);
+  wait_vmem_all();  // so that no wait for the prologue's loads lands inside the loop
+  int stage = 0;
+  for (int i = 0; i < nblk; ++i) {
+    if (i + 1 < nblk)
+      wait_vmem_but<kLoads>();
+    else
+      wait_vmem_all();
+    block_barrier();
+    // every wave is past step i - 1: the table may take the next blocks
+    if (i > 0 && i % kBandTab == 0) refill(i);
+    if (i + 2 < nblk) issue(i + 2, stage == 0 ? 2 : stage - 1);
+    step(i, stage);
+    stage = stage == 2 ? 0 : stage + 1;
+  }
+  wait_vmem_all();
+}
+
+// dq workgroup.  Wave wv owns query rows t0 + 32 wv + lane % 32 (Q and dO
+// as B operands, its base-2 lse and D in registers); the key blocks are the
+// window span kbase + 32 (jlo + i) + row (residue indices), then the global
+// tokens G[32 (i - nwin) + row] (scored by local rows whose window does not
+// hold them).  Per block: S^T = K Q^T, dP^T = V dO^T (lane: one query, 16
+// keys), dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
+__device__ void band_dq(const BwdParams& p, BandShared& sh, const BandTile& bt, int wv) {
+  const int lane = threadIdx.x & 63, c = lane & 31, hl = lane >> 5;
+  const int n = p.n, w = p.w, d = bt.d;
+  const int w_hi = p.causal ? 0 : w;
+  const int ug = p.use_globals;
+  const size_t rs = (size_t)p.H * 64;
+  const size_t boff = (size_t)bt.b * n * rs + (size_t)bt.h * 64;
+  const e16* Q = reinterpret_cast<const e16*>(p.q) + boff;
+  const e16* K = reinterpret_cast<const e16*>(p.k) + boff;
+  const e16* V = reinterpret_cast<const e16*>(p.v) + boff;
+  const e16* DO = reinterpret_cast<const e16*>(p.dout) + boff;
+  const int8_t* mb = p.mask + (size_t)bt.b * n;
+  const size_t bh = (size_t)bt.b * p.H + bt.h;
+
+  const int tq = bt.t0 + 32 * wv + c;
+  const bool qin = tq < bt.len;
+  const int qpos = bt.r + d * (qin ? tq : bt.len - 1);
+  const int qty = qin ? eff_mask(mb[qpos], ug) : 0;
+  const bool qloc = qty == 1;
+  // every wave takes every block; a tile with no local row only writes zeros
+  if (!__syncthreads_or(qloc)) {
+    if (qin) {
+      const float z[4] = {0.f, 0.f, 0.f, 0.f};
+      float* dst = p.dq + boff + (size_t)qpos * rs;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) store_f4(dst + 8 * q + 4 * hl, z);
+    }
+    return;
+  }
+  const float lse2 = qloc ? -p.c * p.lneg[bh * n + qpos] : 0.f;  // lse in base 2
+  const float dd = qloc ? -p.dneg[bh * n + qpos] : 0.f;
+  e16x8 qf[4], df[4];
+
+  const int kbase = bt.t0 - w;
+  const int S = (kBwdBandRows - 1 + w + w_hi) / 32 + 1;
+  const int jlo = kbase >= 0 ? 0 : (-kbase) / 32;
+  const int jhi = min(S, (bt.len - kbase + 31) / 32);
+  const int nwin = max(jhi - jlo, 0);
+  const int nG = ug ? p.gcount[bt.b] : 0;
+  const int32_t* gl = p.glist + (size_t)bt.b * p.gstride;
+  const int nblk = nwin + (nG + 31) / 32;
+  // token position of key row `row` of block i (a valid row in every case)
+  // the global list in LDS (read in asm: no vector-memory instruction in
+  // the block loop but its direct-to-LDS loads)
+  for (int g = threadIdx.x; g < nG; g += 256) sh.gpos[g] = gl[g];
+  auto kpos = [&](int i, int row) -> int {
+    if (i < nwin) {
+      const int kk = kbase + 32 * (jlo + i) + row;
+      return bt.r + d * (kk < 0 ? 0 : (kk >= bt.len ? bt.len - 1 : kk));
+    }
+    const int gi = 32 * (i - nwin) + row;
+    return (int)lds_word(&sh.gpos[gi < nG ? gi : nG - 1]);
+  };
+  const BandAddr ad = band_addr(sh.ring, lane);
+  const int q0w = bt.t0 + 32 * wv;  // the wave's first query row
+  // window key rows that exist and are valid (mask 1 or 2)
+  auto key_ok = [&](int i, int row, int m) {
+    const int kk = kbase + 32 * (jlo + i) + row;
+    return kk >= 0 && kk < bt.len && eff_mask((int8_t)m, ug) != 0;
+  };
+  auto refill = [&](int i0) {
+    if (i0 < nwin) tab_fill(sh, mb, i0, nwin, wv, lane, kpos, key_ok);
+    else __syncthreads();  // the global list is in LDS
+  };
+  f32x16 acc[2] = {zero16(), zero16()};
+  auto issue = [&](int i, int stg) {
+    issue_pair(K, V, rs, [&](int row) { return kpos(i, row); }, sh.ring + stg * kStageB, wv, lane);
+  };
+  auto step = [&](int i, int stage) {
+    uint32_t kval;
+    int k0 = 0;
+    if (i < nwin) {
+      k0 = kbase + 32 * (jlo + i);
+      // no key of the block in the window of any of the wave's queries
+      if (k0 > q0w + 31 + w_hi || k0 + 31 < q0w - w) return;
+      kval = __builtin_amdgcn_readfirstlane(lds_word(&sh.tab[i % kBandTab]));
+    } else {
+      kval = (uint32_t)__ballot(32 * (i - nwin) + c < nG);
+    }
+    if (kval == 0u) return;
+    e16x8 kf[4], vf[4], kt[2][2];
+    if (stage == 0)
+      read_dq<0>(kf, vf, kt, ad);
+    else if (stage == 1)
+      read_dq<kStageB>(kf, vf, kt, ad);
+    else
+      read_dq<2 * kStageB>(kf, vf, kt, ad);
+    f32x16 sc = zero16(), dp = zero16();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      sc = mma(kf[s], qf[s], sc);
+      dp = mma(vf[s], df[s], dp);
+    }
+    bool fast = false;
+    uint32_t okb = 0;  // bit k: (this lane's query, key row k) is a scored pair
+    if (i < nwin) {
+      fast = kval == 0xffffffffu && k0 >= q0w + 31 - w && k0 + 31 <= q0w + w_hi && __all(qloc);
+      if (!fast) okb = qloc ? (kval & bit_range(tq - w - k0, tq + w_hi - k0)) : 0u;
+    } else if (__any(qloc)) {
+      // global keys score where they are not already in the window:
+      // in W(i) when |i - g| <= w d and d divides i - g
+      const int gp = kpos(i, c);
+      const int wd = w * d;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = acc_row(r, hl);
+        const int g = __shfl(gp, kr);
+        const int dg = qpos - g;
+        const bool in_w = dg >= -wd && dg <= wd && dg % d == 0;
+        okb |= (!in_w ? 1u : 0u) << kr;
+      }
+      okb = qloc ? (okb & kval) : 0u;
+    }
+    e16x8 ds8[2];
+    if (fast) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(p.c, sc[r], -lse2));
+        ds8[r >> 3][r & 7] = (e16)(pr * (dp[r] - dd));
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool ok = (okb >> acc_row(r, hl)) & 1u;
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(p.c, sc[r], -lse2));
+        ds8[r >> 3][r & 7] = (e16)(ok ? pr * (dp[r] - dd) : 0.f);
+      }
+      if (kval != 0xffffffffu) zero_cols(kt, kval, hl);
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) acc[db] = mma(kt[db][ks], ds8[ks], acc[db]);
+  };
+  auto prologue = [&]() {
+    load_frag(qf, Q + (size_t)qpos * rs, true, hl);
+    load_frag(df, DO + (size_t)qpos * rs, true, hl);
+  };
+  band_loop<2>(nblk, nwin, issue, prologue, refill, step);
+  if (qin) {
+    float* dst = p.dq + boff + (size_t)qpos * rs;
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = qloc ? sc * acc[db][4 * g + e] : 0.f;
+        store_f4(dst + 32 * db + 8 * g + 4 * hl, v4);
+      }
+  }
+}
+
+// dk/dv workgroup.  Wave wv owns key rows t0 + 32 wv + lane % 32 (K and V
+// as B operands); the query blocks are the rows qbase + 32 (jlo + j) + row
+// whose windows reach the tile's keys, staged with their -lse / scale and
+// -D.  Per block: S = Q K^T, dP = dO V^T (lane: one key, 16 queries), P and
+// dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.  Keys with mask 2 are
+// left to the global-token work (which adds every local row's terms to
+// them); keys with mask 0 get zeros.
+__device__ void band_dkv(const BwdParams& p, BandShared& sh, const BandTile& bt, int wv) {
+  const int lane = threadIdx.x & 63, c = lane & 31, hl = lane >> 5;
+  const int n = p.n, w = p.w, d = bt.d;
+  const int w_hi = p.causal ? 0 : w;
+  const int ug = p.use_globals;
+  const size_t rs = (size_t)p.H * 64;
+  const size_t boff = (size_t)bt.b * n * rs + (size_t)bt.h * 64;
+  const e16* Q = reinterpret_cast<const e16*>(p.q) + boff;
+  const e16* K = reinterpret_cast<const e16*>(p.k) + boff;
+  const e16* V = reinterpret_cast<const e16*>(p.v) + boff;
+  const e16* DO = reinterpret_cast<const e16*>(p.dout) + boff;
+  const int8_t* mb = p.mask + (size_t)bt.b * n;
+  const size_t bh = (size_t)bt.b * p.H + bt.h;
+  const float* lse_bh = p.lneg + bh * n;  // -lse / scale
+  const float* d_bh = p.dneg + bh * n;     // -D
+
+  const int tk = bt.t0 + 32 * wv + c;
+  const bool kin = tk < bt.len;
+  const int kp = bt.r + d * (kin ? tk : bt.len - 1);
+  const int kty = kin ? eff_mask(mb[kp], ug) : 0;
+  const bool kok = kty == 1;
+  f32x16 ak[2] = {zero16(), zero16()}, av[2] = {zero16(), zero16()};
+  auto write_out = [&]() {
+    if (!kin || kty == 2) return;
+    float* dk = p.dk + boff + (size_t)kp * rs;
+    float* dv = p.dv + boff + (size_t)kp * rs;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float k4[4], v4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          k4[e] = kok ? p.scale * ak[db][4 * g + e] : 0.f;
+          v4[e] = kok ? av[db][4 * g + e] : 0.f;
+        }
+        store_f4(dk + 32 * db + 8 * g + 4 * hl, k4);
+        store_f4(dv + 32 * db + 8 * g + 4 * hl, v4);
+      }
+  };
+  if (!__syncthreads_or(kok)) {
+    write_out();
+    return;
+  }
+  e16x8 kf[4], vf[4];
+
+  // rows whose windows reach the tile's keys: tq in [tk - w_hi, tk + w]
+  const int qbase = bt.t0 - w_hi;
+  const int S = (kBwdBandRows - 1 + w + w_hi) / 32 + 1;
+  const int jlo = qbase >= 0 ? 0 : (-qbase) / 32;
+  const int jhi = min(S, (bt.len - qbase + 31) / 32);
+  const int nq = max(jhi - jlo, 0);
+  auto qrow0 = [&](int j) -> int { return qbase + 32 * (jlo + j); };
+  auto qpos = [&](int j, int row) -> int {
+    const int t = qrow0(j) + row;
+    return bt.r + d * (t < 0 ? 0 : (t >= bt.len ? bt.len - 1 : t));
+  };
+  const BandAddr ad = band_addr(sh.ring, lane);
+  const uint32_t sa = lds_addr(sh.ring + 2 * kBlkB) + 16u * (uint32_t)hl;
+  const int k0w = bt.t0 + 32 * wv;  // the wave's first key row
+  const bool all_keys = __all(kok);
+  // query rows that exist and are local (mask 1)
+  auto row_ok = [&](int j, int row, int m) {
+    const int t = qrow0(j) + row;
+    return t >= 0 && t < bt.len && eff_mask((int8_t)m, ug) == 1;
+  };
+  auto refill = [&](int j0) { tab_fill(sh, mb, j0, nq, wv, lane, qpos, row_ok); };
+  // stage: Q rows, dO rows, then the 32 rows' lse (lanes 0-31) and D
+  // (lanes 32-63); every wave loads the statistics (the same bytes), so that
+  // every wave issues the same number of loads
+  auto issue = [&](int j, int stg) {
+    unsigned char* stage = sh.ring + stg * kStageB;
+    issue_pair(Q, DO, rs, [&](int row) { return qpos(j, row); }, stage, wv, lane);
+    const float* src = ((lane >> 5) ? d_bh : lse_bh) + qpos(j, c);
+    __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(stage + 2 * kBlkB), 4, 0, 0);
+  };
+  auto step = [&](int j, int stage) {
+    const int t0q = qrow0(j);
+    // no row of the block has a key of the wave in its window
+    if (t0q > k0w + 31 + w || t0q + 31 < k0w - w_hi) return;
+    const uint32_t qval = __builtin_amdgcn_readfirstlane(lds_word(&sh.tab[j % kBandTab]));
+    if (qval == 0u) return;
+    e16x8 qrf[4], drf[4], qt[2][2], dt[2][2];
+    f32x4 ls[4], ds4[4];
+    if (stage == 0)
+      read_dkv_rows<0>(qrf, drf, ls, ds4, ad, sa);
+    else if (stage == 1)
+      read_dkv_rows<kStageB>(qrf, drf, ls, ds4, ad, sa);
+    else
+      read_dkv_rows<2 * kStageB>(qrf, drf, ls, ds4, ad, sa);
+    // S + (-lse / scale) and dP + (-D): the row statistics enter as the
+    // accumulators' starting values (element r of a lane is row 8 (r / 4) +
+    // 4 hl + r % 4, float4 r / 4 of the staged values)
+    f32x16 sc, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sc[r] = ls[r >> 2][r & 3];
+      dp[r] = ds4[r >> 2][r & 3];
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      sc = mma(qrf[s], kf[s], sc);
+      dp = mma(drf[s], vf[s], dp);
+    }
+    // the transposed reads run while the products above are in the MFMA unit
+    if (stage == 0)
+      read_dkv_cols<0>(qt, dt, ad);
+    else if (stage == 1)
+      read_dkv_cols<kStageB>(qt, dt, ad);
+    else
+      read_dkv_cols<2 * kStageB>(qt, dt, ad);
+    // (query row q, this lane's key) in the window: tk - w_hi <= t0q + q <= tk + w
+    const bool fast = all_keys && qval == 0xffffffffu && t0q + 31 - k0w <= w && k0w + 31 - t0q <= w_hi;
+    e16x8 p8[2], ds8[2];
+    if (fast) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(p.c * sc[r]);
+        p8[r >> 3][r & 7] = (e16)pr;
+        ds8[r >> 3][r & 7] = (e16)(pr * dp[r]);
+      }
+    } else {
+      const uint32_t okb = kok ? (qval & bit_range(tk - w_hi - t0q, tk + w - t0q)) : 0u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool ok = (okb >> acc_row(r, hl)) & 1u;
+        const float pr = __builtin_amdgcn_exp2f(p.c * sc[r]);
+        p8[r >> 3][r & 7] = (e16)(ok ? pr : 0.f);
+        ds8[r >> 3][r & 7] = (e16)(ok ? pr * dp[r] : 0.f);
+      }
+      if (qval != 0xffffffffu) {
+        zero_cols(qt, qval, hl);
+        zero_cols(dt, qval, hl);
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        av[db] = mma(dt[db][ks], p8[ks], av[db]);
+        ak[db] = mma(qt[db][ks], ds8[ks], ak[db]);
+      }
+  };
+  auto prologue = [&]() {
+    load_frag(kf, K + (size_t)kp * rs, true, hl);
+    load_frag(vf, V + (size_t)kp * rs, true, hl);
+  };
+  band_loop<3>(nq, nq, issue, prologue, refill, step);
+  write_out();
+}
+
+// Units of the band launch: unit x runs on XCD x % 8; each XCD is dealt a
+// contiguous range of units (neighbouring tiles share their window rows,
+// which then stay in that XCD's L2), and a tile's dq and dk/dv units are
+// neighbours.
+__device__ void bwd_band_body(const BwdParams& p) {
+  __shared__ union {
+    BandShared band;
+    BwdShared unit[4];
+  } shu;
+  const int N = 2 * p.n_bt;
+  const int x = blockIdx.x;
+  if (x >= N) {
+    // the global-token units, four per workgroup (one per wave), after the
+    // band tiles: they fill the slots the last band tiles leave free
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int unit = 4 * (x - N) + wv;
+    if (unit < p.n_gkv + p.n_gq + p.n_gk) bwd_global_unit(p, shu.unit[wv], unit);
+    return;
+  }
+  BandShared& sh = shu.band;
+  const int per = N / 8, rem = N % 8;
+  const int xcd = x % 8, y = x / 8;
+  const int m = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + y;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const BandTile bt = decode_band(p, m >> 1);
+  if (bt.t0 >= bt.len) return;  // every wave of the workgroup returns here
+  if (m & 1)
+    band_dkv(p, sh, bt, wv);
+  else
+    band_dq(p, sh, bt, wv);
 }
 
 // Global list of batch row b, ascending, by one workgroup of 256 threads:
@@ -646,7 +1192,12 @@ __device__ void prep_body(const BwdParams& p) {
   for (int e = 0; e < 4; ++e) s += (float)o[e] * (float)d[e];
 #pragma unroll
   for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
-  if (q4 == 0) p.Dsum[((size_t)b * p.H + h) * p.n + i] = s;
+  if (q4 == 0) {
+    const size_t at = ((size_t)b * p.H + h) * p.n + i;
+    p.dneg[at] = -s;
+    const float l = p.lse[at];
+    p.lneg[at] = __builtin_isfinite(l) ? -l / p.scale : 0.f;  // -inf: a row with no keys
+  }
   const float z[4] = {0.f, 0.f, 0.f, 0.f};
   store_f4(p.dqg + off, z);
   if (p.use_globals) {
@@ -661,10 +1212,14 @@ __device__ void prep_body(const BwdParams& p) {
 }
 
 #if LF_HALF_F16
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void lf_attn_bwd_f16(const BwdParams p) { bwd_body(p); }
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void lf_attn_bwd_f16(const BwdParams p) {
+  bwd_band_body(p);
+}
 __global__ __launch_bounds__(256) void lf_attn_bwd_prep_f16(const BwdParams p) { prep_body(p); }
 #else
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void lf_attn_bwd_bf16(const BwdParams p) { bwd_body(p); }
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void lf_attn_bwd_bf16(const BwdParams p) {
+  bwd_band_body(p);
+}
 __global__ __launch_bounds__(256) void lf_attn_bwd_prep_bf16(const BwdParams p) { prep_body(p); }
 #endif
 
@@ -676,7 +1231,8 @@ int launch_backward_f16(const BwdParams& bp, void* stream) {
   const size_t rows = (size_t)bp.B * bp.n * bp.H;
   const unsigned nlist = bp.use_globals ? (unsigned)bp.B : 0u;
   hipLaunchKernelGGL(lf_attn_bwd_prep_f16, dim3(nlist + (unsigned)((rows + 15) / 16)), dim3(256), 0, s, bp);
-  hipLaunchKernelGGL(lf_attn_bwd_f16, dim3(2 * bp.n_res + bp.n_gkv + bp.n_gq + bp.n_gk), dim3(64), 0, s, bp);
+  const int nglob = bp.n_gkv + bp.n_gq + bp.n_gk;
+  hipLaunchKernelGGL(lf_attn_bwd_f16, dim3(2 * bp.n_bt + (nglob + 3) / 4), dim3(256), 0, s, bp);
   return (int)hipGetLastError();
 }
 #else
@@ -686,7 +1242,8 @@ int launch_backward(const BwdParams& bp, void* stream) {
   const size_t rows = (size_t)bp.B * bp.n * bp.H;
   const unsigned nlist = bp.use_globals ? (unsigned)bp.B : 0u;
   hipLaunchKernelGGL(lf_attn_bwd_prep_bf16, dim3(nlist + (unsigned)((rows + 15) / 16)), dim3(256), 0, s, bp);
-  hipLaunchKernelGGL(lf_attn_bwd_bf16, dim3(2 * bp.n_res + bp.n_gkv + bp.n_gq + bp.n_gk), dim3(64), 0, s, bp);
+  const int nglob = bp.n_gkv + bp.n_gq + bp.n_gk;
+  hipLaunchKernelGGL(lf_attn_bwd_bf16, dim3(2 * bp.n_bt + (nglob + 3) / 4), dim3(256), 0, s, bp);
   return (int)hipGetLastError();
 }
 #endif

@@ -258,7 +258,7 @@ lf_status lf_attn_forward_lse(const lf_attn_params* p, const void* q, const void
 namespace {
 
 struct BwdLayout {
-  size_t gcount_off = 0, glist_off = 0, dsum_off = 0, bytes = 0;
+  size_t gcount_off = 0, glist_off = 0, dsum_off = 0, lse2_off = 0, bytes = 0;
   int gstride = 1;
 };
 
@@ -268,7 +268,8 @@ BwdLayout bwd_layout(const lf_attn_params* p) {
   L.gcount_off = kAlign;
   L.glist_off = L.gcount_off + align_up((size_t)p->B * sizeof(int32_t), kAlign);
   L.dsum_off = L.glist_off + align_up((size_t)p->B * L.gstride * sizeof(int32_t), kAlign);
-  L.bytes = L.dsum_off + align_up((size_t)p->B * p->H * p->n * sizeof(float), kAlign);
+  L.lse2_off = L.dsum_off + align_up((size_t)p->B * p->H * p->n * sizeof(float), kAlign);
+  L.bytes = L.lse2_off + align_up((size_t)p->B * p->H * p->n * sizeof(float), kAlign);
   return L;
 }
 
@@ -302,19 +303,19 @@ lf_status lf_attn_backward(const lf_attn_params* p, const void* q, const void* k
   const size_t mb = (size_t)p->B * p->n;
   const size_t lb = (size_t)p->B * p->H * p->n * sizeof(float);
   const BwdLayout L = bwd_layout(p);
-  // per-head residue tiles of 32 rows
+  // band tiles: kBwdBandRows consecutive rows of one residue class of one
+  // head (positions r, r + d, ...: n / d + 1 of them for r < n % d, else n / d)
   int64_t tiles = 0;
   lf::BwdParams bp;
   std::memset(&bp, 0, sizeof(bp));
   for (int h = 0; h < p->H; ++h) {
     const int d = pl.dil[h];
-    const int64_t per_class = ((p->n + d - 1) / d + 31) / 32;
+    const int64_t qn = p->n / d, rm = p->n % d, R = lf::kBwdBandRows;
     bp.dil[h] = d;
-    bp.rtiles[h] = (int32_t)per_class;
-    bp.tile0[h] = (int32_t)tiles;
-    tiles += per_class * d;
+    bp.btile0[h] = (int32_t)tiles;
+    tiles += rm * ((qn + 1 + R - 1) / R) + (d - rm) * ((qn + R - 1) / R);
   }
-  bp.tile0[p->H] = (int32_t)tiles;
+  bp.btile0[p->H] = (int32_t)tiles;
   const int64_t gslots = (p->max_global + 31) / 32;
   const int64_t chunks = (p->n + lf::kBwdChunk - 1) / lf::kBwdChunk;
   const int64_t bhn = (int64_t)p->B * p->H;
@@ -359,7 +360,8 @@ lf_status lf_attn_backward(const lf_attn_params* p, const void* q, const void* k
   bp.status = reinterpret_cast<int32_t*>(ws);
   bp.gcount = reinterpret_cast<int32_t*>(ws + L.gcount_off);
   bp.glist = reinterpret_cast<int32_t*>(ws + L.glist_off);
-  bp.Dsum = reinterpret_cast<float*>(ws + L.dsum_off);
+  bp.dneg = reinterpret_cast<float*>(ws + L.dsum_off);
+  bp.lneg = reinterpret_cast<float*>(ws + L.lse2_off);
   bp.B = p->B;
   bp.n = p->n;
   bp.H = p->H;
@@ -371,8 +373,8 @@ lf_status lf_attn_backward(const lf_attn_params* p, const void* q, const void* k
   const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / std::sqrt((double)p->D);
   bp.scale = (float)scale;
   bp.c = (float)(scale * 1.4426950408889634);
-  bp.tiles_per_b = (int32_t)tiles;
-  bp.n_res = (int32_t)(p->B * tiles);
+  bp.bt_per_b = (int32_t)tiles;
+  bp.n_bt = (int32_t)(p->B * tiles);
   bp.n_gkv = (int32_t)n_gkv;
   bp.n_gq = (int32_t)n_gq;
   bp.n_gk = (int32_t)n_gq;

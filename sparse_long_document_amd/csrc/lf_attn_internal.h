@@ -52,7 +52,7 @@ struct KernelParams {
 };
 
 // Backward: keys or rows per global-work unit.
-constexpr int kBwdChunk = 512;
+constexpr int kBwdChunk = 128;
 
 // Everything the backward launches need.
 struct BwdParams {
@@ -72,15 +72,16 @@ struct BwdParams {
   float* dqg;
   float* dkg;
   float* dvg;
-  float* Dsum;         // [B][H][n] workspace: <dout, out> per row
+  float* dneg;         // [B][H][n] workspace: -<dout, out> per row
+  float* lneg;         // [B][H][n] workspace: -lse / scale per row (0 where lse is not finite)
   int32_t* glist;      // [B][gstride] workspace: global positions, ascending
   int32_t* gcount;     // [B] workspace: entries of glist in use
   int32_t* status;     // device status word
   int32_t B, n, H, w, causal, max_global, use_globals, dtype;
   float c;             // score scale * log2(e)
   float scale;
-  int32_t tiles_per_b; // 32-row residue tiles per batch row, all heads
-  int32_t n_res;       // B * tiles_per_b
+  int32_t bt_per_b;    // band tiles (128 rows of one residue class) per batch row, all heads
+  int32_t n_bt;        // B * bt_per_b: the band launch runs a dq and a dk/dv workgroup per tile
   int32_t n_gkv;       // units of the global rows' key work: B * H * ceil(n / 32)
   int32_t n_gq;        // units of the global rows' query work
   int32_t n_gk;        // units of the global keys' work of local rows
@@ -88,12 +89,15 @@ struct BwdParams {
   int32_t chunks;      // ceil(n / kBwdChunk)
   int32_t gstride;     // max(max_global, 1)
   int32_t dil[LF_MAX_HEADS];
-  int32_t tile0[LF_MAX_HEADS + 1];  // first residue tile of each head within a batch row
-  int32_t rtiles[LF_MAX_HEADS];     // tiles per residue class of each head: ceil(ceil(n / d) / 32)
+  int32_t btile0[LF_MAX_HEADS + 1];  // first band tile of each head within a batch row
 };
 
-// Launches the backward (preparation with the global lists, then the
-// gradient kernel) for bf16 or f16 elements.  Returns the hipError_t value as int.
+// Rows of one band tile of the backward (four waves of 32).
+constexpr int kBwdBandRows = 128;
+
+// Launches the backward (preparation with the global lists and row sums,
+// the band kernel, then the global-token kernel when there is global work)
+// for bf16 or f16 elements.  Returns the hipError_t value as int.
 int launch_backward(const BwdParams& bp, void* stream);
 int launch_backward_f16(const BwdParams& bp, void* stream);
 

@@ -217,10 +217,11 @@ def _backward(p, ptrs=None, ws_bytes=1 << 30):
 
 
 def test_backward_workspace_bytes_layout():
-    # status block, B counts, B lists of max_global entries, one fp32 per row
+    # status block, B counts, B lists of max_global entries, two fp32 per
+    # row (<dout, out> and the log2-domain lse)
     p, _k = _params(B=2, n=4096, H=12, max_global=64)
     got = lf.library().lf_attn_backward_workspace_bytes(ctypes.byref(p))
-    assert got == 256 + 256 + 512 + 2 * 12 * 4096 * 4
+    assert got == 256 + 256 + 512 + 2 * 2 * 12 * 4096 * 4
     p, _k = _params(B=0)
     assert lf.library().lf_attn_backward_workspace_bytes(ctypes.byref(p)) == 0
 
