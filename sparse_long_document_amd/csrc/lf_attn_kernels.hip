@@ -560,13 +560,17 @@ struct HalfState {
   f32x16 o[kND];  // O^T of head dims 32db + ..., per 32-dim block db
   float m;      // reference max (log2 domain) of the lane's query
   float l;      // partial row sum of this lane (16 of the 32 keys per block)
-  int cnt;      // partial count of scored keys of this lane
+  int cnt;      // partial count of scored keys of this lane, beyond 16 per full block
+  int nfull;    // blocks whose 16 keys of every lane were all scored (uniform)
+  float thr;    // (m + kRescaleSlack) / c: a raw score above it moves the reference
 };
 
 __device__ __forceinline__ void state_init(HalfState& st) {
   st.m = kMInit;
   st.l = 0.f;
   st.cnt = 0;
+  st.nfull = 0;
+  st.thr = kMInit;  // set by softmax_core before its first use
 #pragma unroll
   for (int db = 0; db < kND; ++db)
 #pragma unroll
@@ -589,6 +593,10 @@ __device__ __forceinline__ void pv(f32x16 (&o)[kND], const PFrag<false>& pf, con
     for (int r = 0; r < 16; ++r) o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vt.a[db][r], pf.x[r], o[db], 0, 0, 0);
 }
 
+
+// Largest of the 16 scores of a lane.  Plain fmaxf: the compiler sees
+// that it reads MFMA results and inserts the wait states such a read needs
+// (it cannot see into inline asm).
 __device__ __forceinline__ float max16(const f32x16& s) {
   const float a = fmaxf(fmaxf(s[0], s[1]), s[2]);
   const float b = fmaxf(fmaxf(s[3], s[4]), s[5]);
@@ -600,17 +608,20 @@ __device__ __forceinline__ float max16(const f32x16& s) {
 
 // Scores of one block (masked scores are -inf) -> online-softmax
 // probabilities, with the running state rescaled if its reference max
-// moves; counts 16 scored keys per lane.  Lanes l and l ^ 32 hold the same
-// query's other 16 keys, but the exchange is only needed when the reference
-// max moves: the test "some score exceeds the reference by more than the
-// slack" is a wave-wide vote.
+// moves.  Lanes l and l ^ 32 hold the same query's other 16 keys, but the
+// exchange is only needed when the reference max moves: the test "some raw
+// score exceeds thr = (m + slack) / c" is a wave-wide vote.  The row sum is
+// that of the probabilities as they enter P V (rounded to the element
+// type; one chain of two-term dot products).
 template <bool B16>
 __device__ __forceinline__ void softmax_core(HalfState& st, f32x16& s, PFrag<B16>& pf, float c) {
-  const float ml = max16(s) * c;
-  if (__any(ml > st.m + kRescaleSlack)) {
+  const float mx = max16(s);
+  if (__any(mx > st.thr)) {
+    const float ml = mx * c;
     const float mn = fmaxf(st.m, fmaxf(ml, __shfl_xor(ml, 32)));
     const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
     st.m = mn;
+    st.thr = (mn + kRescaleSlack) / c;
     st.l *= alpha;
 #pragma unroll
     for (int db = 0; db < kND; ++db)
@@ -619,24 +630,19 @@ __device__ __forceinline__ void softmax_core(HalfState& st, f32x16& s, PFrag<B16
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -st.m));
-  st.cnt += 16;
   if constexpr (B16) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pf.x[ks][e] = (h16)s[8 * ks + e];
-    // row sum of the rounded probabilities that enter P V (two bf16 at a
-    // time with fp32 accumulation), in two chains
     const h16x2 one = {(h16)1.0f, (h16)1.0f};
-    float la = 0.f, lb = 0.f;
+    float l = st.l;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const h16x2 p0 = {pf.x[0][2 * j], pf.x[0][2 * j + 1]};
-      const h16x2 p1 = {pf.x[1][2 * j], pf.x[1][2 * j + 1]};
-      la = dot2h(p0, one, la);
-      lb = dot2h(p1, one, lb);
+    for (int j = 0; j < 8; ++j) {
+      const h16x2 pj = {pf.x[j >> 2][2 * (j & 3)], pf.x[j >> 2][2 * (j & 3) + 1]};
+      l = dot2h(pj, one, l);
     }
-    st.l += la + lb;
+    st.l = l;
   } else {
     float t8[8];
 #pragma unroll
@@ -865,7 +871,8 @@ __device__ void merge_parities(const HalfState& st, Shared<B16>& sh, int qh, int
   for (int g = 0; g < kHalfO / 4; ++g)
     po[g * 64 + lane] = f32x4{give[4 * g], give[4 * g + 1], give[4 * g + 2], give[4 * g + 3]};
   const float l = st.l + __shfl_xor(st.l, 32);
-  const int cnt = st.cnt + __shfl_xor(st.cnt, 32);
+  const int mycnt = st.cnt + 16 * st.nfull;
+  const int cnt = mycnt + __shfl_xor(mycnt, 32);
   float* pm = reinterpret_cast<float*>(mine + kParkOBytes);
   if (hh == 0) {
     pm[lane] = st.m;
@@ -1285,6 +1292,7 @@ struct HalfLoop {
       const f32x16 zero = {};
       s = zero;
       qk(s, kf, qf);
+      st.nfull += 1;
     } else {
       uint32_t keymask;
       if (i >= src.nwin) {
@@ -1313,6 +1321,7 @@ struct HalfLoop {
       if (cls == 2) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
+        st.nfull += 1;
       } else {
         const uint32_t vmk = src.valid_bits(i) & (keymask >> (4 * (ln >> 5)));  // bit c_r: element r scored
         const uint32_t inv = ~vmk;
@@ -1321,7 +1330,7 @@ struct HalfLoop {
         LF_BIAS(0); LF_BIAS(1); LF_BIAS(2); LF_BIAS(3); LF_BIAS(4); LF_BIAS(5); LF_BIAS(6); LF_BIAS(7);
         LF_BIAS(8); LF_BIAS(9); LF_BIAS(10); LF_BIAS(11); LF_BIAS(12); LF_BIAS(13); LF_BIAS(14); LF_BIAS(15);
 #undef LF_BIAS
-        st.cnt += __popc(vmk & 0x0f0f0f0fu) - 16;  // softmax_core adds 16
+        st.cnt += __popc(vmk & 0x0f0f0f0fu);
       }
       qk(s, kf, qf);
     }
@@ -1464,6 +1473,7 @@ __device__ void vec_global_columns(HalfState& st, const Frag<true>& qf, const Ba
       const float mn = fmaxf(st.m, take ? sc : kNegInf);
       const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
       st.m = mn;
+      st.thr = (mn + kRescaleSlack) / c;
       st.l *= alpha;
 #pragma unroll
       for (int db = 0; db < kND; ++db)
