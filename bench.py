@@ -330,7 +330,7 @@ def report_projections(args, prob, run, ms, mode, t_wall):
                    "timing": mode, "wall_s": round(t_wall, 3)},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": f"lf_proj_{dname}", "flops_per_launch": flops},
+                     "kernel": f"lf_proj_*_{dname}", "flops_per_launch": flops},
     }
     if not args.no_cpu_baseline:
         # the CPU-baseline leg: the fp64 oracle on the whole job, timed; its

@@ -193,7 +193,8 @@ lf_status lf_attn_backward(const lf_attn_params* p,
  * start as copies of the local ones).  fp32 accumulation, the bias added in
  * fp32, the result rounded to nearest even.  Errors: LF_ERR_INVALID_ARG for
  * M, C or P < 1, a NULL x, w or out, or out overlapping an input;
- * LF_ERR_UNSUPPORTED for another dtype, C not a multiple of 64, P > 6.
+ * LF_ERR_UNSUPPORTED for another dtype, C not a multiple of 64, P > 6, x or
+ * w larger than 2^31 - 1 bytes, or x, w, out or bias not 16-byte aligned.
  * Allocates nothing, needs no workspace. */
 lf_status lf_attn_project(int32_t M, int32_t C, int32_t P, int32_t dtype,
                           const void* x, const void* w, const float* bias, void* out, void* stream);

@@ -394,6 +394,10 @@ lf_status lf_attn_project(int32_t M, int32_t C, int32_t P, int32_t dtype, const 
   const int64_t N = (int64_t)P * C;
   if (N > INT32_MAX || (N + 127) / 128 > 65535) return LF_ERR_UNSUPPORTED;
   const size_t xb = (size_t)M * C * 2, wb = (size_t)N * C * 2, ob = (size_t)P * xb, bb = (size_t)N * 4;
+  // x and w are addressed through 32-bit buffer offsets; 16-byte loads and
+  // stores need 16-byte aligned bases
+  if (xb > (size_t)INT32_MAX || wb > (size_t)INT32_MAX) return LF_ERR_UNSUPPORTED;
+  if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)out | (uintptr_t)bias) & 15u) return LF_ERR_UNSUPPORTED;
   if (overlaps(out, ob, x, xb) || overlaps(out, ob, w, wb) || (bias && overlaps(out, ob, bias, bb)))
     return LF_ERR_INVALID_ARG;
   lf::ProjParams pp;

@@ -21,4 +21,9 @@ struct ProjParams {
 // Launches the projection GEMM (bf16 or f16).  Returns the hipError_t value.
 int launch_project(const ProjParams& pp, void* stream);
 
+// Tile configuration the launch uses for M tokens and N stacked features on
+// a device with `cus` compute units: 0 = 128 x 128, 1 = 128 x 192,
+// 2 = 256 x 288 (tokens x features).
+int proj_tile_config(int M, int N, int cus);
+
 }  // namespace lf

@@ -250,3 +250,22 @@ def test_forward_lse_requires_lse():
     # lse overlapping the output
     assert lib.lf_attn_forward_lse(ctypes.byref(p), *args, vp(FAKE + (4 << 32) + 256), *ws) \
         == lf.LF_ERR_INVALID_ARG
+
+
+def test_project_argument_errors():
+    lib = lf.library()
+    vp = ctypes.c_void_p
+    BF16 = lf._DTYPES[torch.bfloat16]
+
+    def call(M=4096, C=768, P=6, dtype=BF16, x=FAKE, w=FAKE + (1 << 32), bias=FAKE + (2 << 32),
+             out=FAKE + (3 << 32)):
+        return lib.lf_attn_project(M, C, P, dtype, vp(x), vp(w), vp(bias), vp(out), vp(None))
+
+    for kw in (dict(M=0), dict(C=0), dict(P=0), dict(x=None), dict(w=None), dict(out=None),
+               dict(out=FAKE + 4096)):  # out overlapping x
+        assert call(**kw) == lf.LF_ERR_INVALID_ARG, kw
+    for kw in (dict(dtype=99), dict(C=96), dict(P=7),
+               dict(M=1 << 20, C=1024),  # x larger than 2^31 - 1 bytes
+               dict(x=FAKE + 8), dict(w=FAKE + (1 << 32) + 2), dict(out=FAKE + (3 << 32) + 4),
+               dict(bias=FAKE + (2 << 32) + 8)):  # bases not 16-byte aligned
+        assert call(**kw) == lf.LF_ERR_UNSUPPORTED, kw

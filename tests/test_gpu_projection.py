@@ -54,6 +54,19 @@ def test_projection_small(M, C, P, dtype):
     check(7 + M, M, C, P, dtype)
 
 
+@pytest.mark.parametrize("M,C,P,dtype", [(2000, 192, 1, torch.bfloat16), (2333, 448, 6, torch.bfloat16),
+                                          (2000, 448, 5, torch.bfloat16), (2000, 448, 5, torch.float16),
+                                          (4000, 704, 6, torch.bfloat16), (4000, 704, 6, torch.float16)],
+                         ids=["s-a", "s-b", "m", "m-f16", "l", "l-f16"])
+def test_projection_tile_configs(M, C, P, dtype):
+    """Each tile configuration of the launch (on a 256-CU device the
+    chooser takes 128 x 128 tiles for the first two sizes, 128 x 192 for the
+    next two and 256 x 288 for the last two), with token counts that are
+    not multiples of the token tile and feature counts that are not
+    multiples of the feature tile."""
+    check(31 + M + C, M, C, P, dtype)
+
+
 def test_projection_without_bias():
     check(11, 130, 128, 2, torch.bfloat16, with_bias=False)
 
