@@ -334,7 +334,9 @@ def project(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = Non
     """The layer's input projections (``lf_attn_project``): x [M, C] (or
     [B, n, C]) bf16/f16, w [P*C, C] stacked weights in the [out, in] layout,
     bias fp32 [P*C] or None.  Returns out [P, M, C] (or [P, B, n, C]);
-    out[p].view(B, n, H, 64) is one attention input."""
+    out[p].view(B, n, H, 64) is one attention input.  The four buffers must
+    start on 16-byte boundaries (freshly allocated tensors do; an offset
+    view may not), else the call raises with LF_ERR_UNSUPPORTED."""
     shape = x.shape
     if x.dim() == 3:
         x = x.reshape(-1, shape[-1])
