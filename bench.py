@@ -233,7 +233,7 @@ class ProjRunner:
     """Prepared arguments for repeated lf_attn_project calls: the six
     projections of the workload's tokens."""
 
-    def __init__(self, prob, device):
+    def __init__(self, prob, device, global_only=False):
         import torch
 
         import sparse_long_document_amd as lf
@@ -241,6 +241,8 @@ class ProjRunner:
 
         B, n, H, D = prob.shape
         self.M, self.C, self.P = B * n, H * D, 6
+        self.global_only = global_only
+        self.mask = prob.mask.reshape(-1).to(torch.int8).to(device).contiguous()
         x, w, b = workloads.projection_problem(3, self.M, self.C, self.P, prob.q.dtype)
         self.x_cpu, self.w_cpu, self.b_cpu = x, w, b
         self.x, self.w, self.b = x.to(device), w.to(device), b.to(device)
@@ -250,9 +252,15 @@ class ProjRunner:
         vp = ctypes.c_void_p
         self.lib = lf.library()
         self.dt = lf._DTYPES[prob.q.dtype]
-        self.args = (self.M, self.C, self.P, self.dt, vp(self.x.data_ptr()), vp(self.w.data_ptr()),
-                     vp(self.b.data_ptr()), vp(self.out.data_ptr()), vp(self.stream))
-        self.fn = self.lib.lf_attn_project
+        if global_only:  # Q_g (projection 3) at the global tokens only
+            self.args = (self.M, self.C, self.P, self.dt, vp(self.x.data_ptr()), vp(self.w.data_ptr()),
+                         vp(self.b.data_ptr()), vp(self.mask.data_ptr()), ctypes.c_uint32(1 << 3),
+                         vp(self.out.data_ptr()), vp(self.stream))
+            self.fn = self.lib.lf_attn_project_global_only
+        else:
+            self.args = (self.M, self.C, self.P, self.dt, vp(self.x.data_ptr()), vp(self.w.data_ptr()),
+                         vp(self.b.data_ptr()), vp(self.out.data_ptr()), vp(self.stream))
+            self.fn = self.lib.lf_attn_project
 
     def launch(self):
         st = self.fn(*self.args)
@@ -317,6 +325,9 @@ def report_projections(args, prob, run, ms, mode, t_wall):
     import torch
 
     flops = 2.0 * run.M * run.C * run.P * run.C
+    if run.global_only:  # Q_g only at the global tokens: the FLOPs actually needed
+        n_glob = int((run.mask == 2).sum().item())
+        flops = 2.0 * run.M * run.C * (run.P - 1) * run.C + 2.0 * n_glob * run.C * run.C
     achieved = flops / (ms * 1e-3) / 1e12
     dname = {torch.bfloat16: "bf16", torch.float16: "f16"}[prob.q.dtype]
     B, n, H, D = prob.shape
@@ -327,6 +338,7 @@ def report_projections(args, prob, run, ms, mode, t_wall):
         "vs_baseline": None, "dtype": dname,
         "data": "synthetic (seeded N(0,1) hidden states, N(0,1/C) weights, N(0,0.01) bias)",
         "config": {"workload": args.workload, "pass": "projections", "M": run.M, "C": run.C, "P": run.P,
+                   "global_only": "Q_g at global tokens" if run.global_only else None,
                    "timing": mode, "wall_s": round(t_wall, 3)},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
@@ -351,6 +363,8 @@ def report_projections(args, prob, run, ms, mode, t_wall):
                                             f"matmul on {threads} BLAS threads, mean of {reps} runs"}
         if not args.no_check:
             got = run.out.float().cpu().numpy()
+            if run.global_only:
+                ref[3][run.mask.cpu().numpy() != 2] = 0.0
             excess = float((np.abs(got - ref) - (2.0 ** -8 * np.abs(ref) + 1e-3)).max())
             result["parity"] = {"kind": "every row of all six projections vs the fp64 oracle run of the "
                                         "CPU-baseline leg", "max_abs_err": float(np.abs(got - ref).max()),
@@ -600,6 +614,9 @@ def main():
     ap.add_argument("--pass", dest="which", choices=["forward", "backward", "projections", "encoder"],
                     default="forward")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing")
+    ap.add_argument("--global-only", action="store_true",
+                    help="with --pass projections: Q_g at the workload's global tokens only "
+                         "(lf_attn_project_global_only)")
     ap.add_argument("--sweep", action="store_true",
                     help="time the longformer-base layer at n = 1024 ... 16384 instead (one line each)")
     args = ap.parse_args()
@@ -619,8 +636,10 @@ def main():
     torch.cuda.set_device(dev)
     bwd = args.which != "forward"  # a runner with out_t, compared across graph replays
     prob = None if args.which == "encoder" else workloads.by_name(args.workload)
-    run = {"forward": Runner, "backward": BwdRunner, "projections": ProjRunner,
-           "encoder": EncRunner}[args.which](prob, dev)
+    if args.which == "projections":
+        run = ProjRunner(prob, dev, global_only=args.global_only)
+    else:
+        run = {"forward": Runner, "backward": BwdRunner, "encoder": EncRunner}[args.which](prob, dev)
     for _ in range(max(1, args.warmup)):
         run.launch()
     torch.cuda.synchronize()

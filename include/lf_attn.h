@@ -199,6 +199,24 @@ lf_status lf_attn_backward(const lf_attn_params* p,
 lf_status lf_attn_project(int32_t M, int32_t C, int32_t P, int32_t dtype,
                           const void* x, const void* w, const float* bias, void* out, void* stream);
 
+/* lf_attn_project with some of the P projections needed at the global
+ * tokens only.  The separate global projections score global attention
+ * (segmentfault Longformer summary, "Linear projections for global
+ * attention"): of them Q_g enters only the rows of global tokens, while
+ * K_g and V_g are read at every token.  For each set bit p of global_only,
+ * out[p][m] is computed as in lf_attn_project where mask[m] == 2 and is
+ * written as zero at every other token m; the other projections are exactly
+ * those of lf_attn_project.  mask: int8 [M], the attention's [B, n] mask
+ * (M = B*n, token-major), read on the device only; tiles of global-only
+ * features with no global token skip their reduction.  With the weights
+ * stacked Q_s, K_s, V_s, Q_g, K_g, V_g, global_only = 1 << 3 gives the
+ * attention all it reads.  Errors: those of lf_attn_project, and
+ * LF_ERR_INVALID_ARG for a bit at p >= P, a NULL mask with global_only != 0,
+ * or out overlapping the mask. */
+lf_status lf_attn_project_global_only(int32_t M, int32_t C, int32_t P, int32_t dtype, const void* x,
+                                      const void* w, const float* bias, const int8_t* mask,
+                                      uint32_t global_only, void* out, void* stream);
+
 /* Size of the device scratch that lf_attn_forward_noalloc uses instead of a
  * workspace (one copy per device, held until the process ends). */
 #define LF_NOALLOC_SCRATCH_BYTES (8u << 20)

@@ -68,7 +68,7 @@ LF_MAX_PROJ = 6
 
 SYMBOLS = ("lf_attn_workspace_bytes", "lf_attn_workspace_init", "lf_attn_forward",
            "lf_attn_forward_lse", "lf_attn_backward_workspace_bytes", "lf_attn_backward",
-           "lf_attn_project", "lf_attn_forward_noalloc",
+           "lf_attn_project", "lf_attn_project_global_only", "lf_attn_forward_noalloc",
            "lf_attn_device_status", "lf_status_str")
 LF_NOALLOC_SCRATCH_BYTES = 8 << 20
 
@@ -123,6 +123,8 @@ def library() -> ctypes.CDLL:
             i32 = ctypes.c_int32
             lib.lf_attn_project.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
             lib.lf_attn_project.restype = ctypes.c_int
+            lib.lf_attn_project_global_only.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, ctypes.c_uint32, vp, vp]
+            lib.lf_attn_project_global_only.restype = ctypes.c_int
             lib.lf_attn_forward_noalloc.argtypes = [ctypes.POINTER(Params), vp, vp, vp, vp, vp, vp,
                                                     vp, vp, vp, vp]
             lib.lf_attn_forward_noalloc.restype = ctypes.c_int
@@ -330,13 +332,20 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 
 def project(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
-            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+            out: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
+            global_only: Sequence[int] = ()) -> torch.Tensor:
     """The layer's input projections (``lf_attn_project``): x [M, C] (or
     [B, n, C]) bf16/f16, w [P*C, C] stacked weights in the [out, in] layout,
     bias fp32 [P*C] or None.  Returns out [P, M, C] (or [P, B, n, C]);
     out[p].view(B, n, H, 64) is one attention input.  The four buffers must
     start on 16-byte boundaries (freshly allocated tensors do; an offset
-    view may not), else the call raises with LF_ERR_UNSUPPORTED."""
+    view may not), else the call raises with LF_ERR_UNSUPPORTED.
+
+    With ``global_only`` (projection indices) and ``mask`` (the attention's
+    [B, n] mask, or [M]), those projections are computed at the tokens with
+    mask 2 only and are zero elsewhere (``lf_attn_project_global_only``);
+    with the weights stacked Q_s, K_s, V_s, Q_g, K_g, V_g, global_only=(3,)
+    leaves the attention's inputs unchanged where it reads them."""
     shape = x.shape
     if x.dim() == 3:
         x = x.reshape(-1, shape[-1])
@@ -357,6 +366,25 @@ def project(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = Non
     _check_tensor("out", out, (P, M, C), x.dtype, x.device)
     vp = ctypes.c_void_p
     stream = torch.cuda.current_stream(x.device).cuda_stream
+    bits = 0
+    for q in global_only:
+        if not 0 <= int(q) < P:
+            raise ValueError(f"global_only index {q} outside 0..{P - 1}")
+        bits |= 1 << int(q)
+    if bits:
+        if mask is None:
+            raise ValueError("global_only needs the mask")
+        m8 = mask.reshape(-1)
+        if m8.numel() != M:
+            raise ValueError("mask must hold one value per token")
+        m8 = m8.to(device=x.device, dtype=torch.int8).contiguous()
+        st = library().lf_attn_project_global_only(
+            M, C, P, _DTYPES.get(x.dtype, 99), vp(x.data_ptr()), vp(w.data_ptr()),
+            vp(bias.data_ptr() if bias is not None else None), vp(m8.data_ptr()), ctypes.c_uint32(bits),
+            vp(out.data_ptr()), vp(stream))
+        if st != LF_OK:
+            raise LfError(st, "lf_attn_project_global_only")
+        return out.view((P,) + tuple(shape[:-1]) + (C,))
     st = library().lf_attn_project(M, C, P, _DTYPES.get(x.dtype, 99), vp(x.data_ptr()), vp(w.data_ptr()),
                                    vp(bias.data_ptr() if bias is not None else None), vp(out.data_ptr()),
                                    vp(stream))
@@ -373,7 +401,9 @@ def encoder_attention(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Ten
     """The attention sublayer of a Longformer/LED encoder layer as a chain
     of the C ABI's calls on the current stream: ``lf_attn_project`` (the six
     input projections Q_s, K_s, V_s, Q_g, K_g, V_g of x [B, n, C] in one
-    launch, w [6C, C] stacked in that order, bias fp32 [6C] or None), then
+    launch, w [6C, C] stacked in that order, bias fp32 [6C] or None; with a
+    mask, ``lf_attn_project_global_only`` with Q_g at the global tokens
+    only, zero elsewhere), then
     ``lf_attn_forward`` on the six [B, n, H, 64] views of its output (H =
     C / 64), then, when w_out [C, C] is given, the output projection with
     ``lf_attn_project`` (P = 1, bias b_out fp32 [C] or None).  Returns
@@ -388,7 +418,8 @@ def encoder_attention(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Ten
     H = C // LF_HEAD_DIM
     if w.shape != (6 * C, C):
         raise ValueError("w must be [6C, C]: Q_s, K_s, V_s, Q_g, K_g, V_g stacked")
-    proj = project(x, w, bias)  # [6, B, n, C]
+    # Q_g is read at the global rows only: computed there, zero elsewhere
+    proj = project(x, w, bias, mask=mask, global_only=(3,)) if mask is not None else project(x, w, bias)
     heads = [proj[i].view(B, n, H, LF_HEAD_DIM) for i in range(6)]
     attn = forward(*heads, mask=mask, window=window, dilation=dilation, scale=scale, max_global=max_global,
                    validate=validate, workspace=workspace)

@@ -385,12 +385,14 @@ lf_status lf_attn_backward(const lf_attn_params* p, const void* q, const void* k
   return e == 0 ? LF_OK : LF_ERR_HIP;
 }
 
-lf_status lf_attn_project(int32_t M, int32_t C, int32_t P, int32_t dtype, const void* x, const void* w,
-                          const float* bias, void* out, void* stream) {
+static lf_status project_impl(int32_t M, int32_t C, int32_t P, int32_t dtype, const void* x, const void* w,
+                              const float* bias, const int8_t* mask, uint32_t global_only, void* out, void* stream) {
   if (M <= 0 || C <= 0 || P <= 0) return LF_ERR_INVALID_ARG;
   if (!x || !w || !out) return LF_ERR_INVALID_ARG;
   if (dtype != LF_BF16 && dtype != LF_F16) return LF_ERR_UNSUPPORTED;
   if (C % 64 != 0 || P > LF_MAX_PROJ) return LF_ERR_UNSUPPORTED;
+  if (global_only >> P) return LF_ERR_INVALID_ARG;  // a projection beyond P
+  if (global_only && !mask) return LF_ERR_INVALID_ARG;
   const int64_t N = (int64_t)P * C;
   if (N > INT32_MAX || (N + 127) / 128 > 65535) return LF_ERR_UNSUPPORTED;
   const size_t xb = (size_t)M * C * 2, wb = (size_t)N * C * 2, ob = (size_t)P * xb, bb = (size_t)N * 4;
@@ -398,7 +400,8 @@ lf_status lf_attn_project(int32_t M, int32_t C, int32_t P, int32_t dtype, const 
   // stores need 16-byte aligned bases
   if (xb > (size_t)INT32_MAX || wb > (size_t)INT32_MAX) return LF_ERR_UNSUPPORTED;
   if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)out | (uintptr_t)bias) & 15u) return LF_ERR_UNSUPPORTED;
-  if (overlaps(out, ob, x, xb) || overlaps(out, ob, w, wb) || (bias && overlaps(out, ob, bias, bb)))
+  if (overlaps(out, ob, x, xb) || overlaps(out, ob, w, wb) || (bias && overlaps(out, ob, bias, bb)) ||
+      (global_only && overlaps(out, ob, mask, (size_t)M)))
     return LF_ERR_INVALID_ARG;
   lf::ProjParams pp;
   pp.x = x;
@@ -409,8 +412,21 @@ lf_status lf_attn_project(int32_t M, int32_t C, int32_t P, int32_t dtype, const 
   pp.C = C;
   pp.N = (int32_t)N;
   pp.dtype = dtype;
+  pp.mask = global_only ? mask : nullptr;
+  pp.global_only = global_only;
   const int e = lf::launch_project(pp, stream);
   return e == 0 ? LF_OK : LF_ERR_HIP;
+}
+
+lf_status lf_attn_project(int32_t M, int32_t C, int32_t P, int32_t dtype, const void* x, const void* w,
+                          const float* bias, void* out, void* stream) {
+  return project_impl(M, C, P, dtype, x, w, bias, nullptr, 0u, out, stream);
+}
+
+lf_status lf_attn_project_global_only(int32_t M, int32_t C, int32_t P, int32_t dtype, const void* x,
+                                      const void* w, const float* bias, const int8_t* mask,
+                                      uint32_t global_only, void* out, void* stream) {
+  return project_impl(M, C, P, dtype, x, w, bias, mask, global_only, out, stream);
 }
 
 lf_status lf_attn_device_status(const void* workspace, void* stream, int32_t* status) {

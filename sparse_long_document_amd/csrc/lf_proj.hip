@@ -24,6 +24,11 @@
 // land.  Consecutive tiles on one XCD form blocks of 8 token tiles by the
 // feature tiles, so that the tiles resident on one L2 share x and w rows.
 //
+// Projections flagged as needed at global tokens only (the global query
+// projection, whose rows other than the global tokens' the attention never
+// reads) are written as zero at the other tokens, and a tile of such
+// features with no global token skips its reduction.
+//
 // The epilogue adds the bias in fp32, rounds to the element type (nearest
 // even), regroups each lane's values with its partner 32 lanes away so
 // that every lane holds eight consecutive features of one token, and
@@ -134,6 +139,22 @@ __device__ void proj_body(const ProjParams& p) {
   const uint32_t rowb = (uint32_t)C * 2u;
   const int steps = C / 64;
 
+  // Projections needed at global tokens only: a tile whose features all
+  // belong to such projections and whose tokens hold no global one only
+  // writes zeros.
+  bool skip = false;
+  if (p.global_only) {
+    const int plo = n0 / C, phi = (min(n0 + BN, N) - 1) / C;
+    bool all = true;
+    for (int q = plo; q <= phi; ++q) all = all && ((p.global_only >> q) & 1u);
+    if (all) {
+      // every wave scans all of the tile's tokens itself: no barrier
+      bool any = false;
+      for (int r = lane; r < BM; r += 64) any = any || (m0 + r < M && p.mask[m0 + r] == 2);
+      skip = !__any(any);
+    }
+  }
+
   // Loads: wave wv stages x rows [8 j, 8 j + 8) for j = wv + kWaves u <
   // BM / 8 and the same w rows below BN.  Lane l of load j takes chunk
   // l % 8 of tile row 8 j + l / 8 (one 16-byte load; a wave covers eight
@@ -200,6 +221,7 @@ __device__ void proj_body(const ProjParams& p) {
   float4 bias4 = {0.f, 0.f, 0.f, 0.f};
   const bool bias_lane = p.bias && tid < BN / 4 && n0 + 4 * tid < N;
 
+  if (!skip) {
   load(0);
   store(0);
   if (steps > 1) load(1);
@@ -230,9 +252,12 @@ __device__ void proj_body(const ProjParams& p) {
     // reading the stage of step s (the bias staging below reuses it)
     lds_barrier();
   }
+  }
   float* bias_lds = reinterpret_cast<float*>(smem + (steps & 1) * Ly::kStageBytes);
-  if (bias_lane) *reinterpret_cast<float4*>(bias_lds + 4 * tid) = bias4;
-  lds_barrier();
+  if (!skip) {
+    if (bias_lane) *reinterpret_cast<float4*>(bias_lds + 4 * tid) = bias4;
+    lds_barrier();
+  }
 
   // Epilogue.  Lane (c, h) = (l % 32, l / 32) of tile (i, j) holds token
   // m0 + wm BM/WM + 32 i + c and features f0 + 8 g + 4 h + e in acc[4 g + e]
@@ -249,7 +274,8 @@ __device__ void proj_body(const ProjParams& p) {
     float4 bv[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      bv[g] = p.bias ? *reinterpret_cast<const float4*>(bias_lds + (f0 - n0) + 8 * g + 4 * h) : float4{0.f, 0.f, 0.f, 0.f};
+      bv[g] = p.bias && !skip ? *reinterpret_cast<const float4*>(bias_lds + (f0 - n0) + 8 * g + 4 * h)
+                              : float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       uint32_t pk[4][2];
@@ -272,12 +298,14 @@ __device__ void proj_body(const ProjParams& p) {
         }
       const int m = m0 + wm * (BM / Ly::WM) + 32 * i + c;
       if (m < M) {
+        const bool global_row = p.global_only && p.mask[m] == 2;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int f = f0 + 16 * q + 8 * h;
           const int proj = f / C, col = f - proj * C;
+          const bool zero = skip || (((p.global_only >> proj) & 1u) && !global_row);
           *reinterpret_cast<u32x4*>(out + ((size_t)proj * M + m) * C + col) =
-              u32x4{pk[2 * q][0], pk[2 * q][1], pk[2 * q + 1][0], pk[2 * q + 1][1]};
+              zero ? u32x4{0u, 0u, 0u, 0u} : u32x4{pk[2 * q][0], pk[2 * q][1], pk[2 * q + 1][0], pk[2 * q + 1][1]};
         }
       }
     }

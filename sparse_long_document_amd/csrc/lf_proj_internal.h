@@ -16,6 +16,11 @@ struct ProjParams {
   const float* bias;  // [N] or null
   void* out;          // [P, M, C]
   int32_t M, C, N, dtype;
+  // projections computed at global tokens only: bit p set -> out[p][m] is
+  // computed where mask[m] == 2 and zero elsewhere (mask [M] int8; null and
+  // 0 for the plain projections)
+  const int8_t* mask;
+  uint32_t global_only;
 };
 
 // Launches the projection GEMM (bf16 or f16).  Returns the hipError_t value.

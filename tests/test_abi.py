@@ -269,3 +269,20 @@ def test_project_argument_errors():
                dict(x=FAKE + 8), dict(w=FAKE + (1 << 32) + 2), dict(out=FAKE + (3 << 32) + 4),
                dict(bias=FAKE + (2 << 32) + 8)):  # bases not 16-byte aligned
         assert call(**kw) == lf.LF_ERR_UNSUPPORTED, kw
+
+
+def test_project_global_only_argument_errors():
+    lib = lf.library()
+    vp = ctypes.c_void_p
+    BF16 = lf._DTYPES[torch.bfloat16]
+
+    def call(P=6, bits=1 << 3, mask=FAKE + (4 << 32), out=FAKE + (3 << 32)):
+        return lib.lf_attn_project_global_only(4096, 768, P, BF16, vp(FAKE), vp(FAKE + (1 << 32)),
+                                               vp(FAKE + (2 << 32)), vp(mask), ctypes.c_uint32(bits), vp(out),
+                                               vp(None))
+
+    assert call(bits=1 << 6) == lf.LF_ERR_INVALID_ARG  # a projection beyond P
+    assert call(P=3, bits=1 << 3) == lf.LF_ERR_INVALID_ARG
+    assert call(mask=None) == lf.LF_ERR_INVALID_ARG
+    assert call(mask=FAKE + (3 << 32) + 4096) == lf.LF_ERR_INVALID_ARG  # mask inside out
+    assert call(P=7) == lf.LF_ERR_UNSUPPORTED

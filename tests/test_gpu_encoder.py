@@ -51,6 +51,9 @@ def check_chain(prob, heads=None, rows_per_head=None):
     # stage 1: the six projections
     x64 = prob.x.reshape(B * n, C).float().numpy()
     ref_p = oracle.project(x64, prob.w.float().numpy(), prob.bias.numpy()).reshape(6, B, n, C)
+    # the chain computes Q_g at the global tokens only and zero elsewhere
+    # (lf_attn_project_global_only): the attention reads it nowhere else
+    ref_p[3][prob.mask.numpy() != 2] = 0.0
     gp = proj.float().cpu().numpy()
     assert _proj_ok(gp, ref_p), float(np.abs(gp - ref_p).max())
     # stage 2: attention on the GPU's projections
@@ -84,7 +87,9 @@ def test_encoder_chain_copied_global_projections():
     _y, proj, _a = lf.encoder_attention(prob.x.to(d), prob.w.to(d), prob.bias.to(d), prob.mask.to(d),
                                         prob.window, w_out=prob.w_out.to(d), b_out=prob.b_out.to(d),
                                         return_intermediate=True)
-    assert torch.equal(proj[:3], proj[3:])
+    assert torch.equal(proj[1:3], proj[4:6])
+    g = prob.mask.to(d) == 2
+    assert torch.equal(proj[0][g], proj[3][g]) and not proj[3][~g].any()
 
 
 def test_led_encoder_n16384_two_heads():

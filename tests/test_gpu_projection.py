@@ -67,6 +67,61 @@ def test_projection_tile_configs(M, C, P, dtype):
     check(31 + M + C, M, C, P, dtype)
 
 
+def check_global_only(seed, M, C, P, dtype, bits, mask):
+    """lf_attn_project_global_only: projections in ``bits`` at the tokens
+    with mask 2 only (zero elsewhere), the others as lf_attn_project, and
+    exactly the plain launch's values wherever it computes them."""
+    _say(f"[gpu proj global-only] M={M} C={C} P={P} dtype={dtype} bits={bits} globals={(mask == 2).sum()}")
+    x, w, b = workloads.projection_problem(seed, M, C, P, dtype)
+    d = torch.device("cuda")
+    m = torch.from_numpy(mask.astype(np.int8))
+    y = lf.project(x.to(d), w.to(d), b.to(d), mask=m.to(d), global_only=bits)
+    full = lf.project(x.to(d), w.to(d), b.to(d))
+    torch.cuda.synchronize()
+    ref = oracle.project(x.float().numpy(), w.float().numpy(), b.numpy())
+    g = mask == 2
+    for q in bits:
+        ref[q][~g] = 0.0
+    got = y.float().cpu().numpy()
+    excess = np.abs(got - ref) - (REL[dtype] * np.abs(ref) + 1e-3)
+    _say(f"      max abs err {np.abs(got - ref).max():.3e}, worst excess {excess.max():.3e}")
+    assert excess.max() <= 0
+    gt = torch.from_numpy(g).to(d)
+    for q in range(P):
+        if q in bits:
+            assert torch.equal(y[q][gt], full[q][gt]) and not y[q][~gt].any()
+        else:
+            assert torch.equal(y[q], full[q])
+
+
+def _mask(rng, M, n_global, others=True):
+    m = np.ones(M, dtype=np.int64)
+    if others:
+        m[rng.random(M) < 0.05] = 0
+        m[rng.random(M) < 0.01] = 3  # not a global token
+    if n_global:
+        m[rng.choice(M, size=n_global, replace=False)] = 2
+    return m
+
+
+@pytest.mark.parametrize("M,C,P,bits,n_global", [(300, 128, 6, (3,), 5), (2000, 448, 5, (3, 4), 9),
+                                                 (4000, 704, 6, (3,), 17), (4096, 768, 6, (3,), 1),
+                                                 (2333, 448, 6, (3,), 0)],
+                         ids=["s", "m-two", "l", "longformer-base", "no-global"])
+def test_projection_global_only(M, C, P, bits, n_global):
+    rng = np.random.default_rng(M + C)
+    check_global_only(41 + M, M, C, P, torch.bfloat16, bits, _mask(rng, M, n_global))
+
+
+def test_projection_global_only_f16_clustered():
+    """Global tokens all in one token tile: every other tile of Q_g
+    features skips its reduction."""
+    M = 2000
+    m = np.ones(M, dtype=np.int64)
+    m[130:140] = 2
+    check_global_only(47, M, 448, 5, torch.float16, (3,), m)
+
+
 def test_projection_without_bias():
     check(11, 130, 128, 2, torch.bfloat16, with_bias=False)
 
