@@ -12,24 +12,27 @@
 // D_i = <dout_i, out_i>, de_j = p_j (dp_j - D_i); dq_i = s sum_j de_j k_j,
 // dk_j += s de_j q_i, dv_j += p_j dout_i.
 //
-// Three launches:
-//   * preparation: the global token list of each batch row, D_i per row,
-//     and zeroed rows for the gradients that the global-token work adds to;
-//   * band kernel: 4-wave workgroups over tiles of 128 consecutive rows of
-//     one residue class of one head (a dilated window is a plain window over
-//     its residue class: segmentfault summary, "Dilated sliding window").
-//     A dq workgroup owns 128 query rows (wave w: 32 of them) and streams the
-//     key blocks of its window span and then the batch row's global tokens
-//     through LDS; a dk/dv workgroup owns 128 key rows and streams the query
-//     blocks whose windows reach them, with their lse and D.  Each staged
-//     block is read by all four waves; every gradient row has one owner, and
-//     S and dP are formed once per (block, wave) in each of the two roles;
-//   * global-token kernel (only with global work): single-wave units that
-//     add the local rows' dk, dv of global tokens and the global rows' dq_g
-//     (fp32 atomics onto zeroed rows), and write dk_g, dv_g:
+// Two launches:
+//   * preparation: the global token list of each batch row, -D_i and
+//     -lse_i / scale per row, and zeroed rows for the gradients that the
+//     global-token work adds to;
+//   * gradient launch: 4-wave band workgroups over tiles of 128 consecutive
+//     rows of one residue class of one head (a dilated window is a plain
+//     window over its residue class: segmentfault summary, "Dilated sliding
+//     window").  A dq workgroup owns 128 query rows (wave w: 32 of them) and
+//     streams the key blocks of its window span and then the batch row's
+//     global tokens through LDS; a dk/dv workgroup owns 128 key rows and
+//     streams the query blocks whose windows reach them, with their
+//     statistics.  Each staged block is read by all four waves; every
+//     gradient row has one owner, and S and dP are formed once per (block,
+//     wave) in each of the two roles.  After the band workgroups, in the
+//     same grid, the global-token work (only with global tokens) runs as
+//     single-wave units, four per workgroup, adding the local rows' dk, dv of
+//     global tokens and the global rows' dq_g (fp32 atomics onto rows the
+//     preparation zeroed), and writing dk_g, dv_g:
 //       GKV: one wave per 32 tokens; walks the global rows; writes dk_g, dv_g.
-//       GQ:  one wave per 32 global rows and 512 keys; adds to dq_g.
-//       GK:  one wave per 32 global tokens and 512 rows; adds to dk, dv.
+//       GQ:  one wave per 32 global rows and 128 keys; adds to dq_g.
+//       GK:  one wave per 32 global tokens and 128 rows; adds to dk, dv.
 // Block products are 32x32x16 MFMA chains; the transposed operands come from
 // staged rows through ds_read_b64_tr_b16.
 #include <hip/hip_runtime.h>
@@ -373,7 +376,7 @@ __device__ void bwd_global_unit(const BwdParams& p, BwdShared& sh, int bid) {
   }
   bid -= p.n_gkv;
 
-  // GQ and GK: (b, h, block of 32 global slots, 512-token chunk)
+  // GQ and GK: (b, h, block of 32 global slots, kBwdChunk-token chunk)
   const bool gq = bid < p.n_gq;
   if (!gq) bid -= p.n_gq;
   const int per_bh = p.gslots * p.chunks;
