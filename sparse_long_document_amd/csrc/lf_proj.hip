@@ -11,11 +11,12 @@
 // contiguous along the reduction, the operand layout of the 32x32x16 MFMA
 // for its A (a row of w) and B (a row of x) inputs.
 //
-// Tiles of BM tokens x BN features, one per workgroup, in one of three
+// Tiles of BM tokens x BN features, one per workgroup, in one of four
 // configurations chosen per launch (the one whose busiest CU has the least
 // work, tiles weighted by the bytes they stage per MFMA): 128 x 128 and
 // 128 x 192 with four waves (two workgroups per CU), 256 x 288 with eight
-// waves of 32 x 288 (one workgroup per CU).  Each wave holds its share of
+// waves of 32 x 288 and 256 x 256 with eight waves of 128 x 64 (one
+// workgroup per CU).  Each wave holds its share of
 // the tile as 32 x 32 fp32 accumulators.  The reduction runs in steps of 64
 // (one 128-byte line of every row) through two LDS stages: each step's
 // rows are loaded into registers a step ahead (16 bytes per lane, whole
@@ -79,10 +80,15 @@ struct Tile {
 };
 // 128 x 192 and 128 x 128 for launches with few tiles (two workgroups per
 // CU); 256 x 288 (eight waves of 32 x 288, one workgroup per CU) for large
-// ones: 40 % fewer bytes staged per MFMA than 128 x 192.
+// ones: 40 % fewer bytes staged per MFMA than 128 x 192.  256 x 256 with
+// eight waves of 128 x 64 reads a third fewer fragment bytes from LDS per
+// MFMA than 256 x 288 (six 1 KB reads per eight MFMAs against ten per
+// nine); the chooser takes it where it needs no more rounds of tiles than
+// 256 x 288 (feature counts that are multiples of 256).
 using TileS = Tile<128, 128, 2, 2>;
 using TileM = Tile<128, 192, 2, 2>;
 using TileL = Tile<256, 288, 8, 1>;
+using TileX = Tile<256, 256, 2, 4>;
 
 template <class T>
 __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
@@ -324,6 +330,7 @@ __device__ void proj_body(const ProjParams& p) {
 LF_PROJ_KERNELS(lf_proj_s, TileS)
 LF_PROJ_KERNELS(lf_proj_m, TileM)
 LF_PROJ_KERNELS(lf_proj_l, TileL)
+LF_PROJ_KERNELS(lf_proj_x, TileX)
 #undef LF_PROJ_KERNELS
 
 template <class Ly>
@@ -347,6 +354,8 @@ double cost_of(int M, int N, int cus) {
 
 int proj_tile_config(int M, int N, int cus) {
   const double cs = cost_of<TileS>(M, N, cus), cm = cost_of<TileM>(M, N, cus), cl = cost_of<TileL>(M, N, cus);
+  const double cx = cost_of<TileX>(M, N, cus);
+  if (cx < cl && cx <= cm && cx <= cs) return 3;
   if (cl <= cm && cl <= cs) return 2;
   return cm <= cs ? 1 : 0;
 }
@@ -370,6 +379,10 @@ int launch_project(const ProjParams& pp, void* stream) {
     case 1:
       hipLaunchKernelGGL(f16 ? lf_proj_m_f16 : lf_proj_m_bf16, dim3((unsigned)tiles_of<TileM>(pp.M, pp.N)),
                          dim3(TileM::kThreads), 0, s, pp);
+      break;
+    case 3:
+      hipLaunchKernelGGL(f16 ? lf_proj_x_f16 : lf_proj_x_bf16, dim3((unsigned)tiles_of<TileX>(pp.M, pp.N)),
+                         dim3(TileX::kThreads), 0, s, pp);
       break;
     default:
       hipLaunchKernelGGL(f16 ? lf_proj_l_f16 : lf_proj_l_bf16, dim3((unsigned)tiles_of<TileL>(pp.M, pp.N)),

@@ -28,7 +28,7 @@ int launch_project(const ProjParams& pp, void* stream);
 
 // Tile configuration the launch uses for M tokens and N stacked features on
 // a device with `cus` compute units: 0 = 128 x 128, 1 = 128 x 192,
-// 2 = 256 x 288 (tokens x features).
+// 2 = 256 x 288, 3 = 256 x 256 (tokens x features).
 int proj_tile_config(int M, int N, int cus);
 
 }  // namespace lf

@@ -56,14 +56,16 @@ def test_projection_small(M, C, P, dtype):
 
 @pytest.mark.parametrize("M,C,P,dtype", [(2000, 192, 1, torch.bfloat16), (2333, 448, 6, torch.bfloat16),
                                           (2000, 448, 5, torch.bfloat16), (2000, 448, 5, torch.float16),
-                                          (4000, 704, 6, torch.bfloat16), (4000, 704, 6, torch.float16)],
-                         ids=["s-a", "s-b", "m", "m-f16", "l", "l-f16"])
+                                          (4000, 704, 6, torch.bfloat16), (4000, 704, 6, torch.float16),
+                                          (6000, 1024, 2, torch.bfloat16), (7000, 960, 2, torch.bfloat16),
+                                          (7000, 960, 2, torch.float16)],
+                         ids=["s-a", "s-b", "m", "m-f16", "l", "l-f16", "x", "x-ragged", "x-f16"])
 def test_projection_tile_configs(M, C, P, dtype):
     """Each tile configuration of the launch (on a 256-CU device the
     chooser takes 128 x 128 tiles for the first two sizes, 128 x 192 for the
-    next two and 256 x 288 for the last two), with token counts that are
-    not multiples of the token tile and feature counts that are not
-    multiples of the feature tile."""
+    next two, 256 x 288 for the two after and 256 x 256 for the last three),
+    with token counts that are not multiples of the token tile and feature
+    counts that are not multiples of the feature tile."""
     check(31 + M + C, M, C, P, dtype)
 
 
@@ -106,8 +108,8 @@ def _mask(rng, M, n_global, others=True):
 
 @pytest.mark.parametrize("M,C,P,bits,n_global", [(300, 128, 6, (3,), 5), (2000, 448, 5, (3, 4), 9),
                                                  (4000, 704, 6, (3,), 17), (4096, 768, 6, (3,), 1),
-                                                 (2333, 448, 6, (3,), 0)],
-                         ids=["s", "m-two", "l", "longformer-base", "no-global"])
+                                                 (2333, 448, 6, (3,), 0), (7000, 960, 2, (1,), 13)],
+                         ids=["s", "m-two", "l", "longformer-base", "no-global", "x"])
 def test_projection_global_only(M, C, P, bits, n_global):
     rng = np.random.default_rng(M + C)
     check_global_only(41 + M, M, C, P, torch.bfloat16, bits, _mask(rng, M, n_global))
