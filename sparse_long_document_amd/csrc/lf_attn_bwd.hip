@@ -750,16 +750,24 @@ __device__ __forceinline__ BandTile decode_band(const BwdParams& p, int tile) {
 // i only block i's loads must have landed: block i + 1's, issued after
 // them, may still fly.  prologue() makes the role's own loads; refill(i0)
 // fills the validity table for blocks i0 .. i0 + kBandTab - 1 (every wave,
-// at a barrier).  step(i, stage) uses block i.
-template <int kLoads, class Issue, class Prologue, class Refill, class Step>
-__device__ __forceinline__ void band_loop(int nblk, int pre, Issue issue, Prologue prologue, Refill refill,
-                                          Step step) {
+// at a barrier).  step(i, stage) uses block i.  gate(), after the first
+// refill, decides for the whole workgroup whether the loop runs at all
+// (false: the loads in flight are waited for and the loop is skipped), so
+// that the loads the decision needs fly with all the others.  Returns
+// gate()'s answer.
+template <int kLoads, class Issue, class Prologue, class Refill, class Gate, class Step>
+__device__ __forceinline__ bool band_loop(int nblk, int pre, Issue issue, Prologue prologue, Refill refill,
+                                          Gate gate, Step step) {
   // the first two blocks' loads (those that need no table: pre of them)
   // fly while the prologue's own loads and the table's mask bytes load
   const int early = min(min(pre, nblk), 2);
   for (int i = 0; i < early; ++i) issue(i, i);
   prologue();
   refill(0);
+  if (!gate()) {
+    wait_vmem_all();  // no direct-to-LDS load may outlive the workgroup
+    return false;
+  }
   for (int i = early; i < min(nblk, 2); ++i) issue(i, i);
   wait_vmem_all();  // so that no wait for the prologue's loads lands inside the loop
   int stage = 0;
@@ -776,6 +784,7 @@ __device__ __forceinline__ void band_loop(int nblk, int pre, Issue issue, Prolog
     stage = stage == 2 ? 0 : stage + 1;
   }
   wait_vmem_all();
+  return true;
 }
 
 // dq workgroup.  Wave wv owns query rows t0 + 32 wv + lane % 32 (Q and dO
@@ -801,20 +810,15 @@ __device__ void band_dq(const BwdParams& p, BandShared& sh, const BandTile& bt, 
   const int tq = bt.t0 + 32 * wv + c;
   const bool qin = tq < bt.len;
   const int qpos = bt.r + d * (qin ? tq : bt.len - 1);
-  const int qty = qin ? eff_mask(mb[qpos], ug) : 0;
-  const bool qloc = qty == 1;
-  // every wave takes every block; a tile with no local row only writes zeros
-  if (!__syncthreads_or(qloc)) {
-    if (qin) {
-      const float z[4] = {0.f, 0.f, 0.f, 0.f};
-      float* dst = p.dq + boff + (size_t)qpos * rs;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) store_f4(dst + 8 * q + 4 * hl, z);
-    }
-    return;
-  }
-  const float lse2 = qloc ? -p.c * p.lneg[bh * n + qpos] : 0.f;  // lse in base 2
-  const float dd = qloc ? -p.dneg[bh * n + qpos] : 0.f;
+  // the row's mask byte, statistics and the batch row's global count load
+  // together (qpos is a valid row in every case); the validity test waits
+  // for the block loop's first loads as well
+  const int8_t mq = mb[qpos];
+  const float lneg_q = p.lneg[bh * n + qpos], dneg_q = p.dneg[bh * n + qpos];
+  const int nG = ug ? p.gcount[bt.b] : 0;
+  int qty = 0;
+  bool qloc = false;
+  float lse2 = 0.f, dd = 0.f;  // lse in base 2, and D
   e16x8 qf[4], df[4];
 
   const int kbase = bt.t0 - w;
@@ -822,13 +826,11 @@ __device__ void band_dq(const BwdParams& p, BandShared& sh, const BandTile& bt, 
   const int jlo = kbase >= 0 ? 0 : (-kbase) / 32;
   const int jhi = min(S, (bt.len - kbase + 31) / 32);
   const int nwin = max(jhi - jlo, 0);
-  const int nG = ug ? p.gcount[bt.b] : 0;
   const int32_t* gl = p.glist + (size_t)bt.b * p.gstride;
   const int nblk = nwin + (nG + 31) / 32;
   // token position of key row `row` of block i (a valid row in every case)
   // the global list in LDS (read in asm: no vector-memory instruction in
   // the block loop but its direct-to-LDS loads)
-  for (int g = threadIdx.x; g < nG; g += 256) sh.gpos[g] = gl[g];
   auto kpos = [&](int i, int row) -> int {
     if (i < nwin) {
       const int kk = kbase + 32 * (jlo + i) + row;
@@ -844,9 +846,32 @@ __device__ void band_dq(const BwdParams& p, BandShared& sh, const BandTile& bt, 
     const int kk = kbase + 32 * (jlo + i) + row;
     return kk >= 0 && kk < bt.len && eff_mask((int8_t)m, ug) != 0;
   };
+  // the first refill also puts the global list in LDS: its loads fly with
+  // the table's, its stores follow the table's barrier and get their own
+  static_assert(LF_MAX_GLOBAL <= 4 * 256, "four list entries per thread");
   auto refill = [&](int i0) {
+    int gv[4] = {0, 0, 0, 0};
+    if (i0 == 0)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if ((int)threadIdx.x + 256 * k < nG) gv[k] = gl[threadIdx.x + 256 * k];
     if (i0 < nwin) tab_fill(sh, mb, i0, nwin, wv, lane, kpos, key_ok);
-    else __syncthreads();  // the global list is in LDS
+    if (i0 == 0 && nG > 0) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if ((int)threadIdx.x + 256 * k < nG) sh.gpos[threadIdx.x + 256 * k] = gv[k];
+      __syncthreads();
+    } else if (i0 >= nwin) {
+      __syncthreads();
+    }
+  };
+  // every wave takes every block; a tile with no local row only writes zeros
+  auto gate = [&]() {
+    qty = qin ? eff_mask(mq, ug) : 0;
+    qloc = qty == 1;
+    lse2 = qloc ? -p.c * lneg_q : 0.f;
+    dd = qloc ? -dneg_q : 0.f;
+    return __syncthreads_or(qloc) != 0;
   };
   f32x16 acc[2] = {zero16(), zero16()};
   auto issue = [&](int i, int stg) {
@@ -922,7 +947,7 @@ __device__ void band_dq(const BwdParams& p, BandShared& sh, const BandTile& bt, 
     load_frag(qf, Q + (size_t)qpos * rs, true, hl);
     load_frag(df, DO + (size_t)qpos * rs, true, hl);
   };
-  band_loop<2>(nblk, nwin, issue, prologue, refill, step);
+  band_loop<2>(nblk, nwin, issue, prologue, refill, gate, step);
   if (qin) {
     float* dst = p.dq + boff + (size_t)qpos * rs;
     const float sc = p.scale;
@@ -964,8 +989,11 @@ __device__ void band_dkv(const BwdParams& p, BandShared& sh, const BandTile& bt,
   const int tk = bt.t0 + 32 * wv + c;
   const bool kin = tk < bt.len;
   const int kp = bt.r + d * (kin ? tk : bt.len - 1);
-  const int kty = kin ? eff_mask(mb[kp], ug) : 0;
-  const bool kok = kty == 1;
+  // the key's mask byte loads with the block loop's first loads (kp is a
+  // valid row in every case)
+  const int8_t mk = mb[kp];
+  int kty = 0;
+  bool kok = false, all_keys = false;
   f32x16 ak[2] = {zero16(), zero16()}, av[2] = {zero16(), zero16()};
   auto write_out = [&]() {
     if (!kin || kty == 2) return;
@@ -985,10 +1013,6 @@ __device__ void band_dkv(const BwdParams& p, BandShared& sh, const BandTile& bt,
         store_f4(dv + 32 * db + 8 * g + 4 * hl, v4);
       }
   };
-  if (!__syncthreads_or(kok)) {
-    write_out();
-    return;
-  }
   e16x8 kf[4], vf[4];
 
   // rows whose windows reach the tile's keys: tq in [tk - w_hi, tk + w]
@@ -1005,7 +1029,6 @@ __device__ void band_dkv(const BwdParams& p, BandShared& sh, const BandTile& bt,
   const BandAddr ad = band_addr(sh.ring, lane);
   const uint32_t sa = lds_addr(sh.ring + 2 * kBlkB) + 16u * (uint32_t)hl;
   const int k0w = bt.t0 + 32 * wv;  // the wave's first key row
-  const bool all_keys = __all(kok);
   // query rows that exist and are local (mask 1)
   auto row_ok = [&](int j, int row, int m) {
     const int t = qrow0(j) + row;
@@ -1092,7 +1115,14 @@ __device__ void band_dkv(const BwdParams& p, BandShared& sh, const BandTile& bt,
     load_frag(kf, K + (size_t)kp * rs, true, hl);
     load_frag(vf, V + (size_t)kp * rs, true, hl);
   };
-  band_loop<3>(nq, nq, issue, prologue, refill, step);
+  // a tile with no key of mask 1 only writes zeros
+  auto gate = [&]() {
+    kty = kin ? eff_mask(mk, ug) : 0;
+    kok = kty == 1;
+    all_keys = __all(kok);
+    return __syncthreads_or(kok) != 0;
+  };
+  band_loop<3>(nq, nq, issue, prologue, refill, gate, step);
   write_out();
 }
 
