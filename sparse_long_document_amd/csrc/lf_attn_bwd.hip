@@ -324,32 +324,6 @@ __device__ __forceinline__ void store_f4(float* dst, const float* v) {
 
 // Work on the global tokens: unit `bid` of the single-wave units (GKV,
 // then GQ and GK), run by one wave with its own staging area sh.
-// Global-token unit u, in (b, h)-major order and, within a (b, h), by
-// kBwdChunk-token chunk: the chunk's GKV key blocks, then its GQ units (one
-// per 32 global slots), then its GK units, so that the units of a chunk
-// run near the band workgroups of the same tokens and find their rows in
-// L2.  role: 0 GKV (key block kb), 1 GQ and 2 GK (slot block sb, chunk ch).
-struct GlobalUnit {
-  int role, bh, kb, sb, ch;
-};
-__device__ __forceinline__ GlobalUnit decode_global(const BwdParams& p, int u) {
-  constexpr int kpc = kBwdChunk / 32;  // key blocks per chunk
-  const int kbn = (p.n + 31) / 32;
-  const int per_bh = kbn + 2 * p.gslots * p.chunks;
-  GlobalUnit g;
-  g.bh = u / per_bh;
-  const int r = u - g.bh * per_bh;
-  const int U = kpc + 2 * p.gslots;  // units of a whole chunk
-  const int full = (p.chunks - 1) * U;
-  g.ch = r < full ? r / U : p.chunks - 1;
-  const int q = r < full ? r - g.ch * U : r - full;
-  const int nkb = min(kpc, kbn - kpc * g.ch);
-  g.kb = kpc * g.ch + q;
-  g.role = q < nkb ? 0 : (q < nkb + p.gslots ? 1 : 2);
-  g.sb = g.role == 1 ? q - nkb : q - nkb - p.gslots;
-  return g;
-}
-
 __device__ void bwd_global_unit(const BwdParams& p, BwdShared& sh, int bid) {
   const int lane = threadIdx.x & 63, c = lane & 31, hl = lane >> 5;
   const int n = p.n;
@@ -362,10 +336,11 @@ __device__ void bwd_global_unit(const BwdParams& p, BwdShared& sh, int bid) {
   const e16* VG = reinterpret_cast<const e16*>(p.vg);
   const e16* DO = reinterpret_cast<const e16*>(p.dout);
 
-  const GlobalUnit gu = decode_global(p, bid);
-  if (gu.role == 0) {
-    const int bh = gu.bh;
-    const int kb0 = gu.kb * 32;
+  // global roles: GKV (key blocks of every (b, h)), then GQ and GK
+  if (bid < p.n_gkv) {
+    const int kblocks = (n + 31) / 32;
+    const int bh = bid / kblocks;
+    const int kb0 = (bid - bh * kblocks) * 32;
     const int b = bh / p.H, h = bh - b * p.H;
     const size_t boff = (size_t)b * n * rs + (size_t)h * 64;
     const int8_t* mb = p.mask + (size_t)b * n;
@@ -399,10 +374,16 @@ __device__ void bwd_global_unit(const BwdParams& p, BwdShared& sh, int bid) {
     }
     return;
   }
+  bid -= p.n_gkv;
 
   // GQ and GK: (b, h, block of 32 global slots, kBwdChunk-token chunk)
-  const bool gq = gu.role == 1;
-  const int bh = gu.bh, sb = gu.sb, ch = gu.ch;
+  const bool gq = bid < p.n_gq;
+  if (!gq) bid -= p.n_gq;
+  const int per_bh = p.gslots * p.chunks;
+  const int bh = bid / per_bh;
+  const int rem = bid - bh * per_bh;
+  const int sb = rem / p.chunks;
+  const int ch = rem - sb * p.chunks;
   const int b = bh / p.H, h = bh - b * p.H;
   const int nG = p.gcount[b];
   if (32 * sb >= nG) return;
@@ -1145,39 +1126,30 @@ __device__ void band_dkv(const BwdParams& p, BandShared& sh, const BandTile& bt,
   write_out();
 }
 
-// Workgroups of the gradient launch: the band units (a tile's dq and dk/dv
-// workgroups next to each other, tiles in (b, h) order) and the global
-// workgroups (four global units each, also in (b, h) order).  Workgroup x
-// runs on XCD x % 8.  Each XCD is dealt a contiguous range of band units
-// (neighbouring tiles share their window rows, which then stay in that
-// XCD's L2) and, after them, the matching range of global workgroups (the
-// same share of each list), whose rows are those of the XCD's own heads.
+// Units of the band launch: unit x runs on XCD x % 8; each XCD is dealt a
+// contiguous range of units (neighbouring tiles share their window rows,
+// which then stay in that XCD's L2), and a tile's dq and dk/dv units are
+// neighbours.
 __device__ void bwd_band_body(const BwdParams& p) {
   __shared__ union {
     BandShared band;
     BwdShared unit[4];
   } shu;
   const int N = 2 * p.n_bt;
-  const int nglob = p.n_gkv + p.n_gq + p.n_gk;
-  const int NG = (nglob + 3) / 4;
-  const int T = N + NG;
   const int x = blockIdx.x;
-  const int per = T / 8, rem = T % 8;
-  const int xcd = x % 8, y = x / 8;
-  // workgroups dealt to XCDs before this one, and to this one
-  const int c0 = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
-  const int c1 = c0 + per + (xcd < rem ? 1 : 0);
-  // the XCD's band units are [b0, b1), its global workgroups the rest
-  const int b0 = (int)(((long long)c0 * N) / T), b1 = (int)(((long long)c1 * N) / T);
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (y >= b1 - b0) {
-    // global workgroup (c0 - b0) + (y - (b1 - b0)): four global units, one per wave
-    const int unit = 4 * (c0 - b0 + y - (b1 - b0)) + wv;
-    if (unit < nglob) bwd_global_unit(p, shu.unit[wv], unit);
+  if (x >= N) {
+    // the global-token units, four per workgroup (one per wave), after the
+    // band tiles: they fill the slots the last band tiles leave free
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int unit = 4 * (x - N) + wv;
+    if (unit < p.n_gkv + p.n_gq + p.n_gk) bwd_global_unit(p, shu.unit[wv], unit);
     return;
   }
   BandShared& sh = shu.band;
-  const int m = b0 + y;
+  const int per = N / 8, rem = N % 8;
+  const int xcd = x % 8, y = x / 8;
+  const int m = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + y;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const BandTile bt = decode_band(p, m >> 1);
   if (bt.t0 >= bt.len) return;  // every wave of the workgroup returns here
   if (m & 1)
