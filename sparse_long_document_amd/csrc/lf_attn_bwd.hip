@@ -34,7 +34,13 @@
 //       GQ:  one wave per 32 global rows and 128 keys; adds to dq_g.
 //       GK:  one wave per 32 global tokens and 128 rows; adds to dk, dv.
 // Block products are 32x32x16 MFMA chains; the transposed operands come from
-// staged rows through ds_read_b64_tr_b16.
+// staged rows through ds_read_b64_tr_b16.  The gradient launch runs three
+// waves per SIMD (at most 168 VGPRs), so that a CU holds three band
+// workgroups: both band roles read a staged block one tensor at a time, the
+// dk/dv role keeps its K and V fragments in LDS rather than in registers,
+// the staged blocks go through two LDS stages (block i + 1 loads while
+// block i is used), and the global-token units load each block when they
+// use it.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -166,27 +172,18 @@ __device__ void q_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16*
   load_frag(df, dob + (size_t)(qty ? qpos : 0) * rs, qty != 0, hl);
   acc[0] = zero16();
   acc[1] = zero16();
-  int kpos = -1, kt = 0, kcode = 0;
-  e16x8 kf[4], vf[4];
-  if (nblk > 0) {
-    keyof(0, c, kpos, kt, kcode);
+  for (int j = 0; j < nblk; ++j) {
+    int kpos = -1, kt = 0, kcode = 0;
+    keyof(j, c, kpos, kt, kcode);
+    e16x8 kf[4], vf[4];
     load_frag(kf, kb + (size_t)(kpos >= 0 ? kpos : 0) * rs, kpos >= 0, hl);
     load_frag(vf, vb + (size_t)(kpos >= 0 ? kpos : 0) * rs, kpos >= 0, hl);
-  }
-  for (int j = 0; j < nblk; ++j) {
     const int kty = slot_type(kpos, kcode, p.use_globals);
     keep_frag(kf, kty != 0);
     keep_frag(vf, kty != 0);
     if (hl == 0) sh.info[c] = make_int4(kpos, kt, kty, 0);
     stage_frag(sh, 0, c, hl, kf);
     wave_lds_sync();
-    // the next block's rows fly during this block's products: their loads
-    // depend on positions only, not on the mask bytes loaded beside them
-    int npos = -1, nt = 0, ncode = 0;
-    if (j + 1 < nblk) keyof(j + 1, c, npos, nt, ncode);
-    e16x8 nkf[4], nvf[4];
-    load_frag(nkf, kb + (size_t)(npos >= 0 ? npos : 0) * rs, npos >= 0, hl);
-    load_frag(nvf, vb + (size_t)(npos >= 0 ? npos : 0) * rs, npos >= 0, hl);
     f32x16 S = zero16(), dP = zero16();
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -214,14 +211,6 @@ __device__ void q_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16*
 #pragma unroll
       for (int t = 0; t < 2; ++t) acc[half] = mma(col_frag(sh, 0, t, lane, half), ds8[t], acc[half]);
     wave_lds_sync();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      kf[s] = nkf[s];
-      vf[s] = nvf[s];
-    }
-    kpos = npos;
-    kt = nt;
-    kcode = ncode;
   }
 }
 
@@ -240,9 +229,6 @@ __device__ void kv_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16
   load_frag(kf, kb + (size_t)(kty ? kpos : 0) * rs, kty != 0, hl);
   load_frag(vf, vb + (size_t)(kty ? kpos : 0) * rs, kty != 0, hl);
   acc_k[0] = acc_k[1] = acc_v[0] = acc_v[1] = zero16();
-  int qpos = -1, qt = 0, qcode = 0;
-  float ql = 0.f, qd = 0.f;
-  e16x8 qf[4], df[4];
   auto fetch = [&](int j, int& pos, int& tt, int& code, float& l2, float& dd, e16x8 (&a)[4], e16x8 (&b)[4]) {
     pos = -1;
     tt = 0;
@@ -254,8 +240,11 @@ __device__ void kv_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16
     load_frag(a, qb + (size_t)(pos >= 0 ? pos : 0) * rs, pos >= 0, hl);
     load_frag(b, dob + (size_t)(pos >= 0 ? pos : 0) * rs, pos >= 0, hl);
   };
-  if (nblk > 0) fetch(0, qpos, qt, qcode, ql, qd, qf, df);
   for (int j = 0; j < nblk; ++j) {
+    int qpos = -1, qt = 0, qcode = 0;
+    float ql = 0.f, qd = 0.f;
+    e16x8 qf[4], df[4];
+    fetch(j, qpos, qt, qcode, ql, qd, qf, df);
     const int qty = slot_type(qpos, qcode, p.use_globals);
     keep_frag(qf, qty != 0);
     keep_frag(df, qty != 0);
@@ -266,16 +255,13 @@ __device__ void kv_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16
     stage_frag(sh, 0, c, hl, qf);
     stage_frag(sh, 1, c, hl, df);
     wave_lds_sync();
-    int npos, nt, ncode;
-    float nl, nd;
-    e16x8 nqf[4], ndf[4];
-    fetch(j + 1, npos, nt, ncode, nl, nd, nqf, ndf);
+    // the staged rows are read back as the products' row operands, so that
+    // the fragments need not stay in registers
     f32x16 S = zero16(), dP = zero16();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      S = mma(qf[s], kf[s], S);
-      dP = mma(df[s], vf[s], dP);
-    }
+    for (int s = 0; s < 4; ++s) S = mma(*reinterpret_cast<const e16x8*>(&sh.st[0][c][16 * s + 8 * hl]), kf[s], S);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dP = mma(*reinterpret_cast<const e16x8*>(&sh.st[1][c][16 * s + 8 * hl]), vf[s], dP);
     e16x8 p8[2], ds8[2];
     if (keys_ok && geom(j) && __all(qty == want_q)) {
 #pragma unroll
@@ -305,16 +291,6 @@ __device__ void kv_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16
         acc_k[half] = mma(ds8[t], col_frag(sh, 0, t, lane, half), acc_k[half]);
       }
     wave_lds_sync();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      qf[s] = nqf[s];
-      df[s] = ndf[s];
-    }
-    qpos = npos;
-    qt = nt;
-    qcode = ncode;
-    ql = nl;
-    qd = nd;
   }
 }
 
@@ -452,7 +428,7 @@ constexpr int kRowB = 128;                   // staged row: 64 head dims of 16 b
 constexpr int kBlkB = 32 * kRowB;            // one 32-row block of one tensor
 constexpr int kStatB = 256;                  // dk/dv role: -lse / scale then -D of the block's 32 rows
 constexpr int kStageB = 2 * kBlkB + kStatB;  // two tensors and the row statistics
-constexpr int kBandStages = 3;               // blocks i + 1 and i + 2 fly while block i is used
+constexpr int kBandStages = 2;               // block i + 1 flies while block i is used
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(LDS_AS const void*)p; }
 
@@ -461,7 +437,15 @@ constexpr int kBandTab = 64;                 // blocks whose row validity is tab
 struct BandShared {
   __attribute__((aligned(16))) unsigned char ring[kBandStages * kStageB];
   uint32_t tab[kBandTab];     // row-validity bits of blocks i0 .. i0 + kBandTab - 1 (entry i % kBandTab)
-  int32_t gpos[LF_MAX_GLOBAL];  // dq role: the batch row's global positions
+  union {
+    int32_t gpos[LF_MAX_GLOBAL];  // dq role: the batch row's global positions
+    // dk/dv role: each wave's K and V fragments, [wave][fragment s][lane]
+    // 16 bytes each
+    struct {
+      __attribute__((aligned(16))) unsigned char kfr[4 * 4 * 64 * 16];
+      __attribute__((aligned(16))) unsigned char vfr[4 * 4 * 64 * 16];
+    };
+  };
 };
 
 // A 32-bit LDS word read in an asm block that waits for its own read (see
@@ -503,13 +487,6 @@ __device__ __forceinline__ int bswz(int r) {
 }
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// at most N vector-memory instructions of this wave outstanding (they
-// complete in issue order)
-template <int N>
-__device__ __forceinline__ void wait_vmem_but() {
-  static_assert(N >= 0 && N < 16, "small counts");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 
@@ -567,123 +544,89 @@ __device__ __forceinline__ e16x8 join8(u32x2 lo, u32x2 hi) {
   return __builtin_bit_cast(e16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
-// The reads of one staged block (kOff: the stage's byte offset), in asm
-// blocks that wait for their own reads: the compiler cannot tell them from
-// the direct-to-LDS loads still in flight into the other stages and would
-// otherwise wait for those first.
-//   dq role:  rows of tensor 0 (K) and 1 (V), transposed tensor 0 (K^T).
-template <int kOff>
-__device__ __forceinline__ void read_dq(e16x8 (&kf)[4], e16x8 (&vf)[4], e16x8 (&kt)[2][2], const BandAddr& a) {
-  u32x4 k[4], v[4];
+// The reads of one staged block, one tensor per asm block (so that few
+// registers are live at once), each asm block waiting for its own reads:
+// the compiler cannot tell them from the direct-to-LDS loads still in
+// flight into the other stage and would otherwise wait for those first.
+// so is the stage's byte offset in the ring, added to the fragment
+// addresses computed once (BandAddr).
+//   read_rows4<kT>: the rows of tensor kT (0 or 1 of the stage).
+template <int kT>
+__device__ __forceinline__ void read_rows4(e16x8 (&f)[4], const BandAddr& a, uint32_t so) {
+  u32x4 q[4];
+  const uint32_t r0 = a.ro[0] + so, r1 = a.ro[1] + so, r2 = a.ro[2] + so, r3 = a.ro[3] + so;
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%8\n"
+      "ds_read_b128 %1, %5 offset:%8\n"
+      "ds_read_b128 %2, %6 offset:%8\n"
+      "ds_read_b128 %3, %7 offset:%8\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3])
+      : "v"(r0), "v"(r1), "v"(r2), "v"(r3), "i"(kT * kBlkB)
+      : "memory");
+#pragma unroll
+  for (int s = 0; s < 4; ++s) f[s] = as8(q[s]);
+}
+
+//   read_rows_stats<kT> (dk/dv role): the rows of tensor kT (0: Q, 1: dO),
+//   their row statistics (this lane's 16 rows 8 g + 4 hl .. + 3: float4 g of
+//   -lse / scale for Q, of -D for dO, at sa) and the wave's K (kT = 0) or V
+//   (kT = 1) fragments from LDS at fb (fragment s at fb + 1024 s).
+template <int kT>
+__device__ __forceinline__ void read_rows_stats(e16x8 (&f)[4], f32x4 (&st)[4], e16x8 (&bf)[4], const BandAddr& a,
+                                                uint32_t sa, uint32_t fb, uint32_t so) {
+  u32x4 q[4], v[4];
+  const uint32_t r0 = a.ro[0] + so, r1 = a.ro[1] + so, r2 = a.ro[2] + so, r3 = a.ro[3] + so, s0 = sa + so;
+  asm volatile(
+      "ds_read_b128 %0, %12 offset:%18\n"
+      "ds_read_b128 %1, %13 offset:%18\n"
+      "ds_read_b128 %2, %14 offset:%18\n"
+      "ds_read_b128 %3, %15 offset:%18\n"
+      "ds_read_b128 %4, %16 offset:%19\n"
+      "ds_read_b128 %5, %16 offset:%20\n"
+      "ds_read_b128 %6, %16 offset:%21\n"
+      "ds_read_b128 %7, %16 offset:%22\n"
+      "ds_read_b128 %8, %17\n"
+      "ds_read_b128 %9, %17 offset:1024\n"
+      "ds_read_b128 %10, %17 offset:2048\n"
+      "ds_read_b128 %11, %17 offset:3072\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(st[0]), "=&v"(st[1]), "=&v"(st[2]), "=&v"(st[3]),
+        "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(r0), "v"(r1), "v"(r2), "v"(r3), "v"(s0), "v"(fb), "i"(kT * kBlkB), "i"(128 * kT),
+        "i"(128 * kT + 32), "i"(128 * kT + 64), "i"(128 * kT + 96)
+      : "memory");
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    f[s] = as8(q[s]);
+    bf[s] = as8(v[s]);
+  }
+}
+
+//   read_cols<kT>: tensor kT transposed (ds_read_b64_tr_b16): t8[db][ks]
+//   holds head dim 32 db + lane % 32 of the block's rows 16 ks + {4 hl ..
+//   4 hl + 3, 8 + 4 hl .. 8 + 4 hl + 3}.
+template <int kT>
+__device__ __forceinline__ void read_cols(e16x8 (&t8)[2][2], const BandAddr& a, uint32_t so) {
   u32x2 t[8];  // [db][ks][half]
+  const uint32_t c00 = a.co[0][0] + so, c01 = a.co[0][1] + so, c10 = a.co[1][0] + so, c11 = a.co[1][1] + so;
   asm volatile(
-      "ds_read_b128 %0, %16 offset:%24\n"
-      "ds_read_b128 %1, %17 offset:%24\n"
-      "ds_read_b128 %2, %18 offset:%24\n"
-      "ds_read_b128 %3, %19 offset:%24\n"
-      "ds_read_b128 %4, %16 offset:%25\n"
-      "ds_read_b128 %5, %17 offset:%25\n"
-      "ds_read_b128 %6, %18 offset:%25\n"
-      "ds_read_b128 %7, %19 offset:%25\n"
-      "ds_read_b64_tr_b16 %8, %20 offset:%24\n"
-      "ds_read_b64_tr_b16 %9, %21 offset:%24\n"
-      "ds_read_b64_tr_b16 %10, %20 offset:%26\n"
-      "ds_read_b64_tr_b16 %11, %21 offset:%26\n"
-      "ds_read_b64_tr_b16 %12, %22 offset:%24\n"
-      "ds_read_b64_tr_b16 %13, %23 offset:%24\n"
-      "ds_read_b64_tr_b16 %14, %22 offset:%26\n"
-      "ds_read_b64_tr_b16 %15, %23 offset:%26\n"
+      "ds_read_b64_tr_b16 %0, %8 offset:%12\n"
+      "ds_read_b64_tr_b16 %1, %9 offset:%12\n"
+      "ds_read_b64_tr_b16 %2, %8 offset:%13\n"
+      "ds_read_b64_tr_b16 %3, %9 offset:%13\n"
+      "ds_read_b64_tr_b16 %4, %10 offset:%12\n"
+      "ds_read_b64_tr_b16 %5, %11 offset:%12\n"
+      "ds_read_b64_tr_b16 %6, %10 offset:%13\n"
+      "ds_read_b64_tr_b16 %7, %11 offset:%13\n"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]),
-        "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
-      : "v"(a.ro[0]), "v"(a.ro[1]), "v"(a.ro[2]), "v"(a.ro[3]), "v"(a.co[0][0]), "v"(a.co[0][1]), "v"(a.co[1][0]),
-        "v"(a.co[1][1]), "i"(kOff), "i"(kOff + kBlkB), "i"(kOff + 2048)
-      : "memory");
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    kf[s] = as8(k[s]);
-    vf[s] = as8(v[s]);
-  }
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) kt[db][ks] = join8(t[4 * db + 2 * ks], t[4 * db + 2 * ks + 1]);
-}
-
-//   dk/dv role, in two asm blocks (fewer registers live at once): rows of
-//   tensor 0 (Q) and 1 (dO) with the row statistics (this lane's 16 rows
-//   8 g + 4 hl .. + 3: float4 g of -lse / scale, then of -D, at sa), then
-//   transposed tensor 0 (Q^T) and 1 (dO^T).
-template <int kOff>
-__device__ __forceinline__ void read_dkv_rows(e16x8 (&qf)[4], e16x8 (&df)[4], f32x4 (&ls)[4], f32x4 (&dd)[4],
-                                              const BandAddr& a, uint32_t sa) {
-  u32x4 q[4], d[4];
-  asm volatile(
-      "ds_read_b128 %0, %16 offset:%21\n"
-      "ds_read_b128 %1, %17 offset:%21\n"
-      "ds_read_b128 %2, %18 offset:%21\n"
-      "ds_read_b128 %3, %19 offset:%21\n"
-      "ds_read_b128 %4, %16 offset:%22\n"
-      "ds_read_b128 %5, %17 offset:%22\n"
-      "ds_read_b128 %6, %18 offset:%22\n"
-      "ds_read_b128 %7, %19 offset:%22\n"
-      "ds_read_b128 %8, %20 offset:%23\n"
-      "ds_read_b128 %9, %20 offset:%24\n"
-      "ds_read_b128 %10, %20 offset:%25\n"
-      "ds_read_b128 %11, %20 offset:%26\n"
-      "ds_read_b128 %12, %20 offset:%27\n"
-      "ds_read_b128 %13, %20 offset:%28\n"
-      "ds_read_b128 %14, %20 offset:%29\n"
-      "ds_read_b128 %15, %20 offset:%30\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]),
-        "=&v"(ls[0]), "=&v"(ls[1]), "=&v"(ls[2]), "=&v"(ls[3]), "=&v"(dd[0]), "=&v"(dd[1]), "=&v"(dd[2]),
-        "=&v"(dd[3])
-      : "v"(a.ro[0]), "v"(a.ro[1]), "v"(a.ro[2]), "v"(a.ro[3]), "v"(sa), "i"(kOff), "i"(kOff + kBlkB), "i"(kOff),
-        "i"(kOff + 32), "i"(kOff + 64), "i"(kOff + 96), "i"(kOff + 128), "i"(kOff + 160), "i"(kOff + 192),
-        "i"(kOff + 224)
-      : "memory");
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    qf[s] = as8(q[s]);
-    df[s] = as8(d[s]);
-  }
-}
-
-template <int kOff>
-__device__ __forceinline__ void read_dkv_cols(e16x8 (&qt)[2][2], e16x8 (&dt)[2][2], const BandAddr& a) {
-  u32x2 t[16];  // [tensor][db][ks][half]
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %16 offset:%20\n"
-      "ds_read_b64_tr_b16 %1, %17 offset:%20\n"
-      "ds_read_b64_tr_b16 %2, %16 offset:%22\n"
-      "ds_read_b64_tr_b16 %3, %17 offset:%22\n"
-      "ds_read_b64_tr_b16 %4, %18 offset:%20\n"
-      "ds_read_b64_tr_b16 %5, %19 offset:%20\n"
-      "ds_read_b64_tr_b16 %6, %18 offset:%22\n"
-      "ds_read_b64_tr_b16 %7, %19 offset:%22\n"
-      "ds_read_b64_tr_b16 %8, %16 offset:%21\n"
-      "ds_read_b64_tr_b16 %9, %17 offset:%21\n"
-      "ds_read_b64_tr_b16 %10, %16 offset:%23\n"
-      "ds_read_b64_tr_b16 %11, %17 offset:%23\n"
-      "ds_read_b64_tr_b16 %12, %18 offset:%21\n"
-      "ds_read_b64_tr_b16 %13, %19 offset:%21\n"
-      "ds_read_b64_tr_b16 %14, %18 offset:%23\n"
-      "ds_read_b64_tr_b16 %15, %19 offset:%23\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7]),
-        "=&v"(t[8]), "=&v"(t[9]), "=&v"(t[10]), "=&v"(t[11]), "=&v"(t[12]), "=&v"(t[13]), "=&v"(t[14]),
-        "=&v"(t[15])
-      : "v"(a.co[0][0]), "v"(a.co[0][1]), "v"(a.co[1][0]), "v"(a.co[1][1]), "i"(kOff), "i"(kOff + kBlkB),
-        "i"(kOff + 2048), "i"(kOff + kBlkB + 2048)
+      : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
+      : "v"(c00), "v"(c01), "v"(c10), "v"(c11), "i"(kT * kBlkB), "i"(kT * kBlkB + 2048)
       : "memory");
 #pragma unroll
   for (int db = 0; db < 2; ++db)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      qt[db][ks] = join8(t[4 * db + 2 * ks], t[4 * db + 2 * ks + 1]);
-      dt[db][ks] = join8(t[8 + 4 * db + 2 * ks], t[8 + 4 * db + 2 * ks + 1]);
-    }
+    for (int ks = 0; ks < 2; ++ks) t8[db][ks] = join8(t[4 * db + 2 * ks], t[4 * db + 2 * ks + 1]);
 }
 
 // Zero the entries of a transposed operand whose row is clear in vm (a row
@@ -744,23 +687,24 @@ __device__ __forceinline__ BandTile decode_band(const BwdParams& p, int tile) {
 }
 
 // The block loop shared by both roles: blocks i < nblk, block i staged in
-// stage i % 3.  Every wave runs every step (one barrier each) and issues,
-// after the barrier, the direct-to-LDS loads of block i + 2 (issue(i,
-// stage): exactly kLoads vector-memory instructions).  At the start of step
-// i only block i's loads must have landed: block i + 1's, issued after
-// them, may still fly.  prologue() makes the role's own loads; refill(i0)
+// stage i % 2.  Every wave runs every step (one barrier each): it waits for
+// its own loads of block i (the only ones in flight), and after the barrier
+// (all of block i is in LDS, every wave is done with block i - 1) issues
+// the direct-to-LDS loads of block i + 1 into block i - 1's stage (issue(i,
+// stage): its share of the block), which land during
+// step i.  prologue() makes the role's own loads; refill(i0)
 // fills the validity table for blocks i0 .. i0 + kBandTab - 1 (every wave,
 // at a barrier).  step(i, stage) uses block i.  gate(), after the first
 // refill, decides for the whole workgroup whether the loop runs at all
 // (false: the loads in flight are waited for and the loop is skipped), so
 // that the loads the decision needs fly with all the others.  Returns
 // gate()'s answer.
-template <int kLoads, class Issue, class Prologue, class Refill, class Gate, class Step>
+template <class Issue, class Prologue, class Refill, class Gate, class Step>
 __device__ __forceinline__ bool band_loop(int nblk, int pre, Issue issue, Prologue prologue, Refill refill,
                                           Gate gate, Step step) {
-  // the first two blocks' loads (those that need no table: pre of them)
-  // fly while the prologue's own loads and the table's mask bytes load
-  const int early = min(min(pre, nblk), 2);
+  // the first block's loads (if it needs no table: pre > 0) fly while the
+  // prologue's own loads and the table's mask bytes load
+  const int early = min(min(pre, nblk), 1);
   for (int i = 0; i < early; ++i) issue(i, i);
   prologue();
   refill(0);
@@ -768,20 +712,18 @@ __device__ __forceinline__ bool band_loop(int nblk, int pre, Issue issue, Prolog
     wait_vmem_all();  // no direct-to-LDS load may outlive the workgroup
     return false;
   }
-  for (int i = early; i < min(nblk, 2); ++i) issue(i, i);
+  for (int i = early; i < min(nblk, 1); ++i) issue(i, i);
   wait_vmem_all();  // so that no wait for the prologue's loads lands inside the loop
   int stage = 0;
   for (int i = 0; i < nblk; ++i) {
-    if (i + 1 < nblk)
-      wait_vmem_but<kLoads>();
-    else
-      wait_vmem_all();
+    wait_vmem_all();  // block i's loads (the only ones in flight)
     block_barrier();
-    // every wave is past step i - 1: the table may take the next blocks
+    // every wave is past step i - 1: the table may take the next blocks,
+    // and the stage of block i - 1 the loads of block i + 1
     if (i > 0 && i % kBandTab == 0) refill(i);
-    if (i + 2 < nblk) issue(i + 2, stage == 0 ? 2 : stage - 1);
+    if (i + 1 < nblk) issue(i + 1, stage ^ 1);
     step(i, stage);
-    stage = stage == 2 ? 0 : stage + 1;
+    stage ^= 1;
   }
   wait_vmem_all();
   return true;
@@ -889,18 +831,18 @@ __device__ void band_dq(const BwdParams& p, BandShared& sh, const BandTile& bt, 
       kval = (uint32_t)__ballot(32 * (i - nwin) + c < nG);
     }
     if (kval == 0u) return;
-    e16x8 kf[4], vf[4], kt[2][2];
-    if (stage == 0)
-      read_dq<0>(kf, vf, kt, ad);
-    else if (stage == 1)
-      read_dq<kStageB>(kf, vf, kt, ad);
-    else
-      read_dq<2 * kStageB>(kf, vf, kt, ad);
+    // one tensor at a time (few registers live at once): S^T from the K
+    // rows, dP^T from the V rows, then K^T for dQ^T
+    const uint32_t so = (uint32_t)(stage * kStageB);
     f32x16 sc = zero16(), dp = zero16();
+    {
+      e16x8 rf[4];
+      read_rows4<0>(rf, ad, so);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      sc = mma(kf[s], qf[s], sc);
-      dp = mma(vf[s], df[s], dp);
+      for (int s = 0; s < 4; ++s) sc = mma(rf[s], qf[s], sc);
+      read_rows4<1>(rf, ad, so);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dp = mma(rf[s], df[s], dp);
     }
     bool fast = false;
     uint32_t okb = 0;  // bit k: (this lane's query, key row k) is a scored pair
@@ -930,14 +872,17 @@ __device__ void band_dq(const BwdParams& p, BandShared& sh, const BandTile& bt, 
         ds8[r >> 3][r & 7] = (e16)(pr * (dp[r] - dd));
       }
     } else {
+      const uint32_t okh = okb >> (4 * hl);  // row acc_row(r, hl) is bit acc_row(r, 0)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const bool ok = (okb >> acc_row(r, hl)) & 1u;
+        const bool ok = (okh >> acc_row(r, 0)) & 1u;
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(p.c, sc[r], -lse2));
         ds8[r >> 3][r & 7] = (e16)(ok ? pr * (dp[r] - dd) : 0.f);
       }
-      if (kval != 0xffffffffu) zero_cols(kt, kval, hl);
     }
+    e16x8 kt[2][2];
+    read_cols<0>(kt, ad, so);  // K^T
+    if (!fast && kval != 0xffffffffu) zero_cols(kt, kval, hl);
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -947,7 +892,7 @@ __device__ void band_dq(const BwdParams& p, BandShared& sh, const BandTile& bt, 
     load_frag(qf, Q + (size_t)qpos * rs, true, hl);
     load_frag(df, DO + (size_t)qpos * rs, true, hl);
   };
-  band_loop<2>(nblk, nwin, issue, prologue, refill, gate, step);
+  band_loop(nblk, nwin, issue, prologue, refill, gate, step);
   if (qin) {
     float* dst = p.dq + boff + (size_t)qpos * rs;
     const float sc = p.scale;
@@ -964,7 +909,8 @@ __device__ void band_dq(const BwdParams& p, BandShared& sh, const BandTile& bt, 
 }
 
 // dk/dv workgroup.  Wave wv owns key rows t0 + 32 wv + lane % 32 (K and V
-// as B operands); the query blocks are the rows qbase + 32 (jlo + j) + row
+// as B operands, kept in LDS and read with each block); the query blocks
+// are the rows qbase + 32 (jlo + j) + row
 // whose windows reach the tile's keys, staged with their -lse / scale and
 // -D.  Per block: S = Q K^T, dP = dO V^T (lane: one key, 16 queries), P and
 // dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.  Keys with mask 2 are
@@ -994,7 +940,7 @@ __device__ void band_dkv(const BwdParams& p, BandShared& sh, const BandTile& bt,
   const int8_t mk = mb[kp];
   int kty = 0;
   bool kok = false, all_keys = false;
-  f32x16 ak[2] = {zero16(), zero16()}, av[2] = {zero16(), zero16()};
+  f32x16 ak[2], av[2];  // zeroed at the gate, after the prologue's registers are free
   auto write_out = [&]() {
     if (!kin || kty == 2) return;
     float* dk = p.dk + boff + (size_t)kp * rs;
@@ -1028,6 +974,8 @@ __device__ void band_dkv(const BwdParams& p, BandShared& sh, const BandTile& bt,
   };
   const BandAddr ad = band_addr(sh.ring, lane);
   const uint32_t sa = lds_addr(sh.ring + 2 * kBlkB) + 16u * (uint32_t)hl;
+  const uint32_t vb = lds_addr(sh.vfr) + 4096u * (uint32_t)wv + 16u * (uint32_t)lane;
+  const uint32_t kb = lds_addr(sh.kfr) + 4096u * (uint32_t)wv + 16u * (uint32_t)lane;
   const int k0w = bt.t0 + 32 * wv;  // the wave's first key row
   // query rows that exist and are local (mask 1)
   auto row_ok = [&](int j, int row, int m) {
@@ -1050,66 +998,71 @@ __device__ void band_dkv(const BwdParams& p, BandShared& sh, const BandTile& bt,
     if (t0q > k0w + 31 + w || t0q + 31 < k0w - w_hi) return;
     const uint32_t qval = __builtin_amdgcn_readfirstlane(lds_word(&sh.tab[j % kBandTab]));
     if (qval == 0u) return;
-    e16x8 qrf[4], drf[4], qt[2][2], dt[2][2];
-    f32x4 ls[4], ds4[4];
-    if (stage == 0)
-      read_dkv_rows<0>(qrf, drf, ls, ds4, ad, sa);
-    else if (stage == 1)
-      read_dkv_rows<kStageB>(qrf, drf, ls, ds4, ad, sa);
-    else
-      read_dkv_rows<2 * kStageB>(qrf, drf, ls, ds4, ad, sa);
-    // S + (-lse / scale) and dP + (-D): the row statistics enter as the
-    // accumulators' starting values (element r of a lane is row 8 (r / 4) +
-    // 4 hl + r % 4, float4 r / 4 of the staged values)
-    f32x16 sc, dp;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sc[r] = ls[r >> 2][r & 3];
-      dp[r] = ds4[r >> 2][r & 3];
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      sc = mma(qrf[s], kf[s], sc);
-      dp = mma(drf[s], vf[s], dp);
-    }
-    // the transposed reads run while the products above are in the MFMA unit
-    if (stage == 0)
-      read_dkv_cols<0>(qt, dt, ad);
-    else if (stage == 1)
-      read_dkv_cols<kStageB>(qt, dt, ad);
-    else
-      read_dkv_cols<2 * kStageB>(qt, dt, ad);
     // (query row q, this lane's key) in the window: tk - w_hi <= t0q + q <= tk + w
     const bool fast = all_keys && qval == 0xffffffffu && t0q + 31 - k0w <= w && k0w + 31 - t0q <= w_hi;
-    e16x8 p8[2], ds8[2];
-    if (fast) {
+    // One tensor at a time, so that few registers are live at once: S from
+    // the Q rows, dP from the dO rows (V from LDS), P and dS, then
+    // dV^T += dO^T P and dK^T += Q^T dS from the transposed rows.
+    auto body = [&](uint32_t so) {
+      e16x8 rf[4];
+      f32x4 st4[4];
+      // S + (-lse / scale) and dP + (-D): the row statistics enter as the
+      // accumulators' starting values (element r of a lane is row 8 (r / 4)
+      // + 4 hl + r % 4, float4 r / 4 of the staged values)
+      // P first (bf16, 8 registers), so that S is dead before dP is formed;
+      // dS = P dP takes the rounded P
+      e16x8 p8[2], ds8[2];
+      {
+        f32x16 sc;
+        e16x8 kf[4];
+        read_rows_stats<0>(rf, st4, kf, ad, sa, kb, so);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(p.c * sc[r]);
-        p8[r >> 3][r & 7] = (e16)pr;
-        ds8[r >> 3][r & 7] = (e16)(pr * dp[r]);
-      }
-    } else {
-      const uint32_t okb = kok ? (qval & bit_range(tk - w_hi - t0q, tk + w - t0q)) : 0u;
+        for (int r = 0; r < 16; ++r) sc[r] = st4[r >> 2][r & 3];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool ok = (okb >> acc_row(r, hl)) & 1u;
-        const float pr = __builtin_amdgcn_exp2f(p.c * sc[r]);
-        p8[r >> 3][r & 7] = (e16)(ok ? pr : 0.f);
-        ds8[r >> 3][r & 7] = (e16)(ok ? pr * dp[r] : 0.f);
-      }
-      if (qval != 0xffffffffu) {
-        zero_cols(qt, qval, hl);
-        zero_cols(dt, qval, hl);
-      }
-    }
+        for (int s = 0; s < 4; ++s) sc = mma(rf[s], kf[s], sc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (fast) {
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+          for (int r = 0; r < 16; ++r) p8[r >> 3][r & 7] = (e16)__builtin_amdgcn_exp2f(p.c * sc[r]);
+        } else {
+          // bits of this lane's rows: row acc_row(r, hl) is bit acc_row(r, 0) of okh
+          const uint32_t okh = (kok ? (qval & bit_range(tk - w_hi - t0q, tk + w - t0q)) : 0u) >> (4 * hl);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        av[db] = mma(dt[db][ks], p8[ks], av[db]);
-        ak[db] = mma(qt[db][ks], ds8[ks], ak[db]);
+          for (int r = 0; r < 16; ++r) {
+            const bool ok = (okh >> acc_row(r, 0)) & 1u;
+            p8[r >> 3][r & 7] = (e16)(ok ? __builtin_amdgcn_exp2f(p.c * sc[r]) : 0.f);
+          }
+        }
       }
+      {
+        f32x16 dp;
+        e16x8 vf[4];
+        read_rows_stats<1>(rf, st4, vf, ad, sa, vb, so);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = st4[r >> 2][r & 3];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) dp = mma(rf[s], vf[s], dp);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ds8[r >> 3][r & 7] = (e16)((float)p8[r >> 3][r & 7] * dp[r]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const bool zc = !fast && qval != 0xffffffffu;
+      e16x8 t8[2][2];
+      read_cols<1>(t8, ad, so);  // dO^T
+      if (zc) zero_cols(t8, qval, hl);
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) av[db] = mma(t8[db][ks], p8[ks], av[db]);
+      __builtin_amdgcn_sched_barrier(0);
+      read_cols<0>(t8, ad, so);  // Q^T
+      if (zc) zero_cols(t8, qval, hl);
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) ak[db] = mma(t8[db][ks], ds8[ks], ak[db]);
+    };
+    body((uint32_t)(stage * kStageB));
   };
   auto prologue = [&]() {
     load_frag(kf, K + (size_t)kp * rs, true, hl);
@@ -1120,9 +1073,18 @@ __device__ void band_dkv(const BwdParams& p, BandShared& sh, const BandTile& bt,
     kty = kin ? eff_mask(mk, ug) : 0;
     kok = kty == 1;
     all_keys = __all(kok);
-    return __syncthreads_or(kok) != 0;
+    const bool go = __syncthreads_or(kok) != 0;
+    // the wave's V fragments to LDS (read back each step, by this wave only)
+    if (go)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        *reinterpret_cast<e16x8*>(sh.kfr + 4096 * wv + 1024 * s + 16 * lane) = kf[s];
+        *reinterpret_cast<e16x8*>(sh.vfr + 4096 * wv + 1024 * s + 16 * lane) = vf[s];
+      }
+    ak[0] = ak[1] = av[0] = av[1] = zero16();
+    return go;
   };
-  band_loop<3>(nq, nq, issue, prologue, refill, gate, step);
+  band_loop(nq, nq, issue, prologue, refill, gate, step);
   write_out();
 }
 
@@ -1245,12 +1207,12 @@ __device__ void prep_body(const BwdParams& p) {
 }
 
 #if LF_HALF_F16
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void lf_attn_bwd_f16(const BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void lf_attn_bwd_f16(const BwdParams p) {
   bwd_band_body(p);
 }
 __global__ __launch_bounds__(256) void lf_attn_bwd_prep_f16(const BwdParams p) { prep_body(p); }
 #else
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void lf_attn_bwd_bf16(const BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void lf_attn_bwd_bf16(const BwdParams p) {
   bwd_band_body(p);
 }
 __global__ __launch_bounds__(256) void lf_attn_bwd_prep_bf16(const BwdParams p) { prep_body(p); }
