@@ -78,10 +78,10 @@ __device__ __forceinline__ int eff_mask(int8_t m, int use_g) {
 }
 
 struct BwdShared {
-  e16 st[2][32][kLdsRow];  // rows staged for the column-wise operand
-  int4 info[32];           // current block's slots: position, residue index, mask type
-  float2 stat[32];         // current block's query rows: log2-domain lse, D
-  int opos[32];            // positions of the wave's own 32 keys
+  e16 st[2][32][kLdsRow];                 // rows staged for the column-wise operand
+  __attribute__((aligned(16))) float sx[32];  // streamed query rows: -lse in base 2 (key-owning units)
+  __attribute__((aligned(16))) float sy[32];  // ... and -D
+  int opos[32];                           // positions of the wave's own 32 keys
 };
 
 // Slot code from a block description: a token's raw mask byte (0..255), or
@@ -153,35 +153,61 @@ __device__ __forceinline__ e16x8 col_frag(const BwdShared& sh, int which, int t,
   return __builtin_bit_cast(e16x8, v);
 }
 
-// Query-owning wave: 32 query rows (lane c's row at qpos, residue index qt,
-// type qty), nblk key blocks described by keyof(j, slot) -> (pos, t, slot code),
-// membership member(qty, qt, kty, kt).  Returns dq^T in acc: lane (c, hl)
-// holds head dims 32 half + acc_row(r, hl) of query c in acc[half][r].
-// geom(j) is a wave-uniform claim that every (query, key) pair of block j
-// lies in the relation when both are of the right type: then, if every key
-// and query slot is of that type, the block needs no per-element test.
-template <class KeyOf, class Member, class Geom>
+// A row fragment read from a row that exists (the caller clamps the
+// position), without a branch, so that the compiler's count of loads in
+// flight stays exact; rows that take no part are zeroed with keep_frag.
+__device__ __forceinline__ void load_frag_any(e16x8 (&f)[4], const e16* row, int hl) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) f[s] = ld8(row + 16 * s + 8 * hl);
+}
+
+// Membership of a slot type: want < 0 takes every type but 0, otherwise
+// exactly type want.
+__device__ __forceinline__ bool takes(int ty, int want) { return want < 0 ? ty != 0 : ty == want; }
+
+// Query-owning wave of the global units: 32 query rows (lane c's row at
+// qpos, type qty; its -lse in base 2 and -D in lse2, dd), nblk key blocks
+// described by keyof(j, slot) -> (pos, slot code).  A (query, key) pair
+// takes part when the query's type is want_q and the key's type is taken
+// by want_k.  Returns dq^T in acc: lane (c, hl) holds head dims 32 half +
+// acc_row(r, hl) of query c in acc[half][r].  The next block's rows load
+// while the current one is used.
+template <class KeyOf>
 __device__ void q_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16* qb, const e16* dob,
-                        const e16* kb, const e16* vb, int qpos, int qt, int qty, float lse2, float dd,
-                        int nblk, KeyOf keyof, Member member, Geom geom, int want_q, int want_k,
-                        f32x16 (&acc)[2]) {
-  const bool rows_ok = __all(qty == want_q);
+                        const e16* kb, const e16* vb, int qpos, int qty, float lse2, float dd, int nblk,
+                        KeyOf keyof, int want_q, int want_k, f32x16 (&acc)[2]) {
   const int lane = threadIdx.x & 63, c = lane & 31, hl = lane >> 5;
+  const bool qin = qty == want_q;
   e16x8 qf[4], df[4];
-  load_frag(qf, qb + (size_t)(qty ? qpos : 0) * rs, qty != 0, hl);
-  load_frag(df, dob + (size_t)(qty ? qpos : 0) * rs, qty != 0, hl);
+  load_frag_any(qf, qb + (size_t)(qty ? qpos : 0) * rs, hl);
+  load_frag_any(df, dob + (size_t)(qty ? qpos : 0) * rs, hl);
+  keep_frag(qf, qty != 0);
+  keep_frag(df, qty != 0);
   acc[0] = zero16();
   acc[1] = zero16();
+  int npos = -1, ncode = 0;
+  e16x8 nkf[4], nvf[4];
+  auto fetch = [&](int j) {
+    keyof(j, c, npos, ncode);
+    const size_t at = (size_t)(npos >= 0 ? npos : 0) * rs;
+    load_frag_any(nkf, kb + at, hl);
+    load_frag_any(nvf, vb + at, hl);
+  };
+  if (nblk > 0) fetch(0);
   for (int j = 0; j < nblk; ++j) {
-    int kpos = -1, kt = 0, kcode = 0;
-    keyof(j, c, kpos, kt, kcode);
+    const int kpos = npos, kcode = ncode;
     e16x8 kf[4], vf[4];
-    load_frag(kf, kb + (size_t)(kpos >= 0 ? kpos : 0) * rs, kpos >= 0, hl);
-    load_frag(vf, vb + (size_t)(kpos >= 0 ? kpos : 0) * rs, kpos >= 0, hl);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kf[s] = nkf[s];
+      vf[s] = nvf[s];
+    }
+    if (j + 1 < nblk) fetch(j + 1);
     const int kty = slot_type(kpos, kcode, p.use_globals);
     keep_frag(kf, kty != 0);
     keep_frag(vf, kty != 0);
-    if (hl == 0) sh.info[c] = make_int4(kpos, kt, kty, 0);
+    // keys taking part, by key row (lanes c and c + 32 hold key c)
+    const uint32_t kbits = (uint32_t)__ballot(takes(kty, want_k));
     stage_frag(sh, 0, c, hl, kf);
     wave_lds_sync();
     f32x16 S = zero16(), dP = zero16();
@@ -191,20 +217,11 @@ __device__ void q_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16*
       dP = mma(vf[s], df[s], dP);
     }
     e16x8 ds8[2];
-    if (rows_ok && geom(j) && __all(want_k < 0 ? kty != 0 : kty == want_k)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(p.c * S[r] - lse2);
-        ds8[r >> 3][r & 7] = (e16)(pr * (dP[r] - dd));
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int4 ki = sh.info[acc_row(r, hl)];
-        const bool ok = member(qty, qt, ki.z, ki.y);
-        const float pr = ok ? __builtin_amdgcn_exp2f(p.c * S[r] - lse2) : 0.f;
-        ds8[r >> 3][r & 7] = (e16)(ok ? pr * (dP[r] - dd) : 0.f);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const bool ok = qin && ((kbits >> acc_row(r, hl)) & 1u);
+      const float pr = __builtin_amdgcn_exp2f(p.c * S[r] - lse2);
+      ds8[r >> 3][r & 7] = (e16)(ok ? pr * (dP[r] - dd) : 0.f);
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half)
@@ -214,43 +231,56 @@ __device__ void q_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16*
   }
 }
 
-// Key-owning wave: 32 keys (lane c's key at kpos, residue index kt, type
-// kty), nblk query blocks described by rowof(j, slot) -> (pos, t, slot code).
-// Returns dk^T-free results: acc_k[half][r], acc_v[half][r] hold head dim
-// 32 half + c of own key acc_row(r, hl).
-template <class RowOf, class Member, class Geom>
+// Key-owning wave of the global units: 32 keys (lane c's key at kpos, type
+// kty), nblk query blocks described by rowof(j, slot) -> (pos, slot code),
+// the rows' -lse / scale and -D in lse_bh, d_bh.  A pair takes part when the
+// query row's type is want_q and the key's type is taken by want_k.
+// Returns acc_k[half][r], acc_v[half][r]: head dim 32 half + c of own key
+// acc_row(r, hl).  The next block's rows load while the current one is used.
+template <class RowOf>
 __device__ void kv_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16* kb, const e16* vb,
-                         const e16* qb, const e16* dob, const float* lse_bh, const float* d_bh, int kpos,
-                         int kt, int kty, int nblk, RowOf rowof, Member member, Geom geom, int want_q,
-                         int want_k, f32x16 (&acc_k)[2], f32x16 (&acc_v)[2]) {
-  const bool keys_ok = __all(want_k < 0 ? kty != 0 : kty == want_k);
+                         const e16* qb, const e16* dob, const float* lse_bh, const float* d_bh, int kpos, int kty,
+                         int nblk, RowOf rowof, int want_q, int want_k, f32x16 (&acc_k)[2], f32x16 (&acc_v)[2]) {
   const int lane = threadIdx.x & 63, c = lane & 31, hl = lane >> 5;
+  const bool kin = takes(kty, want_k);
   e16x8 kf[4], vf[4];
-  load_frag(kf, kb + (size_t)(kty ? kpos : 0) * rs, kty != 0, hl);
-  load_frag(vf, vb + (size_t)(kty ? kpos : 0) * rs, kty != 0, hl);
+  load_frag_any(kf, kb + (size_t)(kty ? kpos : 0) * rs, hl);
+  load_frag_any(vf, vb + (size_t)(kty ? kpos : 0) * rs, hl);
+  keep_frag(kf, kty != 0);
+  keep_frag(vf, kty != 0);
   acc_k[0] = acc_k[1] = acc_v[0] = acc_v[1] = zero16();
-  auto fetch = [&](int j, int& pos, int& tt, int& code, float& l2, float& dd, e16x8 (&a)[4], e16x8 (&b)[4]) {
-    pos = -1;
-    tt = 0;
-    code = 0;
-    if (j < nblk) rowof(j, c, pos, tt, code);
-    // loads depend on the position only; the mask type applies at use
-    l2 = pos >= 0 ? -p.c * lse_bh[pos] : 0.f;  // lse in base 2
-    dd = pos >= 0 ? -d_bh[pos] : 0.f;
-    load_frag(a, qb + (size_t)(pos >= 0 ? pos : 0) * rs, pos >= 0, hl);
-    load_frag(b, dob + (size_t)(pos >= 0 ? pos : 0) * rs, pos >= 0, hl);
+  int npos = -1, ncode = 0;
+  float nl = 0.f, nd = 0.f;
+  e16x8 nqf[4], ndf[4];
+  auto fetch = [&](int j) {
+    rowof(j, c, npos, ncode);
+    const int at = npos >= 0 ? npos : 0;
+    nl = -p.c * lse_bh[at];  // lse in base 2
+    nd = -d_bh[at];
+    load_frag_any(nqf, qb + (size_t)at * rs, hl);
+    load_frag_any(ndf, dob + (size_t)at * rs, hl);
   };
+  if (nblk > 0) fetch(0);
   for (int j = 0; j < nblk; ++j) {
-    int qpos = -1, qt = 0, qcode = 0;
-    float ql = 0.f, qd = 0.f;
+    const int qpos = npos, qcode = ncode;
+    const float ql = nl, qd = nd;
     e16x8 qf[4], df[4];
-    fetch(j, qpos, qt, qcode, ql, qd, qf, df);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      qf[s] = nqf[s];
+      df[s] = ndf[s];
+    }
+    if (j + 1 < nblk) fetch(j + 1);
     const int qty = slot_type(qpos, qcode, p.use_globals);
+    const bool qin = qty == want_q;
     keep_frag(qf, qty != 0);
     keep_frag(df, qty != 0);
+    // rows taking part, by row (lanes c and c + 32 hold row c); their
+    // statistics go through LDS, four consecutive rows per read below
+    const uint32_t qbits = (uint32_t)__ballot(qin);
     if (hl == 0) {
-      sh.info[c] = make_int4(qpos, qt, qty, 0);
-      sh.stat[c] = qty ? make_float2(ql, qd) : make_float2(0.f, 0.f);
+      sh.sx[c] = qin ? ql : 0.f;
+      sh.sy[c] = qin ? qd : 0.f;
     }
     stage_frag(sh, 0, c, hl, qf);
     stage_frag(sh, 1, c, hl, df);
@@ -262,26 +292,20 @@ __device__ void kv_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16
     for (int s = 0; s < 4; ++s) S = mma(*reinterpret_cast<const e16x8*>(&sh.st[0][c][16 * s + 8 * hl]), kf[s], S);
 #pragma unroll
     for (int s = 0; s < 4; ++s) dP = mma(*reinterpret_cast<const e16x8*>(&sh.st[1][c][16 * s + 8 * hl]), vf[s], dP);
+    // accumulator elements 4 g .. 4 g + 3 hold rows 8 g + 4 hl .. + 3
+    f32x4 sx4[4], sy4[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      sx4[g] = *reinterpret_cast<const f32x4*>(&sh.sx[8 * g + 4 * hl]);
+      sy4[g] = *reinterpret_cast<const f32x4*>(&sh.sy[8 * g + 4 * hl]);
+    }
     e16x8 p8[2], ds8[2];
-    if (keys_ok && geom(j) && __all(qty == want_q)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float2 st = sh.stat[acc_row(r, hl)];
-        const float pr = __builtin_amdgcn_exp2f(p.c * S[r] - st.x);
-        p8[r >> 3][r & 7] = (e16)pr;
-        ds8[r >> 3][r & 7] = (e16)(pr * (dP[r] - st.y));
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = acc_row(r, hl);
-        const int4 qi = sh.info[row];
-        const float2 st = sh.stat[row];
-        const bool ok = member(qi.z, qi.y, kty, kt);
-        const float pr = ok ? __builtin_amdgcn_exp2f(p.c * S[r] - st.x) : 0.f;
-        p8[r >> 3][r & 7] = (e16)pr;
-        ds8[r >> 3][r & 7] = (e16)(ok ? pr * (dP[r] - st.y) : 0.f);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const bool ok = kin && ((qbits >> acc_row(r, hl)) & 1u);
+      const float pr = __builtin_amdgcn_exp2f(p.c * S[r] - sx4[r >> 2][r & 3]);
+      p8[r >> 3][r & 7] = (e16)(ok ? pr : 0.f);
+      ds8[r >> 3][r & 7] = (e16)(ok ? pr * (dP[r] - sy4[r >> 2][r & 3]) : 0.f);
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half)
@@ -298,9 +322,95 @@ __device__ __forceinline__ void store_f4(float* dst, const float* v) {
   *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
 }
 
-// Work on the global tokens: unit `bid` of the single-wave units (GKV,
-// then GQ and GK), run by one wave with its own staging area sh.
-__device__ void bwd_global_unit(const BwdParams& p, BwdShared& sh, int bid) {
+// Work on the global tokens, in a launch of its own (global roles):
+//   GKV: one wave per 32 tokens of one (b, h); walks the global rows as
+//        queries and writes dk_g, dv_g of its tokens;
+//   GQ:  a workgroup per (b, h, block of 32 global slots, group of four
+//        kBwdChunk-token chunks), wave w taking chunk 4 g + w: dq_g of the
+//        global rows;
+//   GK:  the same grouping with local rows as queries: dk, dv of the
+//        global tokens as keys of local rows.
+// GQ and GK add into rows the preparation zeroed; the four waves of a
+// workgroup sum their partials through LDS first, so that a group of four
+// chunks costs one set of atomic adds.
+
+// GKV unit `bid`, run by one wave with its own staging area sh.
+__device__ void bwd_gkv_unit(const BwdParams& p, BwdShared& sh, int bid) {
+  const int lane = threadIdx.x & 63, c = lane & 31, hl = lane >> 5;
+  const int n = p.n;
+  const size_t rs = (size_t)p.H * 64;
+  const e16* QG = reinterpret_cast<const e16*>(p.qg);
+  const e16* KG = reinterpret_cast<const e16*>(p.kg);
+  const e16* VG = reinterpret_cast<const e16*>(p.vg);
+  const e16* DO = reinterpret_cast<const e16*>(p.dout);
+
+  const int kblocks = (n + 31) / 32;
+  const int bh = bid / kblocks;
+  const int kb0 = (bid - bh * kblocks) * 32;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const size_t boff = (size_t)b * n * rs + (size_t)h * 64;
+  const int8_t* mb = p.mask + (size_t)b * n;
+  const int nG = p.gcount[b];
+  const int32_t* gl = p.glist + (size_t)b * p.gstride;
+  const int mypos = kb0 + c < n ? kb0 + c : -1;
+  const int myty = mypos >= 0 ? eff_mask(mb[mypos], 1) : 0;
+  auto rowof = [&](int j, int slot, int& pos, int& code) {
+    const int g = 32 * j + slot;
+    const int e = gl[min(g, p.gstride - 1)];  // in the list whatever the count; taken below it only
+    pos = g < nG ? e : -1;
+    code = 256 + 2;
+  };
+  if (hl == 0) sh.opos[c] = mypos;
+  f32x16 ak[2], av[2];
+  // global rows (type 2) against every token that is not padding
+  kv_owner(p, sh, rs, KG + boff, VG + boff, QG + boff, DO + boff, p.lneg + (size_t)bh * n, p.dneg + (size_t)bh * n,
+           mypos, myty, (nG + 31) / 32, rowof, 2, -1, ak, av);
+  wave_lds_sync();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int pos = sh.opos[acc_row(r, hl)];
+    if (pos < 0) continue;
+    float* dk = p.dkg + boff + (size_t)pos * rs;
+    float* dv = p.dvg + boff + (size_t)pos * rs;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      dk[32 * half + c] = p.scale * ak[half][r];
+      dv[32 * half + c] = av[half][r];
+    }
+  }
+}
+
+// Sums the 32 accumulator values per lane of the four waves of a workgroup
+// (same lane layout in every wave) through LDS and passes each sum once to
+// add(half, r, value): wave w takes r = 4 w .. 4 w + 3 of both halves.  A
+// wave's partial goes to its own staging rows, which it no longer reads;
+// every wave of the workgroup calls this (it holds two barriers).
+template <class Add>
+__device__ __forceinline__ void group_add(BwdShared (&unit)[4], int wv, int lane, const f32x16 (&acc)[2], Add add) {
+  static_assert(sizeof(unit[0].st) >= 32 * 64 * sizeof(float), "a partial fits the staging rows");
+  float* mine = reinterpret_cast<float*>(&unit[wv].st[0][0][0]);
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mine[(16 * half + r) * 64 + lane] = acc[half][r];
+  __syncthreads();
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = 4 * wv + rr;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v += reinterpret_cast<const float*>(&unit[w].st[0][0][0])[(16 * half + r) * 64 + lane];
+      add(half, r, v);
+    }
+  __syncthreads();  // the partials are read before the staging rows are written again
+}
+
+// GQ (gq) or GK work of workgroup `grp` of its role; wave wv, with its own
+// staging area unit[wv].
+__device__ void bwd_gqk_group(const BwdParams& p, BwdShared (&unit)[4], int wv, int grp, bool gq) {
+  BwdShared& sh = unit[wv];
   const int lane = threadIdx.x & 63, c = lane & 31, hl = lane >> 5;
   const int n = p.n;
   const size_t rs = (size_t)p.H * 64;
@@ -312,107 +422,56 @@ __device__ void bwd_global_unit(const BwdParams& p, BwdShared& sh, int bid) {
   const e16* VG = reinterpret_cast<const e16*>(p.vg);
   const e16* DO = reinterpret_cast<const e16*>(p.dout);
 
-  // global roles: GKV (key blocks of every (b, h)), then GQ and GK
-  if (bid < p.n_gkv) {
-    const int kblocks = (n + 31) / 32;
-    const int bh = bid / kblocks;
-    const int kb0 = (bid - bh * kblocks) * 32;
-    const int b = bh / p.H, h = bh - b * p.H;
-    const size_t boff = (size_t)b * n * rs + (size_t)h * 64;
-    const int8_t* mb = p.mask + (size_t)b * n;
-    const int nG = p.gcount[b];
-    const int32_t* gl = p.glist + (size_t)b * p.gstride;
-    const int mypos = kb0 + c < n ? kb0 + c : -1;
-    const int myty = mypos >= 0 ? eff_mask(mb[mypos], 1) : 0;
-    auto rowof = [&](int j, int slot, int& pos, int& tt, int& code) {
-      const int g = 32 * j + slot;
-      pos = g < nG ? gl[g] : -1;
-      tt = 0;
-      code = 256 + 2;
-    };
-    auto member = [](int qty, int, int kty, int) { return qty == 2 && kty != 0; };
-    if (hl == 0) sh.opos[c] = mypos;
-    f32x16 ak[2], av[2];
-    kv_owner(p, sh, rs, KG + boff, VG + boff, QG + boff, DO + boff, p.lneg + (size_t)bh * n, p.dneg + (size_t)bh * n,
-             mypos, 0, myty, (nG + 31) / 32, rowof, member, [](int) { return true; }, 2, -1, ak, av);
-    wave_lds_sync();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int pos = sh.opos[acc_row(r, hl)];
-      if (pos < 0) continue;
-      float* dk = p.dkg + boff + (size_t)pos * rs;
-      float* dv = p.dvg + boff + (size_t)pos * rs;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        dk[32 * half + c] = p.scale * ak[half][r];
-        dv[32 * half + c] = av[half][r];
-      }
-    }
-    return;
-  }
-  bid -= p.n_gkv;
-
-  // GQ and GK: (b, h, block of 32 global slots, kBwdChunk-token chunk)
-  const bool gq = bid < p.n_gq;
-  if (!gq) bid -= p.n_gq;
-  const int per_bh = p.gslots * p.chunks;
-  const int bh = bid / per_bh;
-  const int rem = bid - bh * per_bh;
-  const int sb = rem / p.chunks;
-  const int ch = rem - sb * p.chunks;
+  // (b, h, block of 32 global slots, group of four chunks); this wave's chunk
+  const int cg = (p.chunks + 3) / 4;
+  const int per_bh = p.gslots * cg;
+  const int bh = grp / per_bh;
+  const int rem = grp - bh * per_bh;
+  const int sb = rem / cg;
+  const int ch = 4 * (rem - sb * cg) + wv;
   const int b = bh / p.H, h = bh - b * p.H;
   const int nG = p.gcount[b];
-  if (32 * sb >= nG) return;
+  if (32 * sb >= nG) return;  // the same for every wave of the workgroup
   const size_t boff = (size_t)b * n * rs + (size_t)h * 64;
   const int8_t* mb = p.mask + (size_t)b * n;
   const int32_t* gl = p.glist + (size_t)b * p.gstride;
   const int c0 = ch * kBwdChunk;
-  const int nblk = (min(kBwdChunk, n - c0) + 31) / 32;
+  const int nblk = ch < p.chunks ? (min(kBwdChunk, n - c0) + 31) / 32 : 0;
   const int g = 32 * sb + c;
-  const int gpos = g < nG ? gl[g] : -1;
+  const int ge = gl[min(g, p.gstride - 1)];  // in the list whatever the count; taken below it only
+  const int gpos = g < nG ? ge : -1;
   const int gty = g < nG ? 2 : 0;
-  auto tok = [&](int j, int slot, int& pos, int& tt, int& code) {
+  auto tok = [&](int j, int slot, int& pos, int& code) {
     const int t = c0 + 32 * j + slot;
     pos = t < n ? t : -1;
-    tt = 0;
     code = (uint8_t)mb[t < n ? t : 0];
   };
   const float* lse_bh = p.lneg + (size_t)bh * n;  // -lse / scale
   const float* d_bh = p.dneg + (size_t)bh * n;     // -D
   if (gq) {
-    auto member = [](int qty, int, int kty, int) { return qty == 2 && kty != 0; };
     const float lse2 = gty ? -p.c * lse_bh[gpos] : 0.f;
     const float dd = gty ? -d_bh[gpos] : 0.f;
     f32x16 acc[2];
-    q_owner(p, sh, rs, QG + boff, DO + boff, KG + boff, VG + boff, gpos, 0, gty, lse2, dd, nblk, tok, member,
-            [](int) { return true; }, 2, -1, acc);
-    if (gpos >= 0) {
-      float* dst = p.dqg + boff + (size_t)gpos * rs;
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          unsafeAtomicAdd(dst + 32 * half + acc_row(r, hl), p.scale * acc[half][r]);
-    }
+    // global rows (type 2) against the chunk's tokens that are not padding
+    q_owner(p, sh, rs, QG + boff, DO + boff, KG + boff, VG + boff, gpos, gty, lse2, dd, nblk, tok, 2, -1, acc);
+    float* dst = p.dqg + boff + (size_t)(gpos >= 0 ? gpos : 0) * rs;
+    group_add(unit, wv, lane, acc, [&](int half, int r, float v) {
+      if (gpos >= 0) unsafeAtomicAdd(dst + 32 * half + acc_row(r, hl), p.scale * v);
+    });
   } else {
-    auto member = [](int qty, int, int kty, int) { return qty == 1 && kty == 2; };
     if (hl == 0) sh.opos[c] = gpos;
     f32x16 ak[2], av[2];
-    kv_owner(p, sh, rs, K + boff, V + boff, Q + boff, DO + boff, lse_bh, d_bh, gpos, 0, gty, nblk, tok, member,
-             [](int) { return true; }, 1, 2, ak, av);
+    // the chunk's local rows (type 1) against the global tokens as keys (type 2)
+    kv_owner(p, sh, rs, K + boff, V + boff, Q + boff, DO + boff, lse_bh, d_bh, gpos, gty, nblk, tok, 1, 2, ak, av);
     wave_lds_sync();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    group_add(unit, wv, lane, ak, [&](int half, int r, float v) {
       const int pos = sh.opos[acc_row(r, hl)];
-      if (pos < 0) continue;
-      float* dk = p.dk + boff + (size_t)pos * rs;
-      float* dv = p.dv + boff + (size_t)pos * rs;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        unsafeAtomicAdd(dk + 32 * half + c, p.scale * ak[half][r]);
-        unsafeAtomicAdd(dv + 32 * half + c, av[half][r]);
-      }
-    }
+      if (pos >= 0) unsafeAtomicAdd(p.dk + boff + (size_t)pos * rs + 32 * half + c, p.scale * v);
+    });
+    group_add(unit, wv, lane, av, [&](int half, int r, float v) {
+      const int pos = sh.opos[acc_row(r, hl)];
+      if (pos >= 0) unsafeAtomicAdd(p.dv + boff + (size_t)pos * rs + 32 * half + c, v);
+    });
   }
 }
 
@@ -1093,21 +1152,9 @@ __device__ void band_dkv(const BwdParams& p, BandShared& sh, const BandTile& bt,
 // which then stay in that XCD's L2), and a tile's dq and dk/dv units are
 // neighbours.
 __device__ void bwd_band_body(const BwdParams& p) {
-  __shared__ union {
-    BandShared band;
-    BwdShared unit[4];
-  } shu;
+  __shared__ BandShared sh;
   const int N = 2 * p.n_bt;
   const int x = blockIdx.x;
-  if (x >= N) {
-    // the global-token units, four per workgroup (one per wave), after the
-    // band tiles: they fill the slots the last band tiles leave free
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int unit = 4 * (x - N) + wv;
-    if (unit < p.n_gkv + p.n_gq + p.n_gk) bwd_global_unit(p, shu.unit[wv], unit);
-    return;
-  }
-  BandShared& sh = shu.band;
   const int per = N / 8, rem = N % 8;
   const int xcd = x % 8, y = x / 8;
   const int m = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + y;
@@ -1118,6 +1165,25 @@ __device__ void bwd_band_body(const BwdParams& p) {
     band_dkv(p, sh, bt, wv);
   else
     band_dq(p, sh, bt, wv);
+}
+
+// The global-token launch: four units per workgroup, one per wave.
+__device__ void bwd_glob_body(const BwdParams& p) {
+  __shared__ BwdShared unit[4];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int x = blockIdx.x;
+  const int nkv = (p.n_gkv + 3) / 4;  // GKV: four units per workgroup
+  if (x < nkv) {
+    const int u = 4 * x + wv;
+    if (u < p.n_gkv) bwd_gkv_unit(p, unit[wv], u);
+    return;
+  }
+  const int per = p.B * p.H * p.gslots * ((p.chunks + 3) / 4);  // workgroups of GQ, then of GK
+  const int y = x - nkv;
+  if (y < per)
+    bwd_gqk_group(p, unit, wv, y, true);
+  else
+    bwd_gqk_group(p, unit, wv, y - per, false);
 }
 
 // Global list of batch row b, ascending, by one workgroup of 256 threads:
@@ -1211,11 +1277,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void l
   bwd_band_body(p);
 }
 __global__ __launch_bounds__(256) void lf_attn_bwd_prep_f16(const BwdParams p) { prep_body(p); }
+// No wave-count bound: the units' loops keep their fragments, accumulators
+// and block descriptions in registers (bounded to the band kernel's budget
+// they spill, and every reload waits on memory inside the loop).
+__global__ __launch_bounds__(256) void lf_attn_bwd_glob_f16(const BwdParams p) { bwd_glob_body(p); }
 #else
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void lf_attn_bwd_bf16(const BwdParams p) {
   bwd_band_body(p);
 }
 __global__ __launch_bounds__(256) void lf_attn_bwd_prep_bf16(const BwdParams p) { prep_body(p); }
+// No wave-count bound: the units' loops keep their fragments, accumulators
+// and block descriptions in registers (bounded to the band kernel's budget
+// they spill, and every reload waits on memory inside the loop).
+__global__ __launch_bounds__(256) void lf_attn_bwd_glob_bf16(const BwdParams p) { bwd_glob_body(p); }
 #endif
 
 }  // namespace
@@ -1226,8 +1300,9 @@ int launch_backward_f16(const BwdParams& bp, void* stream) {
   const size_t rows = (size_t)bp.B * bp.n * bp.H;
   const unsigned nlist = bp.use_globals ? (unsigned)bp.B : 0u;
   hipLaunchKernelGGL(lf_attn_bwd_prep_f16, dim3(nlist + (unsigned)((rows + 15) / 16)), dim3(256), 0, s, bp);
-  const int nglob = bp.n_gkv + bp.n_gq + bp.n_gk;
-  hipLaunchKernelGGL(lf_attn_bwd_f16, dim3(2 * bp.n_bt + (nglob + 3) / 4), dim3(256), 0, s, bp);
+  hipLaunchKernelGGL(lf_attn_bwd_f16, dim3(2 * bp.n_bt), dim3(256), 0, s, bp);
+  const unsigned nglob = (unsigned)bwd_glob_workgroups(bp.n_gkv, bp.B, bp.H, bp.gslots, bp.chunks);
+  if (nglob > 0) hipLaunchKernelGGL(lf_attn_bwd_glob_f16, dim3(nglob), dim3(256), 0, s, bp);
   return (int)hipGetLastError();
 }
 #else
@@ -1237,8 +1312,9 @@ int launch_backward(const BwdParams& bp, void* stream) {
   const size_t rows = (size_t)bp.B * bp.n * bp.H;
   const unsigned nlist = bp.use_globals ? (unsigned)bp.B : 0u;
   hipLaunchKernelGGL(lf_attn_bwd_prep_bf16, dim3(nlist + (unsigned)((rows + 15) / 16)), dim3(256), 0, s, bp);
-  const int nglob = bp.n_gkv + bp.n_gq + bp.n_gk;
-  hipLaunchKernelGGL(lf_attn_bwd_bf16, dim3(2 * bp.n_bt + (nglob + 3) / 4), dim3(256), 0, s, bp);
+  hipLaunchKernelGGL(lf_attn_bwd_bf16, dim3(2 * bp.n_bt), dim3(256), 0, s, bp);
+  const unsigned nglob = (unsigned)bwd_glob_workgroups(bp.n_gkv, bp.B, bp.H, bp.gslots, bp.chunks);
+  if (nglob > 0) hipLaunchKernelGGL(lf_attn_bwd_glob_bf16, dim3(nglob), dim3(256), 0, s, bp);
   return (int)hipGetLastError();
 }
 #endif

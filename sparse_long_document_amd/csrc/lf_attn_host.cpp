@@ -321,8 +321,8 @@ lf_status lf_attn_backward(const lf_attn_params* p, const void* q, const void* k
   const int64_t bhn = (int64_t)p->B * p->H;
   const int64_t n_gkv = pl.use_globals ? bhn * ((p->n + 31) / 32) : 0;
   const int64_t n_gq = pl.use_globals ? bhn * gslots * chunks : 0;
-  const int64_t grid = 2 * (int64_t)p->B * tiles + n_gkv + 2 * n_gq;
-  if (grid > INT32_MAX) return LF_ERR_UNSUPPORTED;
+  if (2 * (int64_t)p->B * tiles > INT32_MAX || lf::bwd_glob_workgroups(n_gkv, p->B, p->H, gslots, chunks) > INT32_MAX)
+    return LF_ERR_UNSUPPORTED;
   if ((int64_t)p->B + ((int64_t)p->B * p->n * p->H + 15) / 16 > INT32_MAX) return LF_ERR_UNSUPPORTED;
 
   const void* ins[10] = {q, k, v, q_g, k_g, v_g, out, dout, mask, lse};
