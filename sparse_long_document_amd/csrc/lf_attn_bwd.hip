@@ -1172,18 +1172,15 @@ __device__ void bwd_glob_body(const BwdParams& p) {
   __shared__ BwdShared unit[4];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int x = blockIdx.x;
-  const int nkv = (p.n_gkv + 3) / 4;  // GKV: four units per workgroup
-  if (x < nkv) {
-    const int u = 4 * x + wv;
-    if (u < p.n_gkv) bwd_gkv_unit(p, unit[wv], u);
+  // the GQ and GK workgroups first (each walks four chunks), the shorter
+  // GKV units after them, in the slots the first ones leave
+  const int per = p.B * p.H * p.gslots * ((p.chunks + 3) / 4);
+  if (x < 2 * per) {
+    bwd_gqk_group(p, unit, wv, x < per ? x : x - per, x < per);
     return;
   }
-  const int per = p.B * p.H * p.gslots * ((p.chunks + 3) / 4);  // workgroups of GQ, then of GK
-  const int y = x - nkv;
-  if (y < per)
-    bwd_gqk_group(p, unit, wv, y, true);
-  else
-    bwd_gqk_group(p, unit, wv, y - per, false);
+  const int u = 4 * (x - 2 * per) + wv;  // GKV: four units per workgroup
+  if (u < p.n_gkv) bwd_gkv_unit(p, unit[wv], u);
 }
 
 // Global list of batch row b, ascending, by one workgroup of 256 threads:

@@ -95,9 +95,9 @@ struct BwdParams {
 // Rows of one band tile of the backward (four waves of 32).
 constexpr int kBwdBandRows = 128;
 
-// Workgroups of the backward's global-token launch: the GKV units four per
-// workgroup, then one workgroup per (b, h, block of 32 global slots, group
-// of four chunks) for GQ and again for GK; 0 without global work.
+// Workgroups of the backward's global-token launch: one workgroup per (b,
+// h, block of 32 global slots, group of four chunks) for GQ and again for
+// GK, then the GKV units four per workgroup; 0 without global work.
 inline int64_t bwd_glob_workgroups(int64_t n_gkv, int64_t B, int64_t H, int64_t gslots, int64_t chunks) {
   if (n_gkv <= 0) return 0;
   return (n_gkv + 3) / 4 + 2 * B * H * gslots * ((chunks + 3) / 4);
