@@ -45,6 +45,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "lf_attn_internal.h"
 
 namespace lf {
@@ -285,13 +287,14 @@ __device__ void kv_owner(const BwdParams& p, BwdShared& sh, size_t rs, const e16
     stage_frag(sh, 0, c, hl, qf);
     stage_frag(sh, 1, c, hl, df);
     wave_lds_sync();
-    // the staged rows are read back as the products' row operands, so that
-    // the fragments need not stay in registers
+    // the row products from the fragments in registers; the staged rows
+    // serve the transposed reads below
     f32x16 S = zero16(), dP = zero16();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) S = mma(*reinterpret_cast<const e16x8*>(&sh.st[0][c][16 * s + 8 * hl]), kf[s], S);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) dP = mma(*reinterpret_cast<const e16x8*>(&sh.st[1][c][16 * s + 8 * hl]), vf[s], dP);
+    for (int s = 0; s < 4; ++s) {
+      S = mma(qf[s], kf[s], S);
+      dP = mma(df[s], vf[s], dP);
+    }
     // accumulator elements 4 g .. 4 g + 3 hold rows 8 g + 4 hl .. + 3
     f32x4 sx4[4], sy4[4];
 #pragma unroll
@@ -1292,26 +1295,99 @@ __global__ __launch_bounds__(256) void lf_attn_bwd_glob_bf16(const BwdParams p) 
 }  // namespace
 
 #if LF_HALF_F16
-int launch_backward_f16(const BwdParams& bp, void* stream) {
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const size_t rows = (size_t)bp.B * bp.n * bp.H;
-  const unsigned nlist = bp.use_globals ? (unsigned)bp.B : 0u;
-  hipLaunchKernelGGL(lf_attn_bwd_prep_f16, dim3(nlist + (unsigned)((rows + 15) / 16)), dim3(256), 0, s, bp);
-  hipLaunchKernelGGL(lf_attn_bwd_f16, dim3(2 * bp.n_bt), dim3(256), 0, s, bp);
-  const unsigned nglob = (unsigned)bwd_glob_workgroups(bp.n_gkv, bp.B, bp.H, bp.gslots, bp.chunks);
-  if (nglob > 0) hipLaunchKernelGGL(lf_attn_bwd_glob_f16, dim3(nglob), dim3(256), 0, s, bp);
-  return (int)hipGetLastError();
+#define LF_BWD_SUFFIX(x) x##_f16
+#else
+#define LF_BWD_SUFFIX(x) x##_bf16
+#endif
+namespace {
+void LF_BWD_SUFFIX(band_launch)(const BwdParams& bp, void* stream) {
+  hipLaunchKernelGGL(LF_BWD_SUFFIX(lf_attn_bwd), dim3(2 * bp.n_bt), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     bp);
 }
+void LF_BWD_SUFFIX(glob_launch)(const BwdParams& bp, void* stream) {
+  const unsigned nglob = (unsigned)bwd_glob_workgroups(bp.n_gkv, bp.B, bp.H, bp.gslots, bp.chunks);
+  hipLaunchKernelGGL(LF_BWD_SUFFIX(lf_attn_bwd_glob), dim3(nglob), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     bp);
+}
+}  // namespace
+
+#if LF_HALF_F16
+int launch_backward_f16(const BwdParams& bp, void* stream) {
 #else
 int launch_backward(const BwdParams& bp, void* stream) {
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (bp.dtype == LF_F16) return launch_backward_f16(bp, stream);
+#endif
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const size_t rows = (size_t)bp.B * bp.n * bp.H;
   const unsigned nlist = bp.use_globals ? (unsigned)bp.B : 0u;
-  hipLaunchKernelGGL(lf_attn_bwd_prep_bf16, dim3(nlist + (unsigned)((rows + 15) / 16)), dim3(256), 0, s, bp);
-  hipLaunchKernelGGL(lf_attn_bwd_bf16, dim3(2 * bp.n_bt), dim3(256), 0, s, bp);
-  const unsigned nglob = (unsigned)bwd_glob_workgroups(bp.n_gkv, bp.B, bp.H, bp.gslots, bp.chunks);
-  if (nglob > 0) hipLaunchKernelGGL(lf_attn_bwd_glob_bf16, dim3(nglob), dim3(256), 0, s, bp);
+  hipLaunchKernelGGL(LF_BWD_SUFFIX(lf_attn_bwd_prep), dim3(nlist + (unsigned)((rows + 15) / 16)), dim3(256), 0, s, bp);
+  if (bwd_glob_workgroups(bp.n_gkv, bp.B, bp.H, bp.gslots, bp.chunks) == 0) {
+    LF_BWD_SUFFIX(band_launch)(bp, stream);
+    return (int)hipGetLastError();
+  }
+  return launch_backward_pair(bp, stream, LF_BWD_SUFFIX(band_launch), LF_BWD_SUFFIX(glob_launch));
+}
+#undef LF_BWD_SUFFIX
+
+#if !LF_HALF_F16
+// The library's second stream per device for the backward's global-token
+// launch (default priority, not synchronising with the null stream) and its
+// fork and join events, created once, outside graph capture.
+namespace {
+constexpr int kAuxDevices = 64;
+struct BwdAux {
+  std::mutex mu;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;
+};
+BwdAux g_aux[kAuxDevices];
+
+bool make_aux(BwdAux& a) {
+  if (hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking) != hipSuccess) a.s = nullptr;
+  if (a.s && hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) != hipSuccess) a.fork = nullptr;
+  if (a.s && a.fork && hipEventCreateWithFlags(&a.join, hipEventDisableTiming) != hipSuccess) a.join = nullptr;
+  if (a.s && a.fork && a.join) return true;
+  if (a.fork) (void)hipEventDestroy(a.fork);
+  if (a.s) (void)hipStreamDestroy(a.s);
+  a.s = nullptr;
+  a.fork = a.join = nullptr;
+  a.failed = true;
+  (void)hipGetLastError();  // the failure is handled: both launches go on the caller's stream
+  return false;
+}
+}  // namespace
+
+int launch_backward_pair(const BwdParams& bp, void* stream, BwdLaunch band, BwdLaunch glob) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int dev = -1;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kAuxDevices) {
+    BwdAux& a = g_aux[dev];
+    std::lock_guard<std::mutex> lock(a.mu);
+    if (!a.s && !a.failed) {
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) make_aux(a);
+    }
+    // the fork point is after the work already on s (the preparation);
+    // the band launch is enqueued first, so that its workgroups take the
+    // CUs first and the global-token workgroups fill the slots they free
+    if (a.s && hipEventRecord(a.fork, s) == hipSuccess) {
+      band(bp, stream);
+      if (hipStreamWaitEvent(a.s, a.fork, 0) != hipSuccess) {
+        glob(bp, stream);
+        return (int)hipGetLastError();
+      }
+      glob(bp, a.s);
+      // without the join the caller's stream would not wait for the
+      // global-token launch: report it
+      hipError_t e = hipEventRecord(a.join, a.s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s, a.join, 0);
+      if (e != hipSuccess) return (int)e;
+      return (int)hipGetLastError();
+    }
+  }
+  band(bp, stream);
+  glob(bp, stream);
   return (int)hipGetLastError();
 }
 #endif
