@@ -169,7 +169,16 @@ size_t lf_attn_backward_workspace_bytes(const lf_attn_params* p);
  *     and dv from the local rows and no global-row work (the forward drops
  *     them likewise and flags its own status word).  Size max_global to the
  *     mask (the Python binding derives it when validating).
- *   - Asynchronous like lf_attn_forward; the same argument errors. */
+ *   - Asynchronous like lf_attn_forward; the same argument errors.  With
+ *     global tokens, the global-token work runs on a second stream of the
+ *     library (one per device, created at the first such call made outside
+ *     graph capture, kept until the process ends, default priority), forked
+ *     from `stream` after the preparation and joined back into it before
+ *     the call returns, so `stream` orders everything as usual and a graph
+ *     captured from `stream` holds both branches.  Concurrent calls on one
+ *     device take turns enqueueing on that stream.  If it is unavailable,
+ *     or the first such call is made under capture, the work runs on
+ *     `stream`. */
 lf_status lf_attn_backward(const lf_attn_params* p,
                            const void* q, const void* k, const void* v,
                            const void* q_g, const void* k_g, const void* v_g,

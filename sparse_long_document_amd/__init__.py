@@ -36,7 +36,8 @@ LIB_PATH = os.environ.get("LF_ATTN_LIBRARY") or os.path.join(os.path.dirname(os.
 KERNEL_SOURCES = ("csrc/lf_attn_kernels.hip", "csrc/lf_attn_kernels_f16.hip", "csrc/lf_attn_internal.h")
 
 
-BACKWARD_SOURCES = ("csrc/lf_attn_bwd.hip", "csrc/lf_attn_bwd_f16.hip", "csrc/lf_attn_internal.h")
+BACKWARD_SOURCES = ("csrc/lf_attn_bwd.hip", "csrc/lf_attn_bwd_f16.hip", "csrc/lf_attn_internal.h",
+                    "csrc/lf_attn_bwd_internal.h")
 
 
 def kernel_source_hash(sources=KERNEL_SOURCES) -> str:

@@ -47,7 +47,7 @@
 
 #include <mutex>
 
-#include "lf_attn_internal.h"
+#include "lf_attn_bwd_internal.h"
 
 namespace lf {
 namespace {

@@ -8,6 +8,7 @@
 
 #include "lf_attn.h"
 #include "lf_attn_internal.h"
+#include "lf_attn_bwd_internal.h"
 #include "lf_proj_internal.h"
 
 namespace {
