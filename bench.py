@@ -752,7 +752,7 @@ def report_backward(args, prob, run, ms, mode, t_wall):
                    "timing": mode, "wall_s": round(t_wall, 3)},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
-                     "kernel": f"lf_attn_bwd<{dname}> (whole backward: 2 launches)",
+                     "kernel": f"lf_attn_bwd<{dname}> (whole backward: preparation, band and global-token launches)",
                      "flops_per_launch": flops, "algorithmic_bytes": backward_bytes(prob)},
     }
     if not args.no_check:
