@@ -1,7 +1,8 @@
 // Longformer combined sliding-window + global attention forward for gfx950.
 //
 // One launch computes every output row with two kinds of workgroups:
-//   * global-row splits (dispatched first): split c of one (batch row b,
+//   * global-row splits (dispatched before the band tiles, or after them
+//     when the whole launch is resident at once): split c of one (batch row b,
 //     head h) scores every global token of b against keys
 //     [1024c, 1024c + 1024) with the global projections (each global token
 //     attends to every token: segmentfault Longformer summary, "Global
@@ -943,9 +944,9 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 __device__ __forceinline__ int xcd_remap(int x, int N) {
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous range of tiles so neighbouring tiles (which share K/V
-  // halos) share one L2.  x is the band index blockIdx.x - n_glob: every x
-  // of one class x % 8 has blockIdx.x % 8 = (x + n_glob) % 8, so each class
-  // runs on one XCD whatever n_glob is (the class is a relabelling of the
+  // halos) share one L2.  x is the band index blockIdx.x - (0 or n_glob):
+  // every x of one class x % 8 has one blockIdx.x % 8, so each class runs
+  // on one XCD whatever the offset is (the class is a relabelling of the
   // XCD index), and the classes are dealt contiguous ranges of tiles.
   const int per = N / 8, rem = N % 8;
   const int xcd = x % 8, y = x / 8;
@@ -1940,11 +1941,17 @@ __device__ __forceinline__ void fwd_body(const KernelParams& p) {
   // starts next to others already in their block loops gets through them
   // quickly.  The block loops run at normal priority.
   __builtin_amdgcn_s_setprio(2);
-  if (bid < p.n_glob) {
-    global_split<B16>(p, bid, sh);  // first: their merge waits for the last split
+  // Order of the two kinds in the grid: when the whole launch is resident
+  // at once (the host then chose the short split chunk) the splits come
+  // last, so that their loads queue behind the band tiles' first blocks;
+  // otherwise first, so that their merge is not left to the last round.
+  const bool splits_last = p.chunk == kGlobalChunkShort;
+  const int first_band = splits_last ? 0 : p.n_glob;
+  if (bid < first_band || bid >= first_band + p.n_band) {
+    global_split<B16>(p, bid - (splits_last ? p.n_band : 0), sh);
     return;
   }
-  band_tile<B16>(p, xcd_remap(bid - p.n_glob, p.n_band), sh);
+  band_tile<B16>(p, xcd_remap(bid - first_band, p.n_band), sh);
 }
 
 // Waves per SIMD: four workgroups (16 waves) per CU at head dims up to 64
