@@ -176,9 +176,11 @@ size_t lf_attn_backward_workspace_bytes(const lf_attn_params* p);
  *     from `stream` after the preparation and joined back into it before
  *     the call returns, so `stream` orders everything as usual and a graph
  *     captured from `stream` holds both branches.  Concurrent calls on one
- *     device take turns enqueueing on that stream.  If it is unavailable,
- *     or the first such call is made under capture, the work runs on
- *     `stream`. */
+ *     device take turns enqueueing on that stream.  While a graph capture
+ *     that holds such a call is open, no other thread may make such a call
+ *     on the same device (its work would join the capture).  If the second
+ *     stream is unavailable, or the first such call is made under capture,
+ *     the work runs on `stream`. */
 lf_status lf_attn_backward(const lf_attn_params* p,
                            const void* q, const void* k, const void* v,
                            const void* q_g, const void* k_g, const void* v_g,
