@@ -173,3 +173,45 @@ def test_backward_workload_one_head(name, head):
         sv = dv[0, :, h].sum(0)
         np.testing.assert_allclose(sv, do[m == 1, h].sum(0), atol=2e-2 * np.abs(sv).max() + 1e-3)
         assert np.abs(dk[0, :, h].sum(0)).max() <= 2e-2 * np.abs(dk[0, :, h]).sum(0).max()
+
+
+def test_backward_joins_its_second_stream():
+    """With global tokens the global-token work runs on the library's second
+    stream, joined back into the caller's before the call returns: work the
+    caller enqueues on its stream right after the call must see dq_g and
+    dv_g, which only that work writes.  Two calls back to back on a side
+    stream, each followed at once by a reduction on that stream; the sums
+    are taken again after a device-wide synchronisation, and the gradients
+    are compared with single calls on the default stream."""
+    d = torch.device("cuda")
+    kw = dict(B=1, n=2048, H=4, window=64, n_global=3)
+    probs = [workloads.random_problem(410 + i, name=f"bwd_join{i}", **kw) for i in range(2)]
+    douts = [workloads.upstream_grad(410 + i, p.shape, p.q.dtype) for i, p in enumerate(probs)]
+
+    def inputs(p):
+        return [x.to(d) for x in (p.q, p.k, p.v, p.q_g, p.k_g, p.v_g)], p.mask.to(d)
+
+    def call(p, dout):
+        t, mask = inputs(p)
+        out, lse = lf.forward(*t, mask=mask, window=p.window, return_lse=True)
+        return lf.backward(*t, mask, out, dout.to(d), lse, window=p.window)
+
+    _say("[gpu bwd] two calls back to back on a side stream")
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        res = []
+        for p, dout in zip(probs, douts):
+            grads = call(p, dout)
+            res.append((grads, torch.stack([grads[3].double().sum(), grads[5].double().abs().sum()])))
+    torch.cuda.synchronize()
+    for grads, sums in res:
+        again = torch.stack([grads[3].double().sum(), grads[5].double().abs().sum()])
+        assert torch.equal(sums, again), (sums, again)
+        assert again[1].item() > 0.0  # dv_g of the global rows is not all zero
+    for (grads, _), p, dout in zip(res, probs, douts):
+        ref = call(p, dout)
+        torch.cuda.synchronize()
+        for name, g, r in zip(NAMES, grads, ref):
+            g, r = g.double().cpu(), r.double().cpu()
+            tol = 1e-5 * max(r.abs().max().item(), 1e-3)  # fp32 atomics add in any order
+            assert (g - r).abs().max().item() <= tol, name
